@@ -1,0 +1,359 @@
+/*
+ * msa_oracle.c -- plain, slow CPU oracle for MiniMax Sparse Attention (MSA):
+ * the index branch (block max-pool of a single-head index key, q.blockmax
+ * scores, per-query causal top-K) and the sparse branch (standard GQA over
+ * the union of the selected KV blocks).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  It shares no
+ * code, header, table or helper with the HIP library, and neither includes
+ * the other.
+ *
+ * Everything is the plain definition written out: the max-pool is exact in
+ * fp32 (a max rounds nothing); scores and attention are fp64 over exactly
+ * upcast inputs; the softmax is the textbook two-pass form over the full key
+ * set of a query -- no tiling, no online softmax, no log-sum-exp merge.
+ *
+ * Pages cited (title, address):
+ *   [YLY] "MiniMax M3模型算力成本大幅降低原因深度解析",
+ *         youleyou.com/wenzhang/3016623.html
+ *   [CXT] "MiniMax M3 深度实战：当稀疏注意力打破百万 Token 墙 ...",
+ *         chenxutan.com/d/3746.html
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - the block summary is an elementwise max over the block's valid tokens
+ *     only (no zero padding of a partial last block);
+ *   - the max uses the total order -0 < +0 so that the result is unique;
+ *   - scores are a plain dot product (one index head, no scale, no
+ *     activation), one selection per query token shared by all heads;
+ *   - candidates are the blocks strictly before the query's own block; the own
+ *     block is always kept and counts toward K; ties go to the lower index;
+ *   - the selection is stored ascending and padded with -1;
+ *   - query head h reads KV head h / (Hq/Hkv); keys t <= p inside the own
+ *     block are visible (the query sees itself).
+ *
+ * Parallelism: OpenMP over queries (independent work, no reduction across
+ * threads, so results do not depend on the thread count).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_EINVAL -1
+
+/* bf16 -> fp32 is exact: the 16 bits are the top half of the fp32 pattern. */
+static double elem(const void *p, int dtype, int64_t i) {
+  if (dtype == 0) return (double)((const float *)p)[i];
+  uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Strict "a is larger than b" in the total order used for the max-pool:
+ * the IEEE order, with -0 placed below +0. */
+static int f32_above(float a, float b) {
+  if (a > b) return 1;
+  if (a == b && a == 0.0f && !signbit(a) && signbit(b)) return 1;
+  return 0;
+}
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------
+ * Index branch, step 1: block max-pool.  [YLY, "索引分支（Index Branch）"]
+ * kmax[b][c] = max over t in [b*B, min(b*B+B, len)) of idx_k[t][c].
+ * idx_k: [len][d_idx] fp32, kmax: [ceil(len/B)][d_idx] fp32.
+ * ---------------------------------------------------------------------- */
+int oracle_pool(const float *idx_k, int64_t len, int32_t d_idx, int32_t block,
+                float *kmax) {
+  if (!idx_k || !kmax || len < 1 || d_idx < 1 || block < 1) return ORC_EINVAL;
+  int64_t nb = (len + block - 1) / block;
+  for (int64_t b = 0; b < nb; ++b) {
+    int64_t t0 = b * block, t1 = t0 + block < len ? t0 + block : len;
+    for (int32_t c = 0; c < d_idx; ++c) {
+      float m = idx_k[t0 * d_idx + c];
+      for (int64_t t = t0 + 1; t < t1; ++t) {
+        float x = idx_k[t * d_idx + c];
+        if (f32_above(x, m)) m = x;
+      }
+      kmax[b * d_idx + c] = m;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Index branch, steps 2-3: scores and causal top-K.
+ * [YLY, "索引分支（Index Branch）"] single-head key, block max-pool, keep the
+ * Top-K blocks; [CXT §3.3 "Prefilling 与 Decoding 的差异化优化"] prefill scores
+ * every block for every query, decode scores the one new query.
+ *
+ * For query i at position pos = q_pos[i], own = pos / B:
+ *   score[b] = sum_c idx_q[i][c] * kmax[b][c] (fp64), for b < own;
+ *   rank the candidates by (score descending, b ascending), keep the first
+ *   min(K-1, own), add own, store ascending, pad with -1.
+ * Near-tie report (only when some candidate is left out and K >= 2):
+ *   gap_abs  = s_(K-1) - s_(K)   (last kept minus first left out),
+ *   gap_rel  = gap_abs / max(|s_(K-1)|, |s_(K)|),
+ *   err_bnd  = gamma_d * (sum_c |q_c kmax_(K-1),c| + sum_c |q_c kmax_(K),c|),
+ *              gamma_d = d*u/(1-d*u), u = 2^-24: the worst-case fp32 error of
+ *              the two dot products in any summation order.
+ *   All three are NaN when there is no cut.
+ * kmax: [nb_avail][d_idx]; own must be < nb_avail.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  double s;
+  int32_t b;
+} cand_t;
+
+static int cand_cmp(const void *x, const void *y) {
+  const cand_t *a = (const cand_t *)x, *b = (const cand_t *)y;
+  if (a->s > b->s) return -1;
+  if (a->s < b->s) return 1;
+  return (a->b > b->b) - (a->b < b->b);
+}
+
+static int int_cmp(const void *x, const void *y) {
+  int32_t a = *(const int32_t *)x, b = *(const int32_t *)y;
+  return (a > b) - (a < b);
+}
+
+int oracle_select(const float *idx_q, int64_t n_q, const int64_t *q_pos,
+                  const float *kmax, int64_t nb_avail, int32_t d_idx,
+                  int32_t block, int32_t topk, int32_t *sel, double *gap_rel,
+                  double *gap_abs, double *err_bnd) {
+  if (!idx_q || !q_pos || !kmax || !sel || n_q < 0 || d_idx < 1 || block < 1 ||
+      topk < 1)
+    return ORC_EINVAL;
+  for (int64_t i = 0; i < n_q; ++i)
+    if (q_pos[i] < 0 || q_pos[i] / block >= nb_avail) return ORC_EINVAL;
+  const double u = ldexp(1.0, -24);
+  const double gamma = d_idx * u / (1.0 - d_idx * u);
+  int bad = 0;
+#pragma omp parallel
+  {
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)(nb_avail + 1));
+    int32_t *keep = (int32_t *)malloc(sizeof(int32_t) * (size_t)(topk + 1));
+    if (!c || !keep) {
+#pragma omp atomic write
+      bad = 1;
+    }
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t i = 0; i < n_q; ++i) {
+      if (!c || !keep) continue;
+      const float *q = idx_q + i * d_idx;
+      int64_t own = q_pos[i] / block;
+      for (int64_t b = 0; b < own; ++b) {
+        double s = 0.0;
+        for (int32_t cc = 0; cc < d_idx; ++cc)
+          s += (double)q[cc] * (double)kmax[b * d_idx + cc];
+        c[b].s = s;
+        c[b].b = (int32_t)b;
+      }
+      qsort(c, (size_t)own, sizeof(cand_t), cand_cmp);
+      int64_t m = own < topk - 1 ? own : topk - 1;
+      for (int64_t j = 0; j < m; ++j) keep[j] = c[j].b;
+      qsort(keep, (size_t)m, sizeof(int32_t), int_cmp);
+      int32_t *row = sel + i * topk;
+      for (int64_t j = 0; j < m; ++j) row[j] = keep[j];
+      row[m] = (int32_t)own;
+      for (int64_t j = m + 1; j < topk; ++j) row[j] = -1;
+      double gr = NAN, ga = NAN, eb = NAN;
+      if (topk >= 2 && own > topk - 1) {
+        const cand_t *a = &c[topk - 2], *z = &c[topk - 1];
+        ga = a->s - z->s;
+        double den = fabs(a->s) > fabs(z->s) ? fabs(a->s) : fabs(z->s);
+        gr = den > 0.0 ? ga / den : 0.0;
+        double sa = 0.0, sz = 0.0;
+        for (int32_t cc = 0; cc < d_idx; ++cc) {
+          sa += fabs((double)q[cc] * (double)kmax[(int64_t)a->b * d_idx + cc]);
+          sz += fabs((double)q[cc] * (double)kmax[(int64_t)z->b * d_idx + cc]);
+        }
+        eb = gamma * (sa + sz);
+      }
+      if (gap_rel) gap_rel[i] = gr;
+      if (gap_abs) gap_abs[i] = ga;
+      if (err_bnd) err_bnd[i] = eb;
+    }
+    free(c);
+    free(keep);
+  }
+  return bad ? ORC_EINVAL : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Inverse map: queries per KV block, as CSR.
+ * [CXT §2.2 "KV Outer Gather Q：MSA 的关键设计"] the outer loop over KV
+ * blocks needs, per block, the queries that hit it.
+ * Walk queries in ascending order and append i to list[b] for each b in
+ * sel[i]; row_ptr is the prefix sum of the list sizes; slot[i][k] is the
+ * list position of (i, sel[i][k]) (-1 where sel is -1).
+ * Returns nnz, or a negative error.
+ * ---------------------------------------------------------------------- */
+int64_t oracle_invert(const int32_t *sel, int64_t n_q, int32_t topk,
+                      int64_t n_blocks, int32_t *row_ptr, int32_t *q_list,
+                      int32_t *slot) {
+  if (!sel || !row_ptr || !q_list || !slot || n_q < 0 || topk < 1 ||
+      n_blocks < 1)
+    return ORC_EINVAL;
+  int64_t *cnt = (int64_t *)calloc((size_t)n_blocks, sizeof(int64_t));
+  if (!cnt) return ORC_EINVAL;
+  for (int64_t i = 0; i < n_q * topk; ++i) {
+    int32_t b = sel[i];
+    if (b < -1 || b >= n_blocks) {
+      free(cnt);
+      return ORC_EINVAL;
+    }
+    if (b >= 0) cnt[b]++;
+  }
+  row_ptr[0] = 0;
+  for (int64_t b = 0; b < n_blocks; ++b)
+    row_ptr[b + 1] = row_ptr[b] + (int32_t)cnt[b];
+  for (int64_t b = 0; b < n_blocks; ++b) cnt[b] = row_ptr[b];
+  for (int64_t i = 0; i < n_q; ++i)
+    for (int32_t k = 0; k < topk; ++k) {
+      int32_t b = sel[i * topk + k];
+      if (b < 0) {
+        slot[i * topk + k] = -1;
+        continue;
+      }
+      int64_t s = cnt[b]++;
+      q_list[s] = (int32_t)i;
+      slot[i * topk + k] = (int32_t)s;
+    }
+  int64_t nnz = row_ptr[n_blocks];
+  free(cnt);
+  return nnz;
+}
+
+/* ------------------------------------------------------------------------
+ * Sparse branch: standard GQA over the union of the selected blocks.
+ * [YLY, "稀疏分支（Sparse Branch）"] GQA only over the K chosen blocks, the
+ * rest neither loaded nor multiplied; [CXT §2.3 "MSA 算法实现"] softmax of
+ * q.k/sqrt(d) over the gathered keys, weights times the gathered values.
+ *
+ * For eval entry e (query row q_row[e] at position q_pos[e]) and head h,
+ * with g = h / (Hq/Hkv):
+ *   keys  = union over b in sel[e] (b != -1) of {t : b*B <= t <= min(b*B+B-1, pos)}
+ *   s_t   = scale * sum_c q[row][h][c] * k[g][t][c]            (fp64)
+ *   m     = max_t s_t,  w_t = exp(s_t - m),  Z = sum_t w_t
+ *   o     = sum_t w_t v[g][t][:] / Z,  lse = m + ln Z,  both rounded to fp32.
+ * q: [*][Hq][d]; k, v: [Hkv][kv_stride][d]; dtype 0 = fp32, 1 = bf16 bits.
+ * Entries of sel above the own block are rejected (they would see the future).
+ * n_keys (nullable) receives |keys| per eval entry.
+ * ---------------------------------------------------------------------- */
+int oracle_attend(const void *q, const void *k, const void *v, int32_t dtype,
+                  int64_t n_eval, const int64_t *q_row, const int64_t *q_pos,
+                  const int32_t *sel, int32_t topk, int32_t hq, int32_t hkv,
+                  int32_t d, int32_t block, int64_t kv_stride, double scale,
+                  float *o, float *lse, int64_t *n_keys) {
+  if (!q || !k || !v || !q_row || !q_pos || !sel || !o || n_eval < 0 ||
+      topk < 1 || hq < 1 || hkv < 1 || hq % hkv || d < 1 || block < 1 ||
+      (dtype != 0 && dtype != 1))
+    return ORC_EINVAL;
+  for (int64_t e = 0; e < n_eval; ++e) {
+    int64_t own = q_pos[e] / block;
+    if (q_pos[e] < 0 || q_pos[e] >= kv_stride) return ORC_EINVAL;
+    for (int32_t j = 0; j < topk; ++j) {
+      int32_t b = sel[e * topk + j];
+      if (b < -1 || b > own) return ORC_EINVAL;
+    }
+  }
+  const int32_t grp = hq / hkv;
+  int bad = 0;
+#pragma omp parallel
+  {
+    int32_t *blk = (int32_t *)malloc(sizeof(int32_t) * (size_t)topk);
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)topk * block);
+    double *s = (double *)malloc(sizeof(double) * (size_t)topk * block);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!blk || !keys || !s || !acc) {
+#pragma omp atomic write
+      bad = 1;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t e = 0; e < n_eval; ++e) {
+      if (!blk || !keys || !s || !acc) continue;
+      const int64_t pos = q_pos[e];
+      /* the union of the selected blocks: sort, drop repeats and padding */
+      int32_t nblk = 0;
+      for (int32_t j = 0; j < topk; ++j)
+        if (sel[e * topk + j] >= 0) blk[nblk++] = sel[e * topk + j];
+      qsort(blk, (size_t)nblk, sizeof(int32_t), int_cmp);
+      int64_t nk = 0;
+      for (int32_t j = 0; j < nblk; ++j) {
+        if (j > 0 && blk[j] == blk[j - 1]) continue;
+        int64_t t0 = (int64_t)blk[j] * block, t1 = t0 + block - 1;
+        if (t1 > pos) t1 = pos;
+        for (int64_t t = t0; t <= t1; ++t) keys[nk++] = t;
+      }
+      if (n_keys) n_keys[e] = nk;
+      for (int32_t h = 0; h < hq; ++h) {
+        const int64_t g = h / grp;
+        const int64_t qb = (q_row[e] * hq + h) * (int64_t)d;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < nk; ++j) {
+          const int64_t kb = (g * kv_stride + keys[j]) * (int64_t)d;
+          double dot = 0.0;
+          for (int32_t c = 0; c < d; ++c)
+            dot += elem(q, dtype, qb + c) * elem(k, dtype, kb + c);
+          s[j] = scale * dot;
+          if (s[j] > m) m = s[j];
+        }
+        double z = 0.0;
+        for (int32_t c = 0; c < d; ++c) acc[c] = 0.0;
+        for (int64_t j = 0; j < nk; ++j) {
+          const double w = exp(s[j] - m);
+          const int64_t vb = (g * kv_stride + keys[j]) * (int64_t)d;
+          z += w;
+          for (int32_t c = 0; c < d; ++c) acc[c] += w * elem(v, dtype, vb + c);
+        }
+        float *out = o + (e * hq + h) * (int64_t)d;
+        for (int32_t c = 0; c < d; ++c) out[c] = (float)(acc[c] / z);
+        if (lse) lse[e * hq + h] = (float)(m + log(z));
+      }
+    }
+    free(blk);
+    free(keys);
+    free(s);
+    free(acc);
+  }
+  return bad ? ORC_EINVAL : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Work counters taken from an actual selection: the number of (query, block)
+ * pairs and the number of attended (query, key) pairs.  The attended FLOPs
+ * are 4*d*Hq per attended pair (2d for q.k, 2d for p*v).
+ * ---------------------------------------------------------------------- */
+int oracle_counts(const int32_t *sel, int64_t n_q, int32_t topk,
+                  const int64_t *q_pos, int32_t block, int64_t *nnz,
+                  int64_t *attended) {
+  if (!sel || !q_pos || !nnz || !attended || topk < 1 || block < 1)
+    return ORC_EINVAL;
+  int64_t a = 0, z = 0;
+  for (int64_t i = 0; i < n_q; ++i)
+    for (int32_t j = 0; j < topk; ++j) {
+      int32_t b = sel[i * topk + j];
+      if (b < 0) continue;
+      int64_t t0 = (int64_t)b * block, t1 = t0 + block - 1;
+      if (t1 > q_pos[i]) t1 = q_pos[i];
+      z += 1;
+      a += t1 - t0 + 1;
+    }
+  *nnz = z;
+  *attended = a;
+  return ORC_OK;
+}
