@@ -1,0 +1,239 @@
+"""Benchmark: the MSA hot path at 1M-token context on one MI355X.
+
+One step = the whole path over one synthetic sequence: the causal prefill of
+1,048,576 tokens (index-key max-pool, q.blockmax top-K, CSR inversion, sparse
+GQA with the KV-outer pass and the log-sum-exp merge) followed by 256
+sequential decode steps against the 1M-token cache (re-pool of the newest
+block, top-K of the new query, split-KV sparse attention, merge).
+
+Inputs are generated on the device before timing (seeded N(0,1), bf16 q/k/v,
+fp32 index vectors, 128 planted hot blocks) and stay resident in HBM.
+
+Printed (rank 0, one JSON line): ``value`` = attended TFLOP/s of the whole
+step (4*d*Hq FLOP per attended (query, key) pair, prefill and decode);
+``prefill_tflops`` and ``decode_us_per_step`` break it down; ``roofline`` is
+for the sparse-GQA prefill (its two kernels per call, timed with HIP events on
+the launch stream) against the dense bf16 MFMA peak; ``cpu_baseline`` times
+the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_sparse_attention_index_amd import ops, pipeline, synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector / MFMA)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def attended_pairs(q_pos0: int, n_q: int, block: int, topk: int) -> int:
+    """Sum over queries of the keys each attends (every non-own selected
+    block is full): (min(K, own+1) - 1) * B + (p mod B) + 1."""
+    p = np.arange(q_pos0, q_pos0 + n_q, dtype=np.int64)
+    keff = np.minimum(topk, p // block + 1)
+    return int(((keff - 1) * block + p % block + 1).sum())
+
+
+def decode_bytes(L: int, cfg) -> int:
+    """Algorithmic HBM bytes of one decode step for a sequence of length L
+    (query at L-1): K and V of the attended keys, the block summaries scanned,
+    the query, the index query, and the output."""
+    n_keys = attended_pairs(L - 1, 1, cfg.block, cfg.topk)
+    nb = -(-L // cfg.block)
+    elt = 2 if cfg.dtype == "bf16" else 4
+    return (n_keys * cfg.Hkv * cfg.d * elt * 2 + nb * cfg.d_idx * 4 +
+            cfg.Hq * cfg.d * elt + cfg.d_idx * 4 + cfg.Hq * (cfg.d + 1) * 4)
+
+
+def cpu_baseline(x, cfg, budget_s: float = 15.0):
+    """Time the CPU oracle on a bounded sample of the same workload: the
+    index branch and attention for a random sample of prefill queries."""
+    import oracle
+    oracle.build(force=False)
+    T, B, K = cfg.T, cfg.block, cfg.topk
+    rng = np.random.default_rng(0)
+    idx_k = x["idx_k"][:T].cpu().numpy()
+    kmax = oracle.pool(idx_k, B)
+    k_h = synth.host(x["k"])
+    v_h = synth.host(x["v"])
+    # calibrate on a few queries, then size the sample to the budget
+    n_cal = 8 * max(1, oracle.threads())
+    rows = np.sort(rng.choice(T, size=n_cal, replace=False))
+    t0 = time.perf_counter()
+    _run_oracle_rows(oracle, x, cfg, kmax, k_h, v_h, rows)
+    dt = time.perf_counter() - t0
+    n = int(min(T, max(n_cal, n_cal * budget_s / max(dt, 1e-3))))
+    rows = np.sort(rng.choice(T, size=n, replace=False))
+    t0 = time.perf_counter()
+    _run_oracle_rows(oracle, x, cfg, kmax, k_h, v_h, rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * cfg.d * cfg.Hq * sum(attended_pairs(int(p), 1, B, K) for p in rows)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{n} random prefill queries of the 1M-token sequence "
+                      f"(select + attend, fp64), {dt:.1f} s; pool of all 1M "
+                      f"index keys not included"}
+
+
+def _run_oracle_rows(oracle, x, cfg, kmax, k_h, v_h, rows):
+    pos = rows.astype(np.int64)
+    idx_q = x["idx_q"][torch.from_numpy(rows)].cpu().numpy()
+    sel, *_ = oracle.select(idx_q, pos, kmax, cfg.block, cfg.topk)
+    q_h = synth.host(x["q"][torch.from_numpy(rows)])
+    oracle.attend(q_h, k_h, v_h, np.arange(len(rows)), pos, sel, cfg.block,
+                  cfg.scale, oracle.BF16)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="p1m", choices=["p1m", "p32k", "p128k"])
+    ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    cfg = synth.CONFIGS[args.config]
+    n_dec = cfg.n_dec if args.decode_steps is None else args.decode_steps
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.load()
+    T, B, K = cfg.T, cfg.block, cfg.topk
+    L_total = T + n_dec
+    print(f"[bench] generating {cfg.name}: {L_total} tokens", file=sys.stderr, flush=True)
+    x = synth.sequence_inputs(cfg, dev, args.seed, length=L_total)
+    torch.cuda.synchronize()
+
+    nb_max = -(-L_total // B)
+    kmax_dec = torch.zeros((1, nb_max, cfg.d_idx), dtype=torch.float32, device=dev)
+    bufs = pipeline.alloc_prefill(x["q"][:T], x["idx_q"][:T], B, K)
+    bufs.kmax = kmax_dec[0, :-(-T // B)]
+    k_cache, v_cache = x["k"][None], x["v"][None]
+    idx_k_cache = x["idx_k"][None]
+    seq_lens = torch.arange(T + 1, T + n_dec + 1, dtype=torch.int64, device=dev)
+    dbufs = pipeline.alloc_decode(x["q"][:1], kmax_dec, B, K) if n_dec else None
+    stream = torch.cuda.current_stream(dev)
+
+    ev = {"pre": [], "attn": [], "dec": []}
+
+    def step(record: bool):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        # prefill: pool, top-K, then per chunk CSR + sparse GQA (timed per call)
+        q, k, v = x["q"][:T], x["k"], x["v"]
+        ops.msa_index_pool(x["idx_k"][:T], B, kmax=bufs.kmax)
+        ops.msa_index_topk(x["idx_q"][:T], bufs.kmax, B, K, sel=bufs.sel)
+        for c0 in range(0, T, bufs.chunk):
+            c1 = min(T, c0 + bufs.chunk)
+            nbc = -(-c1 // B)
+            n = c1 - c0
+            ops.msa_invert_selection(bufs.sel[c0:c1], nbc, row_ptr=bufs.row_ptr[:nbc + 1],
+                                     q_list=bufs.q_list[:n * K], slot=bufs.slot[:n],
+                                     ws=bufs.inv_ws)
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            ops.msa_sparse_gqa_prefill(q[c0:c1], k, v, bufs.sel[c0:c1],
+                                       bufs.row_ptr[:nbc + 1], bufs.q_list[:n * K],
+                                       bufs.slot[:n], B, cfg.scale, q_pos0=c0,
+                                       o=bufs.o[c0:c1], lse=bufs.lse[c0:c1],
+                                       ws=bufs.attn_ws)
+            a1.record(stream)
+            if record:
+                ev["attn"].append((a0, a1))
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(stream)
+        for s in range(n_dec):
+            pipeline.decode_step(x["q"][T + s:T + s + 1], x["idx_q"][T + s:T + s + 1],
+                                 k_cache, v_cache, idx_k_cache, kmax_dec,
+                                 seq_lens[s:s + 1], B, K, cfg.scale, bufs=dbufs)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        if record:
+            ev["pre"].append((e0, e1))
+            ev["dec"].append((e1, e2))
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = lambda pairs: sum(a.elapsed_time(b) for a, b in pairs)
+    pre_ms = ms(ev["pre"]) / args.steps
+    dec_ms = ms(ev["dec"]) / args.steps
+    attn_ms = ms(ev["attn"]) / len(ev["attn"])           # per prefill-attention call
+    n_calls = len(ev["attn"]) // args.steps
+    pre_pairs = attended_pairs(0, T, B, K)
+    dec_pairs = sum(attended_pairs(T + s, 1, B, K) for s in range(n_dec))
+    fl = 4.0 * cfg.d * cfg.Hq
+    step_s = wall / args.steps
+    value = fl * (pre_pairs + dec_pairs) / step_s / 1e12
+    attn_tflops = fl * pre_pairs / n_calls / (attn_ms * 1e-3) / 1e12
+    dec_us = dec_ms * 1e3 / max(1, n_dec)
+    dec_gbs = (sum(decode_bytes(T + s + 1, cfg) for s in range(n_dec)) /
+               max(1e-12, dec_ms * 1e-3) / 1e9) if n_dec else None
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    out = {
+        "metric": "prefill attended TFLOP/s + decode us/step at 1M ctx; % of MFMA/HBM roofline",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1), planted hot blocks), generated on device",
+        "config": {"workload": f"{cfg.name}: 1 sequence, {T}-token causal prefill + "
+                               f"{n_dec} decode steps, {cfg.dtype} q/k/v, fp32 index, "
+                               f"Hq {cfg.Hq} / Hkv {cfg.Hkv}, d {cfg.d}, d_idx {cfg.d_idx}, "
+                               f"block {B}, top-K {K}, {cfg.n_hot} hot blocks",
+                   "seq_len": T, "decode_steps": n_dec, "global_batch": 1,
+                   "parallelism": "none (1 GPU)"},
+        "prefill_ms": round(pre_ms, 3),
+        "prefill_tflops": round(fl * pre_pairs / (pre_ms * 1e-3) / 1e12, 3),
+        "decode_us_per_step": round(dec_us, 3) if n_dec else None,
+        "decode_hbm_gbs": round(dec_gbs, 1) if dec_gbs else None,
+        "roofline": {"kernel": "msa_sparse_gqa_prefill (KV-outer pass + own-block/merge pass)",
+                     "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 5),
+                     "traffic": None,
+                     "launch_ms": round(attn_ms, 3), "launches_per_step": n_calls},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(x, cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

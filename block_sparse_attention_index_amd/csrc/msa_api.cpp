@@ -1,0 +1,210 @@
+// msa_api.cpp -- the C-ABI entry points declared in include/msa.h: argument
+// validation, workspace sizing and kernel selection.  Every check runs before
+// anything is enqueued, so an error leaves the outputs untouched.  Nothing
+// here allocates device memory, and nothing falls back to another path: an
+// unsupported shape is reported as MSA_ERR_UNSUPPORTED.
+#include "msa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "msa_internal.h"
+
+namespace {
+
+constexpr int32_t kMaxBlock = 4096;
+constexpr int32_t kMaxTopk = 64;
+constexpr int64_t kMaxGridY = 65535;
+
+bool block_ok(int32_t b) { return b >= 16 && b <= kMaxBlock && b % 16 == 0; }
+bool topk_ok(int32_t k) { return k >= 1 && k <= kMaxTopk; }
+bool didx_ok(int32_t d) {
+  return d >= 1 && d <= 1024 && (d % 4 == 0 || d <= 256);
+}
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int status_of(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+namespace msa {
+bool generic_prefill_supported(int32_t d, int32_t group);
+hipError_t launch_prefill_generic(const void *q, const void *k, const void *v,
+                                  int32_t dtype, int64_t kv_stride,
+                                  int64_t q_pos0, int64_t n_q, int32_t hq,
+                                  int32_t hkv, int32_t d, int32_t block,
+                                  const int32_t *sel, int32_t topk,
+                                  const int32_t *row_ptr,
+                                  const int32_t *q_list, const int32_t *slot,
+                                  float scale, float *o, float *lse, void *ws,
+                                  hipStream_t st);
+
+bool prefill_supported(int32_t dtype, int32_t d, int32_t group) {
+  if (dtype != MSA_F32 && dtype != MSA_BF16) return false;
+  return generic_prefill_supported(d, group);
+}
+
+hipError_t launch_prefill(const void *q, const void *k, const void *v,
+                          int32_t dtype, int64_t kv_stride, int64_t q_pos0,
+                          int64_t n_q, int32_t hq, int32_t hkv, int32_t d,
+                          int32_t block, const int32_t *sel, int32_t topk,
+                          const int32_t *row_ptr, const int32_t *q_list,
+                          const int32_t *slot, float scale, float *o,
+                          float *lse, void *ws, hipStream_t st) {
+  return launch_prefill_generic(q, k, v, dtype, kv_stride, q_pos0, n_q, hq, hkv,
+                                d, block, sel, topk, row_ptr, q_list, slot,
+                                scale, o, lse, ws, st);
+}
+}  // namespace msa
+
+extern "C" {
+
+const char *msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK:
+      return "MSA_OK";
+    case MSA_ERR_INVALID_ARG:
+      return "MSA_ERR_INVALID_ARG: invalid argument";
+    case MSA_ERR_UNSUPPORTED:
+      return "MSA_ERR_UNSUPPORTED: no kernel for this configuration";
+    case MSA_ERR_WORKSPACE:
+      return "MSA_ERR_WORKSPACE: workspace too small";
+    case MSA_ERR_HIP:
+      return "MSA_ERR_HIP: HIP launch or runtime error";
+    default:
+      return "unknown msa status";
+  }
+}
+
+int msa_index_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
+                   const int64_t *seq_len, int32_t d_idx, int32_t block,
+                   int64_t blk_begin, int64_t blk_end, float *kmax,
+                   int64_t nb_max, void *stream) {
+  if (!idx_k || !kmax || n_seq < 1 || n_seq > kMaxGridY || len_max < 1 ||
+      !didx_ok(d_idx) || !block_ok(block) || nb_max < cdiv(len_max, block))
+    return MSA_ERR_INVALID_ARG;
+  if (blk_begin >= 0 && (blk_end <= blk_begin || blk_end > nb_max ||
+                         blk_end - blk_begin > INT32_MAX))
+    return MSA_ERR_INVALID_ARG;
+  return status_of(msa::launch_pool(idx_k, n_seq, len_max, seq_len, d_idx,
+                                    block, blk_begin, blk_end, kmax, nb_max,
+                                    as_stream(stream)));
+}
+
+int msa_index_topk(const float *idx_q, int64_t n_q, int64_t q_pos0,
+                   const float *kmax, int64_t nb, int32_t d_idx, int32_t block,
+                   int32_t topk, int32_t *sel, void *stream) {
+  if (!idx_q || !kmax || !sel || n_q < 0 || q_pos0 < 0 || !didx_ok(d_idx) ||
+      !block_ok(block) || !topk_ok(topk) || nb < 1)
+    return MSA_ERR_INVALID_ARG;
+  if (n_q == 0) return MSA_OK;
+  if ((q_pos0 + n_q - 1) / block >= nb || (q_pos0 + n_q - 1) / block > INT32_MAX)
+    return MSA_ERR_INVALID_ARG;
+  return status_of(msa::launch_topk_prefill(idx_q, n_q, q_pos0, kmax, nb, d_idx,
+                                            block, topk, sel,
+                                            as_stream(stream)));
+}
+
+size_t msa_topk_decode_workspace_bytes(int32_t n_seq, int64_t nb_max,
+                                       int32_t topk) {
+  if (n_seq < 1 || nb_max < 1 || !topk_ok(topk)) return 0;
+  return msa::topk_decode_ws_bytes(n_seq, nb_max, topk);
+}
+
+int msa_index_topk_decode(const float *idx_q, int32_t n_seq,
+                          const int64_t *seq_len, const float *kmax,
+                          int64_t nb_max, int32_t d_idx, int32_t block,
+                          int32_t topk, int32_t *sel, void *ws,
+                          size_t ws_bytes, void *stream) {
+  if (!idx_q || !seq_len || !kmax || !sel || !ws || n_seq < 1 ||
+      n_seq > kMaxGridY || nb_max < 1 || nb_max > INT32_MAX ||
+      !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk))
+    return MSA_ERR_INVALID_ARG;
+  if (ws_bytes < msa::topk_decode_ws_bytes(n_seq, nb_max, topk))
+    return MSA_ERR_WORKSPACE;
+  return status_of(msa::launch_topk_decode(idx_q, n_seq, seq_len, kmax, nb_max,
+                                           d_idx, block, topk, sel, ws,
+                                           as_stream(stream)));
+}
+
+size_t msa_invert_workspace_bytes(int64_t n_q, int32_t topk, int64_t n_blocks) {
+  if (n_q < 0 || !topk_ok(topk) || n_blocks < 1) return 0;
+  return msa::invert_ws_bytes(n_q, topk, n_blocks);
+}
+
+int msa_invert_selection(const int32_t *sel, int64_t n_q, int32_t topk,
+                         int64_t n_blocks, int32_t *row_ptr, int32_t *q_list,
+                         int32_t *slot, void *ws, size_t ws_bytes,
+                         void *stream) {
+  if (!sel || !row_ptr || !q_list || !slot || !ws || n_q < 0 ||
+      !topk_ok(topk) || n_blocks < 1 || n_blocks >= INT32_MAX ||
+      n_q * (int64_t)topk >= INT32_MAX)
+    return MSA_ERR_INVALID_ARG;
+  if (ws_bytes < msa::invert_ws_bytes(n_q, topk, n_blocks))
+    return MSA_ERR_WORKSPACE;
+  return status_of(msa::launch_invert(sel, n_q, topk, n_blocks, row_ptr, q_list,
+                                      slot, ws, as_stream(stream)));
+}
+
+size_t msa_prefill_workspace_bytes(int64_t q_pos0, int64_t n_q, int32_t hq,
+                                   int32_t d, int32_t block, int32_t topk) {
+  if (q_pos0 < 0 || n_q < 0 || hq < 1 || d < 1 || !block_ok(block) ||
+      !topk_ok(topk))
+    return 0;
+  return msa::prefill_ws_bytes(q_pos0, n_q, hq, d, block, topk);
+}
+
+int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
+                           int32_t dtype, int64_t kv_stride, int64_t q_pos0,
+                           int64_t n_q, int32_t hq, int32_t hkv, int32_t d,
+                           int32_t block, const int32_t *sel, int32_t topk,
+                           const int32_t *row_ptr, const int32_t *q_list,
+                           const int32_t *slot, float scale, float *o,
+                           float *lse, void *ws, size_t ws_bytes,
+                           void *stream) {
+  if (!q || !k || !v || !sel || !row_ptr || !q_list || !slot || !o || !ws ||
+      (dtype != MSA_F32 && dtype != MSA_BF16) || n_q < 0 || q_pos0 < 0 ||
+      hq < 1 || hkv < 1 || hkv > kMaxGridY || hq % hkv != 0 || d < 1 ||
+      !block_ok(block) || !topk_ok(topk) || !std::isfinite(scale) ||
+      q_pos0 + n_q > kv_stride || n_q * (int64_t)topk >= INT32_MAX)
+    return MSA_ERR_INVALID_ARG;
+  if (!msa::prefill_supported(dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
+  if (n_q == 0) return MSA_OK;
+  if (ws_bytes < msa::prefill_ws_bytes(q_pos0, n_q, hq, d, block, topk))
+    return MSA_ERR_WORKSPACE;
+  return status_of(msa::launch_prefill(q, k, v, dtype, kv_stride, q_pos0, n_q,
+                                       hq, hkv, d, block, sel, topk, row_ptr,
+                                       q_list, slot, scale, o, lse, ws,
+                                       as_stream(stream)));
+}
+
+size_t msa_decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t d,
+                                  int32_t block, int32_t topk) {
+  if (n_seq < 1 || hq < 1 || d < 1 || !block_ok(block) || !topk_ok(topk))
+    return 0;
+  return msa::decode_ws_bytes(n_seq, hq, d, block, topk);
+}
+
+int msa_sparse_gqa_decode(const void *q, const void *k_cache,
+                          const void *v_cache, int32_t dtype, int32_t n_seq,
+                          int64_t len_max, const int64_t *seq_len, int32_t hq,
+                          int32_t hkv, int32_t d, int32_t block,
+                          const int32_t *sel, int32_t topk, float scale,
+                          float *o, float *lse, void *ws, size_t ws_bytes,
+                          void *stream) {
+  if (!q || !k_cache || !v_cache || !seq_len || !sel || !o || !ws ||
+      (dtype != MSA_F32 && dtype != MSA_BF16) || n_seq < 1 ||
+      n_seq > kMaxGridY || len_max < 1 || hq < 1 || hkv < 1 ||
+      hkv > kMaxGridY || hq % hkv != 0 || d < 1 || !block_ok(block) ||
+      !topk_ok(topk) || !std::isfinite(scale))
+    return MSA_ERR_INVALID_ARG;
+  if (!msa::decode_supported(dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
+  if (ws_bytes < msa::decode_ws_bytes(n_seq, hq, d, block, topk))
+    return MSA_ERR_WORKSPACE;
+  return status_of(msa::launch_decode(q, k_cache, v_cache, dtype, n_seq,
+                                      len_max, seq_len, hq, hkv, d, block, sel,
+                                      topk, scale, o, lse, ws,
+                                      as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// pool.hip -- block max-pool of the single-head index key (index branch of
+// "MiniMax M3模型算力成本大幅降低原因深度解析", paragraph "索引分支（Index Branch）").
+//
+// One workgroup per (block, sequence).  The block's rows are streamed with
+// coalesced 16-byte loads (256 threads = R row-groups x d_idx/4 column lanes),
+// reduced in registers, then across row-groups through LDS.  The max runs on
+// an order-preserving integer image of the float bits, which makes it exact,
+// order-free and puts -0 below +0.  HBM-bound: each index key is read once.
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+__device__ __forceinline__ int f2key(float x) {
+  int i = __float_as_int(x);
+  return i ^ ((i >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float key2f(int k) {
+  return __int_as_float(k ^ ((k >> 31) & 0x7fffffff));
+}
+
+// d_idx % 4 == 0 and d_idx <= 1024.
+__global__ __launch_bounds__(256) void pool_vec4(
+    const float *__restrict__ idx_k, int64_t len_max,
+    const int64_t *__restrict__ seq_len, int d_idx, int B, int64_t blk_begin,
+    float *__restrict__ kmax, int64_t nb_max) {
+  __shared__ int4 red[256];
+  const int s = blockIdx.y;
+  int64_t len = seq_len ? seq_len[s] : len_max;
+  if (len > len_max) len = len_max;
+  if (len < 1) return;
+  const int64_t b = blk_begin < 0 ? (len - 1) / B : blk_begin + blockIdx.x;
+  const int64_t t0 = b * B;
+  if (t0 >= len || b >= nb_max) return;
+  const int64_t t1 = t0 + B < len ? t0 + B : len;
+  const int c4n = d_idx >> 2;
+  const int R = 256 / c4n;
+  const int tid = threadIdx.x;
+  const int col = tid % c4n, r = tid / c4n;
+  int4 m = make_int4(INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN);
+  if (r < R) {
+    const float4 *src =
+        reinterpret_cast<const float4 *>(idx_k + ((int64_t)s * len_max) * d_idx);
+    for (int64_t t = t0 + r; t < t1; t += R) {
+      float4 x = src[t * c4n + col];
+      m.x = max(m.x, f2key(x.x));
+      m.y = max(m.y, f2key(x.y));
+      m.z = max(m.z, f2key(x.z));
+      m.w = max(m.w, f2key(x.w));
+    }
+  }
+  red[tid] = m;
+  __syncthreads();
+  if (tid < c4n) {
+    for (int rr = 1; rr < R; ++rr) {
+      int4 y = red[rr * c4n + tid];
+      m.x = max(m.x, y.x);
+      m.y = max(m.y, y.y);
+      m.z = max(m.z, y.z);
+      m.w = max(m.w, y.w);
+    }
+    float4 out = make_float4(key2f(m.x), key2f(m.y), key2f(m.z), key2f(m.w));
+    reinterpret_cast<float4 *>(kmax + ((int64_t)s * nb_max + b) * d_idx)[tid] =
+        out;
+  }
+}
+
+// Any d_idx <= 256.
+__global__ __launch_bounds__(256) void pool_scalar(
+    const float *__restrict__ idx_k, int64_t len_max,
+    const int64_t *__restrict__ seq_len, int d_idx, int B, int64_t blk_begin,
+    float *__restrict__ kmax, int64_t nb_max) {
+  __shared__ int red[256];
+  const int s = blockIdx.y;
+  int64_t len = seq_len ? seq_len[s] : len_max;
+  if (len > len_max) len = len_max;
+  if (len < 1) return;
+  const int64_t b = blk_begin < 0 ? (len - 1) / B : blk_begin + blockIdx.x;
+  const int64_t t0 = b * B;
+  if (t0 >= len || b >= nb_max) return;
+  const int64_t t1 = t0 + B < len ? t0 + B : len;
+  const int R = 256 / d_idx;
+  const int tid = threadIdx.x;
+  const int col = tid % d_idx, r = tid / d_idx;
+  int m = INT32_MIN;
+  if (r < R) {
+    const float *src = idx_k + ((int64_t)s * len_max) * d_idx;
+    for (int64_t t = t0 + r; t < t1; t += R) m = max(m, f2key(src[t * d_idx + col]));
+  }
+  red[tid] = m;
+  __syncthreads();
+  if (tid < d_idx) {
+    for (int rr = 1; rr < R; ++rr) m = max(m, red[rr * d_idx + tid]);
+    kmax[((int64_t)s * nb_max + b) * d_idx + tid] = key2f(m);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
+                       const int64_t *seq_len, int32_t d_idx, int32_t block,
+                       int64_t blk_begin, int64_t blk_end, float *kmax,
+                       int64_t nb_max, hipStream_t st) {
+  const int64_t nblk = blk_begin < 0 ? 1 : blk_end - blk_begin;
+  dim3 grid((unsigned)nblk, (unsigned)n_seq);
+  if (d_idx % 4 == 0)
+    hipLaunchKernelGGL(pool_vec4, grid, dim3(256), 0, st, idx_k, len_max,
+                       seq_len, d_idx, block, blk_begin, kmax, nb_max);
+  else
+    hipLaunchKernelGGL(pool_scalar, grid, dim3(256), 0, st, idx_k, len_max,
+                       seq_len, d_idx, block, blk_begin, kmax, nb_max);
+  return hipGetLastError();
+}
+
+}  // namespace msa

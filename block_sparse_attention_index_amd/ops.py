@@ -1,0 +1,285 @@
+"""Thin Python binding of ``libmsa.so`` (the C ABI in ``include/msa.h``).
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: it checks devices, dtypes and contiguity, allocates outputs and
+workspaces with torch when the caller does not pass them, and passes raw
+device pointers plus torch's current HIP stream.  Every step of the path runs
+in the library's HIP kernels.  If the library is not built, every call raises:
+there is no other implementation behind these names.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmsa.so")
+_lib = None
+
+MSA_F32, MSA_BF16 = 0, 1
+_STATUS = {0: "MSA_OK", -1: "MSA_ERR_INVALID_ARG", -2: "MSA_ERR_UNSUPPORTED",
+           -3: "MSA_ERR_WORKSPACE", -4: "MSA_ERR_HIP"}
+
+ENTRY_POINTS = (
+    "msa_status_string", "msa_index_pool", "msa_index_topk",
+    "msa_topk_decode_workspace_bytes", "msa_index_topk_decode",
+    "msa_invert_workspace_bytes", "msa_invert_selection",
+    "msa_prefill_workspace_bytes", "msa_sparse_gqa_prefill",
+    "msa_decode_workspace_bytes", "msa_sparse_gqa_decode",
+)
+
+
+class MsaError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} returned {status} ({_STATUS.get(status, '?')})")
+
+
+def load():
+    """Load ``libmsa.so`` (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m "
+            "block_sparse_attention_index_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    sz = ctypes.c_size_t
+    sig = {
+        "msa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "msa_index_pool": ([P, i32, i64, P, i32, i32, i64, i64, P, i64, P], ctypes.c_int),
+        "msa_index_topk": ([P, i64, i64, P, i64, i32, i32, i32, P, P], ctypes.c_int),
+        "msa_topk_decode_workspace_bytes": ([i32, i64, i32], sz),
+        "msa_index_topk_decode": ([P, i32, P, P, i64, i32, i32, i32, P, P, sz, P],
+                                  ctypes.c_int),
+        "msa_invert_workspace_bytes": ([i64, i32, i64], sz),
+        "msa_invert_selection": ([P, i64, i32, i64, P, P, P, P, sz, P], ctypes.c_int),
+        "msa_prefill_workspace_bytes": ([i64, i64, i32, i32, i32, i32], sz),
+        "msa_sparse_gqa_prefill": ([P, P, P, i32, i64, i64, i64, i32, i32, i32, i32,
+                                    P, i32, P, P, P, f32, P, P, P, sz, P],
+                                   ctypes.c_int),
+        "msa_decode_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
+        "msa_sparse_gqa_decode": ([P, P, P, i32, i32, i64, P, i32, i32, i32, i32, P,
+                                   i32, f32, P, P, P, sz, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MsaError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ws(nbytes: int, like: torch.Tensor, ws):
+    if ws is not None:
+        _dev(ws, "ws", torch.uint8)
+        return ws
+    return torch.empty(max(1, nbytes), dtype=torch.uint8, device=like.device)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MSA_F32
+    if t.dtype == torch.bfloat16:
+        return MSA_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def status_string(status: int) -> str:
+    return load().msa_status_string(status).decode()
+
+
+# --------------------------------------------------------------------------
+# Index branch
+# --------------------------------------------------------------------------
+def msa_index_pool(idx_k: torch.Tensor, block: int, kmax: torch.Tensor | None = None,
+                   seq_len: torch.Tensor | None = None, blk_begin: int = 0,
+                   blk_end: int | None = None, nb_max: int | None = None):
+    """Block max-pool of index keys.  ``idx_k`` [L, d_idx] or [n_seq, L, d_idx]
+    fp32 -> ``kmax`` [nb_max, d_idx] or [n_seq, nb_max, d_idx] fp32.
+    ``blk_begin < 0`` pools only each sequence's last block (decode append)."""
+    _dev(idx_k, "idx_k", torch.float32)
+    batched = idx_k.dim() == 3
+    n_seq = idx_k.shape[0] if batched else 1
+    L, d = idx_k.shape[-2], idx_k.shape[-1]
+    nb = -(-L // block)
+    nb_max = nb if nb_max is None else nb_max
+    if kmax is None:
+        shape = (n_seq, nb_max, d) if batched else (nb_max, d)
+        kmax = torch.empty(shape, dtype=torch.float32, device=idx_k.device)
+    _dev(kmax, "kmax", torch.float32)
+    if seq_len is not None:
+        _dev(seq_len, "seq_len", torch.int64)
+    if blk_end is None:
+        blk_end = nb
+    st = load().msa_index_pool(_ptr(idx_k), n_seq, L, _ptr(seq_len), d, block,
+                               blk_begin, blk_end, _ptr(kmax), nb_max, _stream(idx_k))
+    _check("msa_index_pool", st)
+    return kmax
+
+
+def msa_index_topk(idx_q: torch.Tensor, kmax: torch.Tensor, block: int, topk: int,
+                   q_pos0: int = 0, sel: torch.Tensor | None = None):
+    """Prefill causal top-K: ``idx_q`` [n_q, d_idx] at positions q_pos0 + i,
+    ``kmax`` [nb, d_idx] -> ``sel`` [n_q, topk] int32 (ascending, -1 padded)."""
+    _dev(idx_q, "idx_q", torch.float32)
+    _dev(kmax, "kmax", torch.float32)
+    n_q, d = idx_q.shape
+    if sel is None:
+        sel = torch.empty((n_q, topk), dtype=torch.int32, device=idx_q.device)
+    _dev(sel, "sel", torch.int32)
+    st = load().msa_index_topk(_ptr(idx_q), n_q, q_pos0, _ptr(kmax), kmax.shape[0],
+                               d, block, topk, _ptr(sel), _stream(idx_q))
+    _check("msa_index_topk", st)
+    return sel
+
+
+def msa_index_topk_decode(idx_q: torch.Tensor, seq_len: torch.Tensor,
+                          kmax: torch.Tensor, block: int, topk: int,
+                          sel: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Decode top-K: one query per sequence at position seq_len[s]-1.
+    ``idx_q`` [n_seq, d_idx], ``kmax`` [n_seq, nb_max, d_idx] -> ``sel`` [n_seq, topk]."""
+    _dev(idx_q, "idx_q", torch.float32)
+    _dev(seq_len, "seq_len", torch.int64)
+    _dev(kmax, "kmax", torch.float32)
+    n_seq, d = idx_q.shape
+    nb_max = kmax.shape[1]
+    lib = load()
+    ws = _ws(lib.msa_topk_decode_workspace_bytes(n_seq, nb_max, topk), idx_q, ws)
+    if sel is None:
+        sel = torch.empty((n_seq, topk), dtype=torch.int32, device=idx_q.device)
+    _dev(sel, "sel", torch.int32)
+    st = lib.msa_index_topk_decode(_ptr(idx_q), n_seq, _ptr(seq_len), _ptr(kmax),
+                                   nb_max, d, block, topk, _ptr(sel), _ptr(ws),
+                                   ws.numel(), _stream(idx_q))
+    _check("msa_index_topk_decode", st)
+    return sel
+
+
+def msa_invert_selection(sel: torch.Tensor, n_blocks: int, row_ptr=None, q_list=None,
+                         slot=None, ws=None):
+    """CSR of queries per block: returns ``(row_ptr [nb+1], q_list [n_q*K]
+    (capacity; the first row_ptr[-1] entries are used), slot [n_q, K])``."""
+    _dev(sel, "sel", torch.int32)
+    n_q, topk = sel.shape
+    dev = sel.device
+    lib = load()
+    ws = _ws(lib.msa_invert_workspace_bytes(n_q, topk, n_blocks), sel, ws)
+    if row_ptr is None:
+        row_ptr = torch.empty(n_blocks + 1, dtype=torch.int32, device=dev)
+    if q_list is None:
+        q_list = torch.empty(max(1, n_q * topk), dtype=torch.int32, device=dev)
+    if slot is None:
+        slot = torch.empty((n_q, topk), dtype=torch.int32, device=dev)
+    for t, nm in ((row_ptr, "row_ptr"), (q_list, "q_list"), (slot, "slot")):
+        _dev(t, nm, torch.int32)
+    st = lib.msa_invert_selection(_ptr(sel), n_q, topk, n_blocks, _ptr(row_ptr),
+                                  _ptr(q_list), _ptr(slot), _ptr(ws), ws.numel(),
+                                  _stream(sel))
+    _check("msa_invert_selection", st)
+    return row_ptr, q_list, slot
+
+
+# --------------------------------------------------------------------------
+# Sparse branch
+# --------------------------------------------------------------------------
+def prefill_workspace_bytes(q_pos0: int, n_q: int, hq: int, d: int, block: int,
+                            topk: int) -> int:
+    return load().msa_prefill_workspace_bytes(q_pos0, n_q, hq, d, block, topk)
+
+
+def msa_sparse_gqa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           sel: torch.Tensor, row_ptr: torch.Tensor,
+                           q_list: torch.Tensor, slot: torch.Tensor, block: int,
+                           scale: float | None = None, q_pos0: int = 0,
+                           o=None, lse=None, ws=None, want_lse: bool = True):
+    """Sparse GQA prefill, KV outer.  ``q`` [n_q, Hq, d]; ``k``/``v``
+    [Hkv, kv_stride, d] (fp32 or bf16); returns ``(o [n_q, Hq, d] fp32,
+    lse [n_q, Hq] fp32 or None)``."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    for t, nm in ((sel, "sel"), (row_ptr, "row_ptr"), (q_list, "q_list"),
+                  (slot, "slot")):
+        _dev(t, nm, torch.int32)
+    n_q, hq, d = q.shape
+    hkv, kv_stride, _ = k.shape
+    topk = sel.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load()
+    ws = _ws(lib.msa_prefill_workspace_bytes(q_pos0, n_q, hq, d, block, topk), q, ws)
+    if o is None:
+        o = torch.empty((n_q, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, hq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.float32)
+    st = lib.msa_sparse_gqa_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), kv_stride, q_pos0, n_q, hq, hkv,
+        d, block, _ptr(sel), topk, _ptr(row_ptr), _ptr(q_list), _ptr(slot), scale,
+        _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(q))
+    _check("msa_sparse_gqa_prefill", st)
+    return o, lse
+
+
+def decode_workspace_bytes(n_seq: int, hq: int, d: int, block: int, topk: int) -> int:
+    return load().msa_decode_workspace_bytes(n_seq, hq, d, block, topk)
+
+
+def msa_sparse_gqa_decode(q: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, seq_len: torch.Tensor,
+                          sel: torch.Tensor, block: int, scale: float | None = None,
+                          o=None, lse=None, ws=None, want_lse: bool = True):
+    """Sparse GQA decode.  ``q`` [n_seq, Hq, d]; caches [n_seq, Hkv, len_max, d];
+    returns ``(o [n_seq, Hq, d] fp32, lse [n_seq, Hq] fp32 or None)``."""
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm)
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q and the caches must share a dtype")
+    _dev(seq_len, "seq_len", torch.int64)
+    _dev(sel, "sel", torch.int32)
+    n_seq, hq, d = q.shape
+    _, hkv, len_max, _ = k_cache.shape
+    topk = sel.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load()
+    ws = _ws(lib.msa_decode_workspace_bytes(n_seq, hq, d, block, topk), q, ws)
+    if o is None:
+        o = torch.empty((n_seq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((n_seq, hq), dtype=torch.float32, device=q.device)
+    st = lib.msa_sparse_gqa_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), n_seq, len_max,
+        _ptr(seq_len), hq, hkv, d, block, _ptr(sel), topk, scale, _ptr(o), _ptr(lse),
+        _ptr(ws), ws.numel(), _stream(q))
+    _check("msa_sparse_gqa_decode", st)
+    return o, lse

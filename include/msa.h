@@ -1,0 +1,203 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) MiniMax Sparse Attention hot path.
+ *
+ * Two stages, after the pages:
+ *   index branch  -- a single-head index key is max-pooled per KV block, each
+ *                    query's index vector is scored against those summaries,
+ *                    and each query keeps its causal top-K blocks
+ *                    ([YLY] paragraph "索引分支（Index Branch）");
+ *   sparse branch -- standard GQA over the selected blocks only
+ *                    ([YLY] paragraph "稀疏分支（Sparse Branch）"), organised
+ *                    as "KV outer, gather Q": each KV block is read once and
+ *                    applied to every query that chose it
+ *                    ([CXT] section 2.2 "KV Outer Gather Q：MSA 的关键设计"),
+ *                    with per-block partial outputs merged by log-sum-exp.
+ * Pages:
+ *   [YLY] "MiniMax M3模型算力成本大幅降低原因深度解析",
+ *         youleyou.com/wenzhang/3016623.html
+ *   [CXT] "MiniMax M3 深度实战：当稀疏注意力打破百万 Token 墙 ...",
+ *         chenxutan.com/d/3746.html
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers to dense row-major arrays owned by
+ *     the caller.  The library never allocates, frees or keeps caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it and return at once.
+ *   - Return value: MSA_OK, or a negative msa_status.  Arguments are checked
+ *     before anything is enqueued; on an error nothing is enqueued and no
+ *     output is touched.  MSA_ERR_HIP reports a failed launch.  Faults inside
+ *     kernels surface at the caller's next synchronisation, not here.
+ *   - Outputs are fully overwritten (no pre-zeroing needed) unless a call
+ *     says otherwise.  Workspaces are scratch: their contents on entry do not
+ *     matter and are undefined on exit.
+ *   - Inputs must be finite.  Calls on one stream are ordered; calls that
+ *     share a workspace must not overlap.  No global mutable state:
+ *     calls from several host threads are safe.
+ *   - Block size B: a multiple of 16, at most 4096.  Top-K: 1 <= K <= 64.
+ *     Index dimension d_idx: 1..1024 (multiples of 4 up to 1024, any value up
+ *     to 256).
+ *   - Positions count from 0.  own(p) = p / B is a token's own block.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes */
+  MSA_ERR_UNSUPPORTED = -2, /* no kernel built for this (dtype, d, B, ...)  */
+  MSA_ERR_WORKSPACE = -3,   /* workspace smaller than the size query says  */
+  MSA_ERR_HIP = -4          /* a HIP launch or runtime call failed         */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *msa_status_string(int status);
+
+/* --------------------------------------------------------------------------
+ * msa_index_pool -- block max-pool of index keys.  [YLY] "索引分支（Index Branch）"
+ *
+ *   kmax[s][b][c] = max over t in [b*B, min(b*B+B, len_s)) of idx_k[s][t][c]
+ *
+ * for every sequence s and every block b of the requested range that holds
+ * at least one valid token (b*B < len_s); other entries of kmax are left
+ * untouched.  The max is exact and uses the total order -0 < +0.
+ *
+ *   idx_k    [n_seq][len_max][d_idx] fp32
+ *   seq_len  device int64 [n_seq], 1 <= len_s <= len_max; NULL = all len_max
+ *   blocks   [blk_begin, blk_end) with 0 <= blk_begin < blk_end <= nb_max;
+ *            blk_begin < 0 selects, per sequence, only the block holding its
+ *            last token (len_s - 1) / B -- the block a decode step appends to
+ *   kmax     [n_seq][nb_max][d_idx] fp32, nb_max >= ceil(len_max / B)
+ * ------------------------------------------------------------------------ */
+int msa_index_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
+                   const int64_t *seq_len, int32_t d_idx, int32_t block,
+                   int64_t blk_begin, int64_t blk_end, float *kmax,
+                   int64_t nb_max, void *stream);
+
+/* --------------------------------------------------------------------------
+ * msa_index_topk -- prefill scores and causal top-K for one sequence.
+ * [YLY] "索引分支（Index Branch）"; [CXT] section 3.3 "Prefilling 与 Decoding
+ * 的差异化优化" (prefill scores every block for every query).
+ *
+ * Query i sits at position p = q_pos0 + i, own = p / B.  Its candidates are
+ * the blocks b < own, scored in fp32 by s[b] = sum_c idx_q[i][c]*kmax[b][c];
+ * it keeps the best min(K-1, own) by (score desc, block asc), adds own, and
+ * writes them ascending to sel[i][0..], padding with -1 up to K.
+ *
+ *   idx_q  [n_q][d_idx] fp32;  kmax [nb][d_idx] fp32 with
+ *          nb >= own of the last query + 1
+ *   sel    [n_q][K] int32 (output)
+ * ------------------------------------------------------------------------ */
+int msa_index_topk(const float *idx_q, int64_t n_q, int64_t q_pos0,
+                   const float *kmax, int64_t nb, int32_t d_idx, int32_t block,
+                   int32_t topk, int32_t *sel, void *stream);
+
+/* --------------------------------------------------------------------------
+ * msa_index_topk_decode -- the same selection for one new query per
+ * sequence ([CXT] section 3.3: decode scores only the new token).  Sequence
+ * s's query sits at position seq_len[s] - 1 (its index key already pooled).
+ *
+ *   idx_q    [n_seq][d_idx] fp32
+ *   seq_len  device int64 [n_seq], 1 <= len_s <= nb_max * B
+ *   kmax     [n_seq][nb_max][d_idx] fp32
+ *   sel      [n_seq][K] int32 (output)
+ *   ws       device scratch of msa_topk_decode_workspace_bytes() bytes
+ * ------------------------------------------------------------------------ */
+size_t msa_topk_decode_workspace_bytes(int32_t n_seq, int64_t nb_max,
+                                       int32_t topk);
+int msa_index_topk_decode(const float *idx_q, int32_t n_seq,
+                          const int64_t *seq_len, const float *kmax,
+                          int64_t nb_max, int32_t d_idx, int32_t block,
+                          int32_t topk, int32_t *sel, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
+ * msa_invert_selection -- the queries that hit each KV block, as CSR.
+ * [CXT] section 2.2: the KV-outer loop needs, per block, the queries that
+ * chose it.  Histogram, prefix sum and a deterministic scatter:
+ *
+ *   row_ptr[b+1] - row_ptr[b] = |{i : b in sel[i]}|,  row_ptr[0] = 0
+ *   q_list[row_ptr[b] ..]     = those i, ascending
+ *   slot[i][k]                = position of (i, sel[i][k]) in q_list,
+ *                               -1 where sel[i][k] == -1
+ *
+ *   sel      [n_q][K] int32, entries -1 or in [0, n_blocks), no repeats in a row
+ *   row_ptr  [n_blocks+1] int32;  q_list [n_q*K] int32 (capacity);
+ *   slot     [n_q][K] int32 (outputs); n_q * K < 2^31
+ *   ws       device scratch of msa_invert_workspace_bytes() bytes
+ * ------------------------------------------------------------------------ */
+size_t msa_invert_workspace_bytes(int64_t n_q, int32_t topk, int64_t n_blocks);
+int msa_invert_selection(const int32_t *sel, int64_t n_q, int32_t topk,
+                         int64_t n_blocks, int32_t *row_ptr, int32_t *q_list,
+                         int32_t *slot, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* --------------------------------------------------------------------------
+ * msa_sparse_gqa_prefill -- GQA over each query's selected blocks, KV outer.
+ * [YLY] "稀疏分支（Sparse Branch）"; [CXT] sections 2.2 and 2.3.
+ *
+ * Query i (position p = q_pos0 + i), head h, KV head g = h / (Hq/Hkv):
+ *   keys  = union over b in sel[i] of {t : b*B <= t <= min(b*B+B-1, p)}
+ *   o     = softmax(scale * q.k_t) . v_t over those keys,
+ *   lse   = natural log of sum_t exp(scale * q.k_t).
+ * Each (block, KV head) pair is streamed once per group of queries that chose
+ * it; every non-own block yields a partial (o, lse) per (query, head) in the
+ * workspace, and the own-block pass merges them by log-sum-exp.
+ *
+ *   q     [n_q][Hq][d]            dtype (fp32 or bf16 bits)
+ *   k, v  [Hkv][kv_stride][d]     dtype; q_pos0 + n_q <= kv_stride
+ *   sel   [n_q][K] from msa_index_topk with the same q_pos0 and B;
+ *         row_ptr, q_list, slot from msa_invert_selection(sel, n_q, K,
+ *         ceil((q_pos0+n_q)/B)).  Results are undefined for other inputs
+ *         (out-of-range entries are skipped, never dereferenced).
+ *   o     [n_q][Hq][d] fp32;  lse [n_q][Hq] fp32 (may be NULL)
+ *   ws    device scratch of msa_prefill_workspace_bytes() bytes
+ *   Supported: fp32 and bf16; d in {64, 128, 256}; Hq/Hkv <= 16.
+ * ------------------------------------------------------------------------ */
+size_t msa_prefill_workspace_bytes(int64_t q_pos0, int64_t n_q, int32_t hq,
+                                   int32_t d, int32_t block, int32_t topk);
+int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
+                           int32_t dtype, int64_t kv_stride, int64_t q_pos0,
+                           int64_t n_q, int32_t hq, int32_t hkv, int32_t d,
+                           int32_t block, const int32_t *sel, int32_t topk,
+                           const int32_t *row_ptr, const int32_t *q_list,
+                           const int32_t *slot, float scale, float *o,
+                           float *lse, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* --------------------------------------------------------------------------
+ * msa_sparse_gqa_decode -- one new query per sequence over its selected
+ * blocks ([CXT] section 3.3, decode), split over (block, key chunk) and
+ * merged by log-sum-exp.  Sequence s's query sits at position seq_len[s]-1;
+ * its own key and value are already in the cache.
+ *
+ *   q        [n_seq][Hq][d] dtype
+ *   k_cache, v_cache  [n_seq][Hkv][len_max][d] dtype
+ *   seq_len  device int64 [n_seq], 1 <= len_s <= len_max
+ *   sel      [n_seq][K] int32 from msa_index_topk_decode
+ *   o        [n_seq][Hq][d] fp32;  lse [n_seq][Hq] fp32 (may be NULL)
+ *   ws       device scratch of msa_decode_workspace_bytes() bytes
+ *   Supported: fp32 and bf16; d in {64, 128, 256}; Hq/Hkv <= 16.
+ * ------------------------------------------------------------------------ */
+size_t msa_decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t d,
+                                  int32_t block, int32_t topk);
+int msa_sparse_gqa_decode(const void *q, const void *k_cache,
+                          const void *v_cache, int32_t dtype, int32_t n_seq,
+                          int64_t len_max, const int64_t *seq_len, int32_t hq,
+                          int32_t hkv, int32_t d, int32_t block,
+                          const int32_t *sel, int32_t topk, float scale,
+                          float *o, float *lse, void *ws, size_t ws_bytes,
+                          void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H */

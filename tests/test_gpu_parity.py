@@ -1,0 +1,276 @@
+"""Device parity: every entry point against the CPU oracle (needs a GPU).
+
+Each stage is fed oracle-produced inputs (pooled summaries, selections, CSR)
+so the device kernels are compared one by one; the end-to-end test then runs
+the whole device pipeline and compares what is unique.  Acceptance:
+pool and CSR bit-exact; selections bit-exact except flagged near-ties;
+outputs within 1e-4 (fp32 inputs) or 1e-2 (bf16 inputs) max-abs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_index_amd import ops, pipeline, synth
+from helpers import TOL_BF16, TOL_F32, check_selection, max_abs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# --------------------------------------------------------------------------
+# pool
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("L,B,d", [(4096, 64, 64), (1000, 16, 128), (777, 128, 24),
+                                   (1, 16, 4), (5000, 512, 128), (300, 32, 1024)])
+def test_pool_bit_exact(orc, L, B, d):
+    _say(f"pool L={L} B={B} d={d}")
+    g = torch.Generator().manual_seed(L * 7 + B + d)
+    x = torch.randn(L, d, generator=g)
+    x[::5, 0] = -0.0
+    x[1::5, 0] = 0.0
+    kmax = ops.msa_index_pool(x.to(DEV), B)
+    want = orc.pool(x.numpy(), B)
+    assert np.array_equal(_np(kmax).view(np.uint32), want.view(np.uint32))
+
+
+def test_pool_batched_ragged_and_last_block(orc):
+    n, Lmax, B, d = 3, 1000, 64, 128
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(n, Lmax, d, generator=g)
+    lens = [1000, 513, 64]
+    nb_max = 17
+    kmax = torch.full((n, nb_max, d), float("nan"), device=DEV)
+    seq_len = torch.tensor(lens, dtype=torch.int64, device=DEV)
+    ops.msa_index_pool(x.to(DEV), B, kmax=kmax, seq_len=seq_len, nb_max=nb_max)
+    got = _np(kmax)
+    for s, L in enumerate(lens):
+        nb = -(-L // B)
+        assert np.array_equal(got[s, :nb], orc.pool(x[s, :L].numpy(), B))
+        assert np.all(np.isnan(got[s, nb:])), "blocks past the sequence stay untouched"
+    # decode append: raise the newest token, re-pool only each last block
+    x2 = x.clone()
+    for s, L in enumerate(lens):
+        x2[s, L - 1] += 3.0
+    ops.msa_index_pool(x2.to(DEV), B, kmax=kmax, seq_len=seq_len, blk_begin=-1,
+                       nb_max=nb_max)
+    got = _np(kmax)
+    for s, L in enumerate(lens):
+        nb = -(-L // B)
+        assert np.array_equal(got[s, :nb], orc.pool(x2[s, :L].numpy(), B))
+
+
+# --------------------------------------------------------------------------
+# top-K (prefill)
+# --------------------------------------------------------------------------
+def _topk_case(orc, idx_q, idx_k, B, K, q_pos0=0):
+    kmax = orc.pool(idx_k, B)
+    n_q = idx_q.shape[0]
+    pos = np.arange(q_pos0, q_pos0 + n_q, dtype=np.int64)
+    sel_o, gr, ga, eb = orc.select(idx_q, pos, kmax, B, K)
+    sel_d = ops.msa_index_topk(torch.from_numpy(idx_q).to(DEV),
+                               torch.from_numpy(kmax).to(DEV), B, K, q_pos0=q_pos0)
+    nf, nm = check_selection(_np(sel_d), sel_o, gr, ga, eb, idx_q, kmax, pos, B)
+    _say(f"  near-ties flagged {nf}, device/oracle differing rows {nm}")
+    return nf, nm
+
+
+def test_topk_tiny_config(orc):
+    cfg = synth.CONFIGS["tiny"]
+    _say("topk tiny")
+    x = synth.sequence_inputs(cfg, "cpu", 0)
+    _topk_case(orc, x["idx_q"].numpy(), x["idx_k"].numpy(), cfg.block, cfg.topk)
+
+
+@pytest.mark.parametrize("T,B,K,d,q0,hot", [
+    (4096, 64, 16, 128, 0, 8),      # the 32K-token config's shape, scaled down
+    (3000, 16, 1, 32, 0, 0),        # K = 1: own block only
+    (2500, 32, 64, 24, 100, 0),     # K = 64 (max), d_idx not a multiple of 64
+    (5000, 128, 16, 128, 1234, 6),  # chunk not aligned to anything
+])
+def test_topk_shapes(orc, T, B, K, d, q0, hot):
+    _say(f"topk T={T} B={B} K={K} d={d} q0={q0}")
+    cfg = synth.Config("t", T, "f32", 1, 1, 64, d, B, K, hot)
+    x = synth.sequence_inputs(cfg, "cpu", 1)
+    _topk_case(orc, x["idx_q"].numpy()[q0:], x["idx_k"].numpy(), B, K, q_pos0=q0)
+
+
+def test_topk_ties_go_low(orc):
+    # every summary identical: all scores tie exactly -> blocks 0..K-2
+    B, K, nb, d = 64, 5, 40, 16
+    kmax = np.tile(np.random.default_rng(0).standard_normal((1, d)).astype(np.float32),
+                   (nb, 1))
+    idx_q = np.random.default_rng(1).standard_normal((nb * B, d)).astype(np.float32)
+    sel = _np(ops.msa_index_topk(torch.from_numpy(idx_q).to(DEV),
+                                 torch.from_numpy(kmax).to(DEV), B, K))
+    for p in range(nb * B):
+        own = p // B
+        m = min(K - 1, own)
+        assert sel[p].tolist() == list(range(m)) + [own] + [-1] * (K - m - 1)
+
+
+# --------------------------------------------------------------------------
+# CSR
+# --------------------------------------------------------------------------
+def _invert_case(orc, sel, nb):
+    ro, qo, so = orc.invert(sel, nb)
+    rd, qd, sd = ops.msa_invert_selection(torch.from_numpy(sel).to(DEV), nb)
+    rd, qd, sd = _np(rd), _np(qd), _np(sd)
+    assert np.array_equal(rd, ro)
+    assert np.array_equal(qd[:ro[-1]], qo)
+    assert np.array_equal(sd, so)
+
+
+def test_invert_tiny_selection(orc):
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.sequence_inputs(cfg, "cpu", 0)
+    kmax = orc.pool(x["idx_k"].numpy(), cfg.block)
+    pos = np.arange(cfg.T, dtype=np.int64)
+    sel, *_ = orc.select(x["idx_q"].numpy(), pos, kmax, cfg.block, cfg.topk)
+    _invert_case(orc, sel, cfg.nb)
+
+
+@pytest.mark.parametrize("n_q,nb,K", [(5000, 9000, 6), (1, 1, 1), (2049, 3, 3),
+                                      (70000, 300, 16)])
+def test_invert_arbitrary_sets(orc, n_q, nb, K):
+    _say(f"invert n_q={n_q} nb={nb} K={K}")
+    rng = np.random.default_rng(n_q + nb)
+    sel = np.full((n_q, K), -1, np.int32)
+    for i in range(n_q):
+        n = rng.integers(0, min(K, nb) + 1)
+        sel[i, :n] = np.sort(rng.choice(nb, size=n, replace=False))
+    _invert_case(orc, sel, nb)
+
+
+# --------------------------------------------------------------------------
+# sparse prefill
+# --------------------------------------------------------------------------
+def _prefill_case(orc, cfg, q_pos0=0, n_q=None, sample=None, seed=0):
+    x = synth.sequence_inputs(cfg, "cpu", seed, length=cfg.T)
+    T, B, K = cfg.T, cfg.block, cfg.topk
+    n_q = T - q_pos0 if n_q is None else n_q
+    kmax = orc.pool(x["idx_k"].numpy(), B)
+    pos = np.arange(q_pos0, q_pos0 + n_q, dtype=np.int64)
+    sel, *_ = orc.select(x["idx_q"].numpy()[q_pos0:q_pos0 + n_q], pos, kmax, B, K)
+    nbc = -(-(q_pos0 + n_q) // B)
+    row_ptr, q_list, slot = orc.invert(sel, nbc)
+    dt = lambda a: torch.from_numpy(a).to(DEV)
+    q = x["q"][q_pos0:q_pos0 + n_q].contiguous()
+    o, lse = ops.msa_sparse_gqa_prefill(
+        q.to(DEV), x["k"].to(DEV), x["v"].to(DEV), dt(sel), dt(row_ptr),
+        dt(np.concatenate([q_list, np.zeros(1, np.int32)])), dt(slot), B, cfg.scale,
+        q_pos0=q_pos0)
+    o, lse = _np(o), _np(lse)
+    rows = np.arange(n_q) if sample is None else np.unique(np.concatenate(
+        [np.arange(min(n_q, B)), np.arange(max(0, n_q - B), n_q),
+         np.random.default_rng(seed).choice(n_q, size=min(n_q, sample), replace=False)]))
+    hq = synth.host(q)
+    oo, lo, _ = orc.attend(hq, synth.host(x["k"]), synth.host(x["v"]), rows,
+                           pos[rows], sel[rows], B, cfg.scale,
+                           0 if cfg.dtype == "f32" else 1)
+    tol = TOL_F32 if cfg.dtype == "f32" else TOL_BF16
+    eo, el = max_abs(o[rows], oo), max_abs(lse[rows], lo)
+    _say(f"  prefill {cfg.name}: rows {len(rows)} max|do| {eo:.3g} max|dlse| {el:.3g}")
+    assert eo <= tol and el <= tol
+
+
+def test_prefill_tiny_config_full(orc):
+    _say("prefill tiny (all 4096 queries)")
+    _prefill_case(orc, synth.CONFIGS["tiny"])
+
+
+@pytest.mark.parametrize("name,over,q0,nq,sample", [
+    ("bf16-p32k-shape", dict(T=4096, n_hot=8), 0, None, 600),
+    ("bf16-ragged-chunk", dict(T=3000, n_hot=5, block=128, topk=6), 1000, 1500, 500),
+    ("f32-G8-d128", dict(T=2000, dtype="f32", n_hot=3, topk=5, block=64), 0, None, 400),
+    ("bf16-B512", dict(T=5000, block=512, topk=4, n_hot=2), 0, None, 300),
+    ("bf16-B16-K1", dict(T=700, block=16, topk=1, n_hot=0), 0, None, None),
+])
+def test_prefill_shapes(orc, name, over, q0, nq, sample):
+    _say(f"prefill {name}")
+    cfg = synth.CONFIGS["p32k"].replace(name=name, **over)
+    _prefill_case(orc, cfg, q_pos0=q0, n_q=nq, sample=sample)
+
+
+def test_prefill_small_heads_d64(orc):
+    _say("prefill G=2 d=64 bf16")
+    cfg = synth.Config("g2", 1500, "bf16", 4, 2, 64, 32, 32, 5, 2)
+    _prefill_case(orc, cfg)
+
+
+# --------------------------------------------------------------------------
+# decode
+# --------------------------------------------------------------------------
+def test_decode_small(orc):
+    cfg = synth.Config("dec-small", 3000, "bf16", 16, 2, 128, 128, 64, 8, 4,
+                       n_seq=3, mode="decode")
+    _say("decode small (3 sequences, ragged lengths)")
+    x = synth.decode_inputs(cfg, "cpu", 0)
+    lens = np.array([3000, 2049, 100], np.int64)
+    B, K = cfg.block, cfg.topk
+    nb_max = cfg.nb
+    seq_len = torch.from_numpy(lens).to(DEV)
+    # pool (bit-exact per sequence)
+    kmax_d = torch.full((cfg.n_seq, nb_max, cfg.d_idx), float("nan"), device=DEV)
+    ops.msa_index_pool(x["idx_k"].to(DEV), B, kmax=kmax_d, seq_len=seq_len, nb_max=nb_max)
+    kmax_o = np.zeros((cfg.n_seq, nb_max, cfg.d_idx), np.float32)
+    for s, L in enumerate(lens):
+        nb = -(-L // B)
+        kmax_o[s, :nb] = orc.pool(x["idx_k"][s, :L].numpy(), B)
+        assert np.array_equal(_np(kmax_d)[s, :nb], kmax_o[s, :nb])
+    # top-K on the oracle's summaries
+    sel_d = _np(ops.msa_index_topk_decode(x["idx_q"].to(DEV), seq_len,
+                                          torch.from_numpy(kmax_o).to(DEV), B, K))
+    for s, L in enumerate(lens):
+        pos = np.array([L - 1])
+        so, gr, ga, eb = orc.select(x["idx_q"][s:s + 1].numpy(), pos, kmax_o[s], B, K)
+        check_selection(sel_d[s:s + 1], so, gr, ga, eb, x["idx_q"][s:s + 1].numpy(),
+                        kmax_o[s], pos, B)
+    # attention on the oracle's selection
+    sels = []
+    for s, L in enumerate(lens):
+        so, *_ = orc.select(x["idx_q"][s:s + 1].numpy(), np.array([L - 1]), kmax_o[s], B, K)
+        sels.append(so[0])
+    sel_o = np.stack(sels).astype(np.int32)
+    o, lse = ops.msa_sparse_gqa_decode(x["q"].to(DEV), x["k_cache"].to(DEV),
+                                       x["v_cache"].to(DEV), seq_len,
+                                       torch.from_numpy(sel_o).to(DEV), B, cfg.scale)
+    o, lse = _np(o), _np(lse)
+    for s, L in enumerate(lens):
+        oo, lo, _ = orc.attend(synth.host(x["q"][s:s + 1]), synth.host(x["k_cache"][s]),
+                               synth.host(x["v_cache"][s]), np.array([0]),
+                               np.array([L - 1]), sel_o[s:s + 1], B, cfg.scale, 1)
+        eo, el = max_abs(o[s], oo[0]), max_abs(lse[s], lo[0])
+        _say(f"  seq {s} len {L}: max|do| {eo:.3g} max|dlse| {el:.3g}")
+        assert eo <= TOL_BF16 and el <= TOL_BF16
+
+
+# --------------------------------------------------------------------------
+# end to end on the device
+# --------------------------------------------------------------------------
+def test_pipeline_end_to_end_tiny(orc):
+    cfg = synth.CONFIGS["tiny"]
+    _say("pipeline tiny end to end")
+    x = synth.sequence_inputs(cfg, "cpu", 0)
+    d = {k: v.to(DEV) for k, v in x.items() if k != "hot"}
+    o, lse, sel = pipeline.prefill(d["q"], d["k"], d["v"], d["idx_q"], d["idx_k"],
+                                   cfg.block, cfg.topk, cfg.scale)
+    kmax = orc.pool(x["idx_k"].numpy(), cfg.block)
+    pos = np.arange(cfg.T, dtype=np.int64)
+    so, gr, ga, eb = orc.select(x["idx_q"].numpy(), pos, kmax, cfg.block, cfg.topk)
+    sel = _np(sel)
+    nf, nm = check_selection(sel, so, gr, ga, eb, x["idx_q"].numpy(), kmax, pos, cfg.block)
+    same = np.all(sel == so, axis=1)
+    oo, lo, _ = orc.attend(synth.host(x["q"]), synth.host(x["k"]), synth.host(x["v"]),
+                           pos, pos, so, cfg.block, cfg.scale, 0)
+    eo = max_abs(_np(o)[same], oo[same])
+    el = max_abs(_np(lse)[same], lo[same])
+    _say(f"  flagged {nf}, differing {nm}; max|do| {eo:.3g} max|dlse| {el:.3g}")
+    assert eo <= TOL_F32 and el <= TOL_F32
