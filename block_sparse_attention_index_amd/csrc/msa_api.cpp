@@ -39,9 +39,19 @@ hipError_t launch_prefill_generic(const void *q, const void *k, const void *v,
                                   float scale, float *o, float *lse, void *ws,
                                   hipStream_t st);
 
+bool mfma_prefill_supported(int32_t dtype, int32_t d, int32_t group);
+hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v,
+                               int64_t kv_stride, int64_t q_pos0, int64_t n_q,
+                               int32_t hq, int32_t hkv, int32_t d,
+                               int32_t block, const int32_t *sel, int32_t topk,
+                               const int32_t *row_ptr, const int32_t *q_list,
+                               const int32_t *slot, float scale, float *o,
+                               float *lse, void *ws, hipStream_t st);
+
 bool prefill_supported(int32_t dtype, int32_t d, int32_t group) {
   if (dtype != MSA_F32 && dtype != MSA_BF16) return false;
-  return generic_prefill_supported(d, group);
+  return mfma_prefill_supported(dtype, d, group) ||
+         generic_prefill_supported(d, group);
 }
 
 hipError_t launch_prefill(const void *q, const void *k, const void *v,
@@ -51,6 +61,12 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v,
                           const int32_t *row_ptr, const int32_t *q_list,
                           const int32_t *slot, float scale, float *o,
                           float *lse, void *ws, hipStream_t st) {
+  // bf16 with d = 128 runs on the matrix cores; everything else (fp32
+  // inputs, other head sizes) on the fp32 VALU kernels.
+  if (mfma_prefill_supported(dtype, d, hq / hkv))
+    return launch_prefill_mfma(q, k, v, kv_stride, q_pos0, n_q, hq, hkv, d,
+                               block, sel, topk, row_ptr, q_list, slot, scale,
+                               o, lse, ws, st);
   return launch_prefill_generic(q, k, v, dtype, kv_stride, q_pos0, n_q, hq, hkv,
                                 d, block, sel, topk, row_ptr, q_list, slot,
                                 scale, o, lse, ws, st);

@@ -192,6 +192,10 @@ def test_prefill_tiny_config_full(orc):
     ("f32-G8-d128", dict(T=2000, dtype="f32", n_hot=3, topk=5, block=64), 0, None, 400),
     ("bf16-B512", dict(T=5000, block=512, topk=4, n_hot=2), 0, None, 300),
     ("bf16-B16-K1", dict(T=700, block=16, topk=1, n_hot=0), 0, None, None),
+    ("bf16-G4-B32", dict(T=1500, Hq=16, Hkv=4, block=32, topk=6, n_hot=2), 0, None, 300),
+    ("bf16-G16-B48", dict(T=1300, Hq=32, Hkv=2, block=48, topk=5, n_hot=2), 200, 1000, 300),
+    ("bf16-G1-B64", dict(T=1200, Hq=4, Hkv=4, block=64, topk=4, n_hot=2), 0, None, None),
+    ("bf16-G2-B16", dict(T=900, Hq=8, Hkv=4, block=16, topk=9, n_hot=2), 0, None, None),
 ])
 def test_prefill_shapes(orc, name, over, q0, nq, sample):
     _say(f"prefill {name}")
