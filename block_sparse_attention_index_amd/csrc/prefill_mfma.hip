@@ -11,14 +11,19 @@
 //           causal attention inside the own block, then the log-sum-exp merge
 //           with pass A's partials; writes O and LSE.
 //
-// Each wave owns 64 query rows as two 32-row N-blocks.  Scores are computed
-// transposed, S^T = K Q^T (keys = MFMA rows), so a lane holds 16 keys of ONE
-// query row: the row max needs a single exchange with lane l^32 and the
-// softmax statistics stay per lane.  P^T leaves the accumulator already in
-// the B-operand layout of O^T = V^T P^T, provided V^T's k-slots use the same
-// key order; V is therefore staged transposed in LDS.  Lazy rescaling: the
-// running reference max moves only when a row's max exceeds it by more than
-// 8 (so every weight is at most 2^8), which removes most O rescales.
+// Each wave owns NB 32-row N-blocks; with NB = 1 and 8 waves a workgroup
+// holds 256 query rows and each SIMD runs two waves, so one wave's softmax
+// overlaps the other's MFMAs.  Scores are computed transposed, S^T = K Q^T
+// (keys = MFMA rows), so a lane holds 16 keys of ONE query row: the row max
+// needs one v_permlane32_swap with lane l^32 and the softmax statistics stay
+// per lane.  P^T leaves the accumulator already in the B-operand layout of
+// O^T = V^T P^T, provided V^T's k-slots follow the same key order: V is
+// staged row-major in LDS and each V^T operand is read with two
+// ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x 16-column tile
+// transposed, so lane i gets column i of four consecutive keys).  Lazy
+// rescaling: the running reference max moves only when a row's max exceeds
+// it by more than 8 (so every weight is at most 2^8), which removes most O
+// rescales.
 #include "msa_internal.h"
 #include "prefill_common.h"
 
@@ -34,13 +39,37 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kD = 128;          // head dim handled here
 constexpr int kKC = 64;          // keys per staged chunk
 constexpr int kKStr = kD + 8;    // K row stride in LDS, bf16 elements (272 B)
-constexpr int kVStr = kKC + 4;   // V^T row stride in LDS, bf16 elements (136 B)
+constexpr int kVStr = kD + 16;   // V row stride in LDS, bf16 elements (288 B)
 constexpr float kLazy = 8.f;     // reference-max slack (log2 units)
 
 struct MfmaSmem {
   uint16_t Ks[kKC * kKStr];
-  uint16_t Vt[kD * kVStr];
+  uint16_t Vs[kKC * kVStr];
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 *lds_s16x4_ptr;
+
+// ds_read_b64_tr_b16: lane i of each 16-lane group gets element i%16 of the
+// group's 16 eight-byte rows read as a 4 x 16 matrix (row r = lanes 4r..4r+3).
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t *p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4_ptr)(const_cast<uint16_t *>(p)));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Value of the lane l^32 combined with the own value: v_permlane32_swap(x, x)
+// returns x from lanes l%32 and l%32+32 in its two results.
+__device__ __forceinline__ float max_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -50,30 +79,60 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Stage keys [row0, row0+nrows) of one (head, block) slice: K row-major with
-// padded rows, V transposed (V^T[c][key]).  Rows past nrows are zero.
-__device__ __forceinline__ void stage(MfmaSmem &sm, const uint16_t *k,
-                                      const uint16_t *v, int64_t row0,
-                                      int nrows) {
+// Staging of one 64-key chunk of a (head, block) slice, split so the global
+// loads of chunk i+1 are in flight while chunk i is computed: load() fills
+// registers, store() writes K and V row-major (padded rows) into one of the
+// two LDS buffers.  Rows past nrows are zero.
+template <int NT>
+struct ChunkRegs {
+  static constexpr int kIt = (kKC * kD / 8) / NT;   // 16-byte pieces per thread
+  u32x4 k[kIt], v[kIt];
+};
+
+template <int NT>
+__device__ __forceinline__ void load_chunk(ChunkRegs<NT> &cr, const uint16_t *k,
+                                           const uint16_t *v, int64_t row0,
+                                           int nrows) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int it = 0; it < (kKC * kD / 8) / 256; ++it) {
-    const int x = tid + 256 * it;
+  for (int it = 0; it < ChunkRegs<NT>::kIt; ++it) {
+    const int x = tid + NT * it;
     const int key = x >> 4, seg = x & 15;
     u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
     if (key < nrows) {
       kv = *reinterpret_cast<const u32x4 *>(k + (row0 + key) * kD + seg * 8);
       vv = *reinterpret_cast<const u32x4 *>(v + (row0 + key) * kD + seg * 8);
     }
-    *reinterpret_cast<u32x4 *>(&sm.Ks[key * kKStr + seg * 8]) = kv;
-    const uint16_t *ve = reinterpret_cast<const uint16_t *>(&vv);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sm.Vt[(seg * 8 + i) * kVStr + key] = ve[i];
+    cr.k[it] = kv;
+    cr.v[it] = vv;
   }
 }
 
-template <int G, bool OWN>
-__global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(
+template <int NT>
+__device__ __forceinline__ void store_chunk(MfmaSmem &sm, const ChunkRegs<NT> &cr) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < ChunkRegs<NT>::kIt; ++it) {
+    const int x = tid + NT * it;
+    const int key = x >> 4, seg = x & 15;
+    *reinterpret_cast<u32x4 *>(&sm.Ks[key * kKStr + seg * 8]) = cr.k[it];
+    *reinterpret_cast<u32x4 *>(&sm.Vs[key * kVStr + seg * 8]) = cr.v[it];
+  }
+}
+
+// Offset of element (pair n, head g*G+hl, column c = cb*32 + 8*rg + 4*hf + e)
+// in the partial-output workspace.  The order follows the O^T accumulator
+// fragments, so that the 2*G lanes holding one token's rows in a wave read or
+// write 32*G contiguous bytes per (cb, rg): [n][g][cb][rg][hf][hl][e].
+__device__ __forceinline__ int64_t frag_off(int64_t n, int g, int hq, int G,
+                                            int hl, int cb, int rg, int hf) {
+  return n * (int64_t)hq * kD + (int64_t)g * G * kD + cb * 32 * G + rg * 8 * G +
+         hf * 4 * G + hl * 4;
+}
+
+// NB = 32-row N-blocks per wave, NW = waves per workgroup.
+template <int G, int NB, int NW, bool OWN>
+__global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, int64_t kv_stride, int64_t q_pos0,
     int64_t n_q, int hq, int B, const int32_t *__restrict__ row_ptr,
@@ -82,10 +141,11 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(
     const int32_t *__restrict__ slot, float scale_log2,
     float *__restrict__ part_o, float *__restrict__ part_lse, int64_t n_part,
     float *__restrict__ o, float *__restrict__ lse) {
+  constexpr int NT = 64 * NW;    // threads
   constexpr int TPN = 32 / G;    // tokens per 32-row N-block
-  constexpr int TPW = 2 * TPN;   // tokens per wave
-  constexpr int TPT = 4 * TPW;   // tokens per tile (workgroup)
-  __shared__ MfmaSmem sm;
+  constexpr int TPW = NB * TPN;  // tokens per wave
+  constexpr int TPT = NW * TPW;  // tokens per tile (workgroup)
+  __shared__ MfmaSmem smb[2];
 
   const int g = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -116,12 +176,12 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(
     min_pos = tok0;
   }
 
-  int64_t qi[2], pos[2];
-  bool act[2];
-  int head[2];
-  bf16x8 qf[2][8];
+  int64_t qi[NB], pos[NB];
+  bool act[NB];
+  int head[NB];
+  bf16x8 qf[NB][8];
 #pragma unroll
-  for (int nbk = 0; nbk < 2; ++nbk) {
+  for (int nbk = 0; nbk < NB; ++nbk) {
     const int tl = wave * TPW + nbk * TPN + j / G;
     head[nbk] = j % G;
     if constexpr (!OWN) {
@@ -145,29 +205,42 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(
     }
   }
 
-  f32x16 acc[2][4];
+  f32x16 acc[NB][4];
 #pragma unroll
-  for (int nbk = 0; nbk < 2; ++nbk)
+  for (int nbk = 0; nbk < NB; ++nbk)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[nbk][cb][r] = 0.f;
-  float mref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  float mref[NB], lsum[NB];
+#pragma unroll
+  for (int nbk = 0; nbk < NB; ++nbk) {
+    mref[nbk] = -INFINITY;
+    lsum[nbk] = 0.f;
+  }
 
   const uint16_t *kb = k + ((int64_t)g * kv_stride) * kD;
   const uint16_t *vb = v + ((int64_t)g * kv_stride) * kD;
-  for (int64_t kc = 0; kc < nkeys; kc += kKC) {
-    const int nrows = (int)(nkeys - kc < kKC ? nkeys - kc : kKC);
-    __syncthreads();
-    stage(sm, kb, vb, b * B + kc, nrows);
-    __syncthreads();
+  const int64_t n_chunks = (nkeys + kKC - 1) / kKC;
+  ChunkRegs<NT> cr;
+  load_chunk(cr, kb, vb, b * B, (int)(nkeys < kKC ? nkeys : kKC));
+  store_chunk(smb[0], cr);
+  __syncthreads();
+  for (int64_t ci = 0; ci < n_chunks; ++ci) {
+    const int64_t kc = ci * kKC;
+    if (ci + 1 < n_chunks) {
+      const int64_t nxt = kc + kKC;
+      load_chunk(cr, kb, vb, b * B + nxt,
+                 (int)(nkeys - nxt < kKC ? nkeys - nxt : kKC));
+    }
+    MfmaSmem &sm = smb[ci & 1];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int koff0 = (int)kc + sub * 32;          // key offset in block
       if (koff0 >= nkeys) break;
-      f32x16 s[2];
+      f32x16 s[NB];
 #pragma unroll
-      for (int nbk = 0; nbk < 2; ++nbk)
+      for (int nbk = 0; nbk < NB; ++nbk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[nbk][r] = 0.f;
 #pragma unroll
@@ -175,14 +248,14 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(
         const u32x4 kraw = *reinterpret_cast<const u32x4 *>(
             &sm.Ks[(sub * 32 + j) * kKStr + cc * 16 + 8 * h]);
         const bf16x8 kf = as_bf16x8(kraw);
-        s[0] = mfma32(kf, qf[0][cc], s[0]);
-        s[1] = mfma32(kf, qf[1][cc], s[1]);
+#pragma unroll
+        for (int nbk = 0; nbk < NB; ++nbk) s[nbk] = mfma32(kf, qf[nbk][cc], s[nbk]);
       }
       const bool need_mask =
           koff0 + 31 >= nkeys || (OWN && b * B + koff0 + 31 > min_pos);
-      bf16x8 pb[2][2];
+      bf16x8 pb[NB][2];
 #pragma unroll
-      for (int nbk = 0; nbk < 2; ++nbk) {
+      for (int nbk = 0; nbk < NB; ++nbk) {
         if (need_mask) {
           const int64_t lim = OWN ? pos[nbk] - b * B : nkeys - 1;
           const int64_t lim2 = lim < nkeys - 1 ? lim : nkeys - 1;
@@ -195,7 +268,7 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(
         float mloc = s[nbk][0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, s[nbk][r]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        mloc = max_with_partner(mloc);
         const float mt = mloc * scale_log2;
         if (__ballot(mt > mref[nbk] + kLazy)) {
           const float mnew = fmaxf(mref[nbk], mt);
@@ -220,26 +293,34 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(
         pb[nbk][0] = __builtin_convertvector(p0, bf16x8);
         pb[nbk][1] = __builtin_convertvector(p1, bf16x8);
       }
+      // V^T operand rows: this lane's 16-lane group reads keys
+      // sub*32 + 16ks + 4h + a/4 (+8), columns cb*32 + 16*(j/16) + 4*(a%4)
+      const int a16 = lane & 15;
+      const uint16_t *vbase = &sm.Vs[(sub * 32 + 4 * h + (a16 >> 2)) * kVStr +
+                                     16 * (j >> 4) + 4 * (a16 & 3)];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-          const uint16_t *vr = &sm.Vt[(cb * 32 + j) * kVStr + sub * 32 + 16 * ks + 4 * h];
-          const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
-          const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 8);
+          const uint16_t *vr = vbase + 16 * ks * kVStr + cb * 32;
+          const u32x2 lo = lds_read_tr(vr);
+          const u32x2 hi = lds_read_tr(vr + 8 * kVStr);
           const u32x4 vraw = {lo[0], lo[1], hi[0], hi[1]};
           const bf16x8 vf = as_bf16x8(vraw);
-          acc[0][cb] = mfma32(vf, pb[0][ks], acc[0][cb]);
-          acc[1][cb] = mfma32(vf, pb[1][ks], acc[1][cb]);
+#pragma unroll
+          for (int nbk = 0; nbk < NB; ++nbk)
+            acc[nbk][cb] = mfma32(vf, pb[nbk][ks], acc[nbk][cb]);
         }
       }
     }
+    if (ci + 1 < n_chunks) store_chunk(smb[(ci + 1) & 1], cr);
+    __syncthreads();
   }
 
   // ---- epilogue ----
 #pragma unroll
-  for (int nbk = 0; nbk < 2; ++nbk) {
-    const float ltot = lsum[nbk] + __shfl_xor(lsum[nbk], 32, 64);
+  for (int nbk = 0; nbk < NB; ++nbk) {
+    const float ltot = sum_with_partner(lsum[nbk]);
     const int hh = g * G + head[nbk];
     if constexpr (!OWN) {
       if (!act[nbk]) continue;
@@ -247,14 +328,13 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(
       const int64_t n_idx = e - own_through(b, q_pos0, n_q, B);
       if (n_idx < 0 || n_idx >= n_part) continue;
       const float inv = 1.f / ltot;
-      float *dst = part_o + (n_idx * hq + hh) * (int64_t)kD;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           float4 val = make_float4(acc[nbk][cb][4 * rg] * inv, acc[nbk][cb][4 * rg + 1] * inv,
                                    acc[nbk][cb][4 * rg + 2] * inv, acc[nbk][cb][4 * rg + 3] * inv);
-          *reinterpret_cast<float4 *>(dst + cb * 32 + 8 * rg + 4 * h) = val;
+          *reinterpret_cast<float4 *>(part_o + frag_off(n_idx, g, hq, G, head[nbk], cb, rg, h)) = val;
         }
       if (h == 0) part_lse[n_idx * hq + hh] = mref[nbk] + __log2f(ltot);
     } else {
@@ -284,12 +364,12 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(
         if (n_idx < 0 || n_idx >= n_part) continue;
         const float wk = fast_exp2(part_lse[n_idx * hq + hh] - mx);
         z += wk;
-        const float *src = part_o + (n_idx * hq + hh) * (int64_t)kD;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
-            const float4 pv = *reinterpret_cast<const float4 *>(src + cb * 32 + 8 * rg + 4 * h);
+            const float4 pv = *reinterpret_cast<const float4 *>(
+                part_o + frag_off(n_idx, g, hq, G, head[nbk], cb, rg, h));
             acc[nbk][cb][4 * rg] = fmaf(wk, pv.x, acc[nbk][cb][4 * rg]);
             acc[nbk][cb][4 * rg + 1] = fmaf(wk, pv.y, acc[nbk][cb][4 * rg + 1]);
             acc[nbk][cb][4 * rg + 2] = fmaf(wk, pv.z, acc[nbk][cb][4 * rg + 2]);
@@ -311,32 +391,272 @@ __global__ __launch_bounds__(256, 1) void prefill_mfma_kernel(
   }
 }
 
-template <int G>
+// ---------------------------------------------------------------------------
+// Pass A, persistent.  One workgroup per CU walks a static range of work
+// items w = (KV head g, tile t); the range of workgroup i is the i%8-th
+// eighth of all items, so the workgroups placed on one XCD share its L2 over
+// a window of consecutive tiles (same head, mostly the same KV block).  The
+// next item's metadata, query fragments and first K/V chunk are fetched while
+// the current item computes.
+//
+// Per-tile metadata (built by prefill_tile_info): info[t] = (block, first CSR
+// position, row end) and tq[t][i] = query index of the tile's i-th row token
+// (-1 past the row end).
+// ---------------------------------------------------------------------------
+template <int TPT>
+__global__ __launch_bounds__(256) void prefill_tile_info(
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ tile_ptr,
+    const int32_t *__restrict__ q_list, int64_t q_pos0, int64_t n_q, int B,
+    int4 *__restrict__ info, int32_t *__restrict__ tq) {
+  const int64_t b = blockIdx.x;
+  const int32_t t0 = tile_ptr[b], t1 = tile_ptr[b + 1];
+  if (t0 == t1) return;
+  const int64_t own_b =
+      own_through(b, q_pos0, n_q, B) - own_through(b - 1, q_pos0, n_q, B);
+  const int32_t base = (int32_t)(row_ptr[b] + own_b), end = row_ptr[b + 1];
+  for (int x = threadIdx.x; x < (t1 - t0) * TPT; x += 256) {
+    const int tt = x / TPT, i = x % TPT;
+    const int32_t e = base + tt * TPT + i;
+    tq[(int64_t)(t0 + tt) * TPT + i] = e < end ? q_list[e] : -1;
+    if (i == 0) info[t0 + tt] = make_int4((int)b, base + tt * TPT, end, 0);
+  }
+}
+
+template <int G, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, int64_t kv_stride, int64_t q_pos0,
+    int64_t n_q, int hq, int hkv, int B, const int32_t *__restrict__ tile_ptr,
+    int64_t nb, const int4 *__restrict__ info, const int32_t *__restrict__ tq,
+    float scale_log2, float *__restrict__ part_o, float *__restrict__ part_lse,
+    int64_t n_part) {
+  constexpr int NT = 64 * NW;
+  constexpr int TPN = 32 / G;
+  constexpr int TPT = NW * TPN;
+  __shared__ MfmaSmem smb[2];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = lane >> 5, j = lane & 31;
+  const int tl = wave * TPN + j / G;  // token slot of this lane's row
+  const int hl = j % G;                // head of this lane's row in the group
+
+  const int64_t T = tile_ptr[nb];
+  const int64_t W = T * hkv;
+  const int xcd = blockIdx.x & 7;
+  const int64_t per = gridDim.x >> 3, r = blockIdx.x >> 3;
+  const int64_t w_end = W * (xcd + 1) / 8;
+  int64_t w = W * xcd / 8 + r;
+  if (w >= w_end) return;
+
+  // metadata of item w: head, tile info, this lane's query
+  int g = (int)(w / T);
+  int4 inf = info[w % T];
+  int32_t qraw = tq[(w % T) * TPT + tl];
+
+  auto load_q = [&](int gg, int32_t qr, bf16x8 (&dst)[8]) {
+    const bool a = qr >= 0 && qr < n_q;
+    const uint16_t *qp = q + (((a ? (int64_t)qr : 0) * hq + (int64_t)gg * G + hl) * kD);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (a) x = *reinterpret_cast<const u32x4 *>(qp + cc * 16 + 8 * h);
+      dst[cc] = as_bf16x8(x);
+    }
+  };
+  auto kv_keys = [&](int64_t bb) {
+    int64_t n = B;
+    if (bb * B + n > kv_stride) n = kv_stride - bb * B;   // invalid input only
+    return n;
+  };
+
+  bf16x8 qf[8];
+  load_q(g, qraw, qf);
+  ChunkRegs<NT> cr;
+  {
+    const int64_t nk = kv_keys(inf.x);
+    load_chunk(cr, k + ((int64_t)g * kv_stride) * kD, v + ((int64_t)g * kv_stride) * kD,
+               (int64_t)inf.x * B, (int)(nk < kKC ? nk : kKC));
+  }
+  int buf = 0;
+  store_chunk(smb[0], cr);
+  __syncthreads();
+
+  for (;;) {
+    const int64_t wn = w + per;
+    const bool has_next = wn < w_end;
+    int gn = 0;
+    int4 infn = make_int4(0, 0, 0, 0);
+    int32_t qrawn = -1;
+    if (has_next) {
+      gn = (int)(wn / T);
+      infn = info[wn % T];
+      qrawn = tq[(wn % T) * TPT + tl];
+    }
+    bf16x8 qfn[8];
+
+    const int64_t b = inf.x;
+    const int64_t nkeys = kv_keys(b);
+    const int64_t n_chunks = (nkeys + kKC - 1) / kKC;
+    const uint16_t *kb = k + ((int64_t)g * kv_stride) * kD;
+    const uint16_t *vb = v + ((int64_t)g * kv_stride) * kD;
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
+    float mref = -INFINITY, lsum = 0.f;
+
+    for (int64_t ci = 0; ci < n_chunks; ++ci) {
+      const int64_t kc = ci * kKC;
+      bool staged = true;
+      if (ci + 1 < n_chunks) {
+        const int64_t nxt = kc + kKC;
+        load_chunk(cr, kb, vb, b * B + nxt, (int)(nkeys - nxt < kKC ? nkeys - nxt : kKC));
+      } else if (has_next) {
+        const int64_t nk = kv_keys(infn.x);
+        load_chunk(cr, k + ((int64_t)gn * kv_stride) * kD, v + ((int64_t)gn * kv_stride) * kD,
+                   (int64_t)infn.x * B, (int)(nk < kKC ? nk : kKC));
+        load_q(gn, qrawn, qfn);
+      } else {
+        staged = false;
+      }
+      MfmaSmem &sm = smb[buf];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int koff0 = (int)kc + sub * 32;
+        if (koff0 >= nkeys) break;
+        f32x16 sacc;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sacc[rr] = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const u32x4 kraw = *reinterpret_cast<const u32x4 *>(
+              &sm.Ks[(sub * 32 + j) * kKStr + cc * 16 + 8 * h]);
+          sacc = mfma32(as_bf16x8(kraw), qf[cc], sacc);
+        }
+        if (koff0 + 31 >= nkeys) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int koff = koff0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+            if (koff >= nkeys) sacc[rr] = -INFINITY;
+          }
+        }
+        float mloc = sacc[0];
+#pragma unroll
+        for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, sacc[rr]);
+        mloc = max_with_partner(mloc);
+        const float mt = mloc * scale_log2;
+        if (__ballot(mt > mref + kLazy)) {
+          const float mnew = fmaxf(mref, mt);
+          const float alpha = fast_exp2(mref - mnew);
+          lsum *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+          mref = mnew;
+        }
+        f32x8 p0, p1;
+        float ps = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          p0[rr] = fast_exp2(fmaf(sacc[rr], scale_log2, -mref));
+          p1[rr] = fast_exp2(fmaf(sacc[rr + 8], scale_log2, -mref));
+          ps += p0[rr] + p1[rr];
+        }
+        lsum += ps;
+        const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
+        const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+        const int a16 = lane & 15;
+        const uint16_t *vbase = &sm.Vs[(sub * 32 + 4 * h + (a16 >> 2)) * kVStr +
+                                       16 * (j >> 4) + 4 * (a16 & 3)];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const uint16_t *vr = vbase + 16 * ks * kVStr + cb * 32;
+            const u32x2 lo = lds_read_tr(vr);
+            const u32x2 hi = lds_read_tr(vr + 8 * kVStr);
+            const u32x4 vraw = {lo[0], lo[1], hi[0], hi[1]};
+            acc[cb] = mfma32(as_bf16x8(vraw), ks == 0 ? pb0 : pb1, acc[cb]);
+          }
+        }
+      }
+      if (staged) store_chunk(smb[buf ^ 1], cr);
+      buf ^= 1;
+      __syncthreads();
+    }
+
+    // partial output of this (query, head) for block b
+    const bool act = qraw >= 0 && qraw < n_q;
+    const float ltot = sum_with_partner(lsum);
+    if (act) {
+      const int64_t e = (int64_t)inf.y + tl;
+      const int64_t n_idx = e - own_through(b, q_pos0, n_q, B);
+      if (n_idx >= 0 && n_idx < n_part) {
+        const float inv = 1.f / ltot;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            float4 val = make_float4(acc[cb][4 * rg] * inv, acc[cb][4 * rg + 1] * inv,
+                                     acc[cb][4 * rg + 2] * inv, acc[cb][4 * rg + 3] * inv);
+            *reinterpret_cast<float4 *>(part_o + frag_off(n_idx, g, hq, G, hl, cb, rg, h)) = val;
+          }
+        if (h == 0) part_lse[n_idx * hq + (int64_t)g * G + hl] = mref + __log2f(ltot);
+      }
+    }
+    if (!has_next) break;
+    w = wn;
+    g = gn;
+    inf = infn;
+    qraw = qrawn;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) qf[cc] = qfn[cc];
+  }
+}
+
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+template <int G, int NB, int NW>
 hipError_t launch_mfma_g(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          int64_t kv_stride, int64_t q_pos0, int64_t n_q, int hq,
                          int hkv, int B, const int32_t *sel, int topk,
                          const int32_t *row_ptr, const int32_t *q_list,
                          const int32_t *slot, float scale, float *o, float *lse,
-                         int32_t *tile_ptr, float *part_o, float *part_lse,
-                         int64_t n_part, hipStream_t st) {
-  constexpr int TPT = 256 / G;
+                         int32_t *tile_ptr, int4 *info, int32_t *tq,
+                         float *part_o, float *part_lse, int64_t n_part,
+                         hipStream_t st) {
+  constexpr int TPT = NW * NB * (32 / G);
   const int64_t nb = (q_pos0 + n_q + B - 1) / B;
   const float sl2 = scale * kLog2e;
   if (n_part > 0) {
     hipLaunchKernelGGL(prefill_tiles, dim3(1), dim3(1024), 0, st, row_ptr, nb,
                        q_pos0, n_q, B, TPT, tile_ptr);
-    const int64_t grid = n_part / TPT + nb;
-    hipLaunchKernelGGL((prefill_mfma_kernel<G, false>), dim3((unsigned)grid, hkv),
-                       dim3(256), 0, st, q, k, v, kv_stride, q_pos0, n_q, hq, B,
-                       row_ptr, q_list, tile_ptr, nb, sel, topk, slot, sl2, part_o,
-                       part_lse, n_part, o, lse);
+    hipLaunchKernelGGL((prefill_tile_info<TPT>), dim3((unsigned)nb), dim3(256), 0,
+                       st, row_ptr, tile_ptr, q_list, q_pos0, n_q, B, info, tq);
+    const int grid = 8 * ((num_cus() + 7) / 8);
+    hipLaunchKernelGGL((prefill_nonown_persistent<G, NW>), dim3(grid), dim3(64 * NW),
+                       0, st, q, k, v, kv_stride, q_pos0, n_q, hq, hkv, B, tile_ptr,
+                       nb, info, tq, sl2, part_o, part_lse, n_part);
   }
   const int64_t b_first = q_pos0 / B, b_last = (q_pos0 + n_q - 1) / B;
   const int64_t tiles = (b_last - b_first + 1) * ((B + TPT - 1) / TPT);
-  hipLaunchKernelGGL((prefill_mfma_kernel<G, true>), dim3((unsigned)tiles, hkv),
-                     dim3(256), 0, st, q, k, v, kv_stride, q_pos0, n_q, hq, B,
-                     row_ptr, q_list, tile_ptr, nb, sel, topk, slot, sl2, part_o,
-                     part_lse, n_part, o, lse);
+  hipLaunchKernelGGL((prefill_mfma_kernel<G, NB, NW, true>),
+                     dim3((unsigned)tiles, hkv), dim3(64 * NW), 0, st, q, k, v,
+                     kv_stride, q_pos0, n_q, hq, B, row_ptr, q_list, tile_ptr, nb,
+                     sel, topk, slot, sl2, part_o, part_lse, n_part, o, lse);
   return hipGetLastError();
 }
 
@@ -364,14 +684,19 @@ hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v,
   float *part_o = reinterpret_cast<float *>(w);
   w += align256((size_t)np * hq * d * 4);
   float *part_lse = reinterpret_cast<float *>(w);
+  w += align256((size_t)np * hq * 4);
+  int4 *info = reinterpret_cast<int4 *>(w);
+  w += align256((size_t)(np / 16 + nb) * 16);   // same bound as the size query
+  int32_t *tq = reinterpret_cast<int32_t *>(w);
   const uint16_t *qq = static_cast<const uint16_t *>(q);
   const uint16_t *kk = static_cast<const uint16_t *>(k);
   const uint16_t *vv = static_cast<const uint16_t *>(v);
-#define MSA_MF(GG)                                                             \
-  case GG:                                                                     \
-    return launch_mfma_g<GG>(qq, kk, vv, kv_stride, q_pos0, n_q, hq, hkv,      \
-                             block, sel, topk, row_ptr, q_list, slot, scale, o, \
-                             lse, tile_ptr, part_o, part_lse, np, st);
+#define MSA_MF(GG)                                                              \
+  case GG:                                                                      \
+    return launch_mfma_g<GG, 1, 8>(qq, kk, vv, kv_stride, q_pos0, n_q, hq, hkv,  \
+                                   block, sel, topk, row_ptr, q_list, slot,      \
+                                   scale, o, lse, tile_ptr, info, tq, part_o,    \
+                                   part_lse, np, st);
   switch (G) {
     MSA_MF(1)
     MSA_MF(2)
