@@ -11,7 +11,8 @@ fp32 index vectors, 128 planted hot blocks) and stay resident in HBM.
 
 Printed (rank 0, one JSON line): ``value`` = attended TFLOP/s of the whole
 step (4*d*Hq FLOP per attended (query, key) pair, prefill and decode);
-``prefill_tflops`` and ``decode_us_per_step`` break it down; ``roofline`` is
+``prefill_tflops`` and ``decode_us_per_step`` break it down (the 256 decode
+steps run as one captured HIP graph, replayed each step); ``roofline`` is
 for the sparse-GQA prefill (its two kernels per call, timed with HIP events on
 the launch stream) against the dense bf16 MFMA peak; ``cpu_baseline`` times
 the CPU oracle on a bounded sample of the same workload.
@@ -133,6 +134,23 @@ def main():
     dbufs = pipeline.alloc_decode(x["q"][:1], kmax_dec, B, K) if n_dec else None
     stream = torch.cuda.current_stream(dev)
 
+    def decode_loop():
+        for s in range(n_dec):
+            pipeline.decode_step(x["q"][T + s:T + s + 1], x["idx_q"][T + s:T + s + 1],
+                                 k_cache, v_cache, idx_k_cache, kmax_dec,
+                                 seq_lens[s:s + 1], B, K, cfg.scale, bufs=dbufs)
+
+    # The decode steps are launch-bound at batch 1: capture them once in a HIP
+    # graph (no allocation or memset inside) and replay it.
+    dec_graph = None
+    if n_dec:
+        decode_loop()                      # eager warm-up of the decode kernels
+        torch.cuda.synchronize()
+        dec_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dec_graph):
+            decode_loop()
+        torch.cuda.synchronize()
+
     ev = {"pre": [], "attn": [], "dec": []}
 
     def step(record: bool):
@@ -162,10 +180,8 @@ def main():
                 ev["attn"].append((a0, a1))
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record(stream)
-        for s in range(n_dec):
-            pipeline.decode_step(x["q"][T + s:T + s + 1], x["idx_q"][T + s:T + s + 1],
-                                 k_cache, v_cache, idx_k_cache, kmax_dec,
-                                 seq_lens[s:s + 1], B, K, cfg.scale, bufs=dbufs)
+        if dec_graph is not None:
+            dec_graph.replay()
         e2 = torch.cuda.Event(enable_timing=True)
         e2.record(stream)
         if record:

@@ -99,8 +99,8 @@ int msa_index_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
   if (!idx_k || !kmax || n_seq < 1 || n_seq > kMaxGridY || len_max < 1 ||
       !didx_ok(d_idx) || !block_ok(block) || nb_max < cdiv(len_max, block))
     return MSA_ERR_INVALID_ARG;
-  if (blk_begin >= 0 && (blk_end <= blk_begin || blk_end > nb_max ||
-                         blk_end - blk_begin > INT32_MAX))
+  if (blk_begin < -2 || (blk_begin >= 0 && (blk_end <= blk_begin || blk_end > nb_max ||
+                                             blk_end - blk_begin > INT32_MAX)))
     return MSA_ERR_INVALID_ARG;
   return status_of(msa::launch_pool(idx_k, n_seq, len_max, seq_len, d_idx,
                                     block, blk_begin, blk_end, kmax, nb_max,
@@ -214,7 +214,9 @@ int msa_sparse_gqa_decode(const void *q, const void *k_cache,
       hkv > kMaxGridY || hq % hkv != 0 || d < 1 || !block_ok(block) ||
       !topk_ok(topk) || !std::isfinite(scale))
     return MSA_ERR_INVALID_ARG;
-  if (!msa::decode_supported(dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
+  if (!msa::decode_supported(dtype, d, hq / hkv) ||
+      !msa::decode_partials_ok(dtype, d, hq / hkv, block, topk))
+    return MSA_ERR_UNSUPPORTED;
   if (ws_bytes < msa::decode_ws_bytes(n_seq, hq, d, block, topk))
     return MSA_ERR_WORKSPACE;
   return status_of(msa::launch_decode(q, k_cache, v_cache, dtype, n_seq,

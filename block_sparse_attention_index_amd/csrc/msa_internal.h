@@ -52,6 +52,8 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v,
 size_t decode_ws_bytes(int32_t n_seq, int32_t hq, int32_t d, int32_t block,
                        int32_t topk);
 bool decode_supported(int32_t dtype, int32_t d, int32_t group);
+bool decode_partials_ok(int32_t dtype, int32_t d, int32_t group, int32_t block,
+                        int32_t topk);
 hipError_t launch_decode(const void *q, const void *k_cache,
                          const void *v_cache, int32_t dtype, int32_t n_seq,
                          int64_t len_max, const int64_t *seq_len, int32_t hq,

@@ -95,12 +95,39 @@ __global__ __launch_bounds__(256) void pool_scalar(
   }
 }
 
+// Append mode: the newest token t = len-1 of each sequence either starts its
+// block's summary (t % B == 0) or raises the running max in place.  Valid
+// when kmax[s][t / B] already holds the max over tokens [t/B*B, t).
+__global__ __launch_bounds__(256) void pool_append(
+    const float *__restrict__ idx_k, int64_t len_max,
+    const int64_t *__restrict__ seq_len, int d_idx, int B,
+    float *__restrict__ kmax, int64_t nb_max) {
+  const int s = blockIdx.x;
+  int64_t len = seq_len ? seq_len[s] : len_max;
+  if (len > len_max) len = len_max;
+  if (len < 1) return;
+  const int64_t t = len - 1, b = t / B;
+  if (b >= nb_max) return;
+  const float *src = idx_k + ((int64_t)s * len_max + t) * d_idx;
+  float *dst = kmax + ((int64_t)s * nb_max + b) * d_idx;
+  const bool first = (t % B) == 0;
+  for (int c = threadIdx.x; c < d_idx; c += 256) {
+    const int x = f2key(src[c]);
+    dst[c] = first ? src[c] : key2f(max(x, f2key(dst[c])));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
                        const int64_t *seq_len, int32_t d_idx, int32_t block,
                        int64_t blk_begin, int64_t blk_end, float *kmax,
                        int64_t nb_max, hipStream_t st) {
+  if (blk_begin == -2) {
+    hipLaunchKernelGGL(pool_append, dim3((unsigned)n_seq), dim3(256), 0, st,
+                       idx_k, len_max, seq_len, d_idx, block, kmax, nb_max);
+    return hipGetLastError();
+  }
   const int64_t nblk = blk_begin < 0 ? 1 : blk_end - blk_begin;
   dim3 grid((unsigned)nblk, (unsigned)n_seq);
   if (d_idx % 4 == 0)

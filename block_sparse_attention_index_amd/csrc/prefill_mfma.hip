@@ -26,15 +26,10 @@
 // rescales.
 #include "msa_internal.h"
 #include "prefill_common.h"
+#include "mfma_common.h"
 
 namespace msa {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;          // head dim handled here
 constexpr int kKC = 64;          // keys per staged chunk
@@ -46,38 +41,6 @@ struct MfmaSmem {
   uint16_t Ks[kKC * kKStr];
   uint16_t Vs[kKC * kVStr];
 };
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 *lds_s16x4_ptr;
-
-// ds_read_b64_tr_b16: lane i of each 16-lane group gets element i%16 of the
-// group's 16 eight-byte rows read as a 4 x 16 matrix (row r = lanes 4r..4r+3).
-__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t *p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4_ptr)(const_cast<uint16_t *>(p)));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// Value of the lane l^32 combined with the own value: v_permlane32_swap(x, x)
-// returns x from lanes l%32 and l%32+32 in its two results.
-__device__ __forceinline__ float max_with_partner(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
-                                                  __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_with_partner(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
-                                                  __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 // Staging of one 64-key chunk of a (head, block) slice, split so the global
 // loads of chunk i+1 are in flight while chunk i is computed: load() fills

@@ -176,56 +176,115 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode, stage 1: workgroup = (chunk of 256 blocks, sequence).  Each thread
-// scores one block; wave 0 then runs the list over the 4 groups of 64 in
-// ascending block order and writes the chunk's top-(K-1) (score desc).
+// Decode, stage 1: workgroup = (chunk of 64 blocks, sequence).  Each wave
+// scores 16 blocks, two at a time (a half-wave reads one summary row with
+// 16-byte loads and reduces the dot product across its 32 lanes); wave 0 then
+// keeps the chunk's best K-1 and writes them (score desc) to the workspace.
+// Stage 2 (one wave per sequence) merges the chunk lists in chunk order, 64
+// candidates per ballot, and writes the selection.
 // ---------------------------------------------------------------------------
-constexpr int kDecChunk = 256;
+constexpr int kDecChunk = 64;
 
-__global__ __launch_bounds__(256) void topk_decode_partial(
-    const float *__restrict__ idx_q, const int64_t *__restrict__ seq_len,
-    const float *__restrict__ kmax, int64_t nb_max, int d_idx, int B, int topk,
-    float *__restrict__ ws_s, int *__restrict__ ws_b, int n_chunks) {
-  __shared__ float qv[1024];
-  __shared__ float scs[kDecChunk];
-  const int s = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
-  const int km = topk - 1;
-  const int64_t len = seq_len[s];
-  const int64_t own = len >= 1 ? (len - 1) / B : 0;
-  for (int c = tid; c < d_idx; c += 256) qv[c] = idx_q[(int64_t)s * d_idx + c];
-  __syncthreads();
-  const int64_t b = (int64_t)ch * kDecChunk + tid;
-  float sc = -INFINITY;
-  if (b < own && b < nb_max) {
-    const float *row = kmax + ((int64_t)s * nb_max + b) * d_idx;
-    float acc = 0.f;
-    for (int c = 0; c < d_idx; ++c) acc = fmaf(qv[c], row[c], acc);
-    sc = acc;
-  }
-  scs[tid] = sc;
-  __syncthreads();
-  if (tid >= 64) return;
-  const int lane = tid;
-  int cnt = 0;
-  float ls = -INFINITY;
-  int lb = -1;
-  for (int g = 0; g < kDecChunk / 64; ++g) {
-    const int64_t bb = (int64_t)ch * kDecChunk + g * 64 + lane;
-    const float x = scs[g * 64 + lane];
-    const bool valid = bb < own && bb < nb_max;
+// As list_insert, with explicit per-lane block ids.
+__device__ __forceinline__ void list_insert_ids(float s, int bid, uint64_t mask,
+                                                int km, int &cnt, float &ls,
+                                                int &lb) {
+  const int lane = threadIdx.x & 63;
+  while (mask) {
+    const int src = __ffsll((unsigned long long)mask) - 1;
+    const float sj = shfl_f(s, src);
+    const int bj = shfl_i(bid, src);
+    const int pos = __popcll(__ballot(lane < cnt && ls >= sj));
+    const float ps = shfl_f(ls, lane > 0 ? lane - 1 : 0);
+    const int pb = shfl_i(lb, lane > 0 ? lane - 1 : 0);
+    const int last = cnt < km - 1 ? cnt : km - 1;
+    if (lane > pos && lane <= last) {
+      ls = ps;
+      lb = pb;
+    }
+    if (lane == pos) {
+      ls = sj;
+      lb = bj;
+    }
+    cnt = cnt + 1 < km ? cnt + 1 : km;
     const float thr = shfl_f(ls, km - 1);
-    const uint64_t mask = __ballot(valid && (cnt < km || x > thr));
-    if (mask) list_insert(x, ch * kDecChunk + g * 64, mask, km, cnt, ls, lb);
-  }
-  const int64_t o = ((int64_t)s * n_chunks + ch) * km;
-  if (lane < km) {
-    ws_s[o + lane] = lane < cnt ? ls : -INFINITY;
-    ws_b[o + lane] = lane < cnt ? lb : -1;
+    mask &= ~(1ull << src);
+    mask &= __ballot(cnt < km || s > thr);
   }
 }
 
-// Decode, stage 2: one wave per sequence merges the chunk lists in chunk
-// order (ascending blocks; within a chunk, rank order keeps ties ascending).
+__global__ __launch_bounds__(256) void topk_decode_kernel(
+    const float *__restrict__ idx_q, const int64_t *__restrict__ seq_len,
+    const float *__restrict__ kmax, int64_t nb_max, int d_idx, int B, int topk,
+    float *__restrict__ ws_s, int *__restrict__ ws_b, int n_chunks) {
+  __shared__ float scs[kDecChunk];
+  const int s = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int km = topk - 1;
+  const int64_t len = seq_len[s];
+  const int64_t own = len >= 1 ? (len - 1) / B : 0;
+  const float *qv = idx_q + (int64_t)s * d_idx;
+
+  // scores of blocks ch*64 + wave*16 + 2*it + (lane >> 5)
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t bw = (int64_t)ch * kDecChunk + wave * 16 + half;
+  if ((d_idx & 3) == 0 && d_idx <= 128) {
+    // one float4 of the row per lane: all eight row loads in flight at once
+    const bool has = 4 * l32 < d_idx;
+    const float4 qa = has ? *reinterpret_cast<const float4 *>(qv + 4 * l32)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 x[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {       // issued before own is known
+      const int64_t b = bw + 2 * it;
+      x[it] = (has && b < nb_max)
+                  ? *reinterpret_cast<const float4 *>(
+                        kmax + ((int64_t)s * nb_max + b) * d_idx + 4 * l32)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      float acc = qa.x * x[it].x;
+      acc = fmaf(qa.y, x[it].y, acc);
+      acc = fmaf(qa.z, x[it].z, acc);
+      acc = fmaf(qa.w, x[it].w, acc);
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      const int64_t b = bw + 2 * it;
+      if (l32 == 0) scs[wave * 16 + 2 * it + half] = (b < own && b < nb_max) ? acc : -INFINITY;
+    }
+  } else {
+    for (int it = 0; it < 8; ++it) {
+      const int64_t b = bw + 2 * it;
+      float acc = 0.f;
+      const bool valid = b < own && b < nb_max;
+      if (valid) {
+        const float *row = kmax + ((int64_t)s * nb_max + b) * d_idx;
+        for (int c = l32; c < d_idx; c += 32) acc = fmaf(row[c], qv[c], acc);
+      }
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      if (l32 == 0) scs[wave * 16 + 2 * it + half] = valid ? acc : -INFINITY;
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && km > 0) {
+    const int64_t bb = (int64_t)ch * kDecChunk + lane;
+    const float x = scs[lane];
+    const bool valid = bb < own && bb < nb_max;
+    int cnt = 0;
+    float ls = -INFINITY;
+    int lb = -1;
+    const uint64_t mask = __ballot(valid);
+    list_insert(x, ch * kDecChunk, mask, km, cnt, ls, lb);
+    const int64_t o = ((int64_t)s * n_chunks + ch) * km;
+    if (lane < km) {
+      ws_s[o + lane] = lane < cnt ? ls : -INFINITY;
+      ws_b[o + lane] = lane < cnt ? lb : -1;
+    }
+  }
+}
+
 __global__ __launch_bounds__(64) void topk_decode_merge(
     const int64_t *__restrict__ seq_len, int B, int topk,
     const float *__restrict__ ws_s, const int *__restrict__ ws_b, int n_chunks,
@@ -233,40 +292,31 @@ __global__ __launch_bounds__(64) void topk_decode_merge(
   const int s = blockIdx.x, lane = threadIdx.x;
   const int km = topk - 1;
   const int64_t len = seq_len[s];
-  const int own = (int)(len >= 1 ? (len - 1) / B : 0);
+  const int64_t own = len >= 1 ? (len - 1) / B : 0;
   int cnt = 0;
   float ls = -INFINITY;
   int lb = INT32_MAX;
-  for (int ch = 0; km > 0 && ch < n_chunks; ++ch) {
-    const int64_t o = ((int64_t)s * n_chunks + ch) * km;
-    const float x = lane < km ? ws_s[o + lane] : -INFINITY;
-    const int xb = lane < km ? ws_b[o + lane] : -1;
-    // Entries arrive in rank order; insert them one by one in that order.
-    uint64_t mask = __ballot(xb >= 0);
-    while (mask) {
-      const int src = __ffsll((unsigned long long)mask) - 1;
-      mask &= ~(1ull << src);
-      const float sj = shfl_f(x, src);
-      const int bj = shfl_i(xb, src);
+  const int64_t nc = (int64_t)n_chunks * km;
+  const int64_t o0 = (int64_t)s * n_chunks * km;
+  constexpr int kPre = 8;   // candidate groups of 64 fetched in one round trip
+  for (int64_t base0 = 0; km > 0 && base0 < nc; base0 += 64 * kPre) {
+    float xs[kPre];
+    int xbs[kPre];
+#pragma unroll
+    for (int gi = 0; gi < kPre; ++gi) {
+      const int64_t i = base0 + 64 * gi + lane;
+      xs[gi] = i < nc ? ws_s[o0 + i] : -INFINITY;
+      xbs[gi] = i < nc ? ws_b[o0 + i] : -1;
+    }
+#pragma unroll
+    for (int gi = 0; gi < kPre; ++gi) {
       const float thr = shfl_f(ls, km - 1);
-      if (!(cnt < km || sj > thr)) break;   // later entries score no higher
-      const int pos = __popcll(__ballot(lane < cnt && ls >= sj));
-      const float ps = shfl_f(ls, lane > 0 ? lane - 1 : 0);
-      const int pb = shfl_i(lb, lane > 0 ? lane - 1 : 0);
-      const int last = cnt < km - 1 ? cnt : km - 1;
-      if (lane > pos && lane <= last) {
-        ls = ps;
-        lb = pb;
-      }
-      if (lane == pos) {
-        ls = sj;
-        lb = bj;
-      }
-      cnt = cnt + 1 < km ? cnt + 1 : km;
+      const uint64_t mask = __ballot(xbs[gi] >= 0 && (cnt < km || xs[gi] > thr));
+      if (mask) list_insert_ids(xs[gi], xbs[gi], mask, km, cnt, ls, lb);
     }
   }
   if (lane >= cnt) lb = INT32_MAX;
-  write_row(sel + (int64_t)s * topk, topk, cnt, lb, own);
+  write_row(sel + (int64_t)s * topk, topk, cnt, lb, (int)own);
 }
 
 }  // namespace
@@ -282,6 +332,7 @@ hipError_t launch_topk_prefill(const float *idx_q, int64_t n_q, int64_t q_pos0,
   return hipGetLastError();
 }
 
+// Layout: [chunk scores][chunk block ids].
 size_t topk_decode_ws_bytes(int32_t n_seq, int64_t nb_max, int32_t topk) {
   const int64_t n_chunks = (nb_max + kDecChunk - 1) / kDecChunk;
   const size_t n = (size_t)n_seq * n_chunks * (topk > 1 ? topk - 1 : 1);
@@ -295,15 +346,14 @@ hipError_t launch_topk_decode(const float *idx_q, int32_t n_seq,
                               hipStream_t st) {
   const int n_chunks = (int)((nb_max + kDecChunk - 1) / kDecChunk);
   const size_t n = (size_t)n_seq * n_chunks * (topk > 1 ? topk - 1 : 1);
-  float *ws_s = static_cast<float *>(ws);
-  int *ws_b = reinterpret_cast<int *>(static_cast<char *>(ws) +
-                                      align256(n * sizeof(float)));
+  char *w = static_cast<char *>(ws);
+  float *ws_s = reinterpret_cast<float *>(w);
+  w += align256(n * sizeof(float));
+  int *ws_b = reinterpret_cast<int *>(w);
   if (topk > 1) {
-    hipLaunchKernelGGL(topk_decode_partial, dim3(n_chunks, n_seq), dim3(256), 0,
-                       st, idx_q, seq_len, kmax, nb_max, d_idx, block, topk,
-                       ws_s, ws_b, n_chunks);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_decode_kernel, dim3(n_chunks, n_seq), dim3(256), 0, st,
+                       idx_q, seq_len, kmax, nb_max, d_idx, block, topk, ws_s,
+                       ws_b, n_chunks);
   }
   hipLaunchKernelGGL(topk_decode_merge, dim3(n_seq), dim3(64), 0, st, seq_len,
                      block, topk, ws_s, ws_b, n_chunks, sel);

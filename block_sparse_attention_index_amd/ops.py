@@ -126,7 +126,8 @@ def msa_index_pool(idx_k: torch.Tensor, block: int, kmax: torch.Tensor | None = 
                    blk_end: int | None = None, nb_max: int | None = None):
     """Block max-pool of index keys.  ``idx_k`` [L, d_idx] or [n_seq, L, d_idx]
     fp32 -> ``kmax`` [nb_max, d_idx] or [n_seq, nb_max, d_idx] fp32.
-    ``blk_begin < 0`` pools only each sequence's last block (decode append)."""
+    ``blk_begin = -1`` re-pools each sequence's last block; ``-2`` folds only
+    the newest token into it (decode append)."""
     _dev(idx_k, "idx_k", torch.float32)
     batched = idx_k.dim() == 3
     n_seq = idx_k.shape[0] if batched else 1

@@ -130,12 +130,13 @@ def decode_step(q, idx_q, k_cache, v_cache, idx_k, kmax, seq_len, block: int,
 
     ``q`` [n_seq, Hq, d]; ``idx_q`` [n_seq, d_idx]; caches [n_seq, Hkv, len_max, d];
     ``idx_k`` [n_seq, len_max, d_idx]; ``kmax`` [n_seq, nb_max, d_idx] (updated in
-    place: the newest token's block is re-pooled).  Returns ``(o, lse, sel)``.
+    place: the newest token is folded into its block's running max, which
+    assumes the previous token was already pooled).  Returns ``(o, lse, sel)``.
     """
     d = q.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     bufs = bufs or alloc_decode(q, kmax, block, topk)
-    ops.msa_index_pool(idx_k, block, kmax=kmax, seq_len=seq_len, blk_begin=-1,
+    ops.msa_index_pool(idx_k, block, kmax=kmax, seq_len=seq_len, blk_begin=-2,
                        nb_max=kmax.shape[1])
     ops.msa_index_topk_decode(idx_q, seq_len, kmax, block, topk, sel=bufs.sel,
                               ws=bufs.topk_ws)

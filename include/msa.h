@@ -73,8 +73,15 @@ const char *msa_status_string(int status);
  *   idx_k    [n_seq][len_max][d_idx] fp32
  *   seq_len  device int64 [n_seq], 1 <= len_s <= len_max; NULL = all len_max
  *   blocks   [blk_begin, blk_end) with 0 <= blk_begin < blk_end <= nb_max;
- *            blk_begin < 0 selects, per sequence, only the block holding its
+ *            blk_begin == -1 selects, per sequence, only the block holding its
  *            last token (len_s - 1) / B -- the block a decode step appends to
+ *            -- and re-pools it from all its tokens;
+ *            blk_begin == -2 is the O(d_idx) append form of the same update:
+ *            with t = len_s - 1, kmax[s][t/B] = idx_k[s][t] when t starts the
+ *            block, else max(kmax[s][t/B], idx_k[s][t]).  It is exact provided
+ *            kmax[s][t/B] already holds the max over tokens [t/B*B, t), which
+ *            holds after a full pool or a previous append of token t-1.
+ *            blk_end is ignored for both modes.
  *   kmax     [n_seq][nb_max][d_idx] fp32, nb_max >= ceil(len_max / B)
  * ------------------------------------------------------------------------ */
 int msa_index_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
@@ -185,7 +192,8 @@ int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
  *   sel      [n_seq][K] int32 from msa_index_topk_decode
  *   o        [n_seq][Hq][d] fp32;  lse [n_seq][Hq] fp32 (may be NULL)
  *   ws       device scratch of msa_decode_workspace_bytes() bytes
- *   Supported: fp32 and bf16; d in {64, 128, 256}; Hq/Hkv <= 16.
+ *   Supported: fp32 and bf16 with d in {64, 128}, bf16 with d = 256;
+ *   Hq/Hkv in {1, 2, 4, 8, 16}.
  * ------------------------------------------------------------------------ */
 size_t msa_decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t d,
                                   int32_t block, int32_t topk);

@@ -67,6 +67,30 @@ def test_pool_batched_ragged_and_last_block(orc):
         assert np.array_equal(got[s, :nb], orc.pool(x2[s, :L].numpy(), B))
 
 
+def test_pool_append_mode_equals_full_pool(orc):
+    # folding tokens one at a time into a running block max reproduces the
+    # full pool (bit-exact), across block boundaries and for several sequences
+    n, Lmax, B, d = 2, 700, 64, 128
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn(n, Lmax, d, generator=g)
+    x[:, ::7, 3] = -0.0
+    start = [600, 250]
+    nb_max = -(-Lmax // B)
+    xd = x.to(DEV)
+    kmax = torch.full((n, nb_max, d), float("nan"), device=DEV)
+    ops.msa_index_pool(xd, B, kmax=kmax, nb_max=nb_max,
+                       seq_len=torch.tensor(start, dtype=torch.int64, device=DEV))
+    for step in range(1, 80):
+        lens = torch.tensor([L + step for L in start], dtype=torch.int64, device=DEV)
+        ops.msa_index_pool(xd, B, kmax=kmax, seq_len=lens, blk_begin=-2, nb_max=nb_max)
+    got = _np(kmax)
+    for s_, L in enumerate(start):
+        Lf = L + 79
+        nbf = -(-Lf // B)
+        assert np.array_equal(got[s_, :nbf].view(np.uint32),
+                              orc.pool(x[s_, :Lf].numpy(), B).view(np.uint32))
+
+
 # --------------------------------------------------------------------------
 # top-K (prefill)
 # --------------------------------------------------------------------------
@@ -212,12 +236,19 @@ def test_prefill_small_heads_d64(orc):
 # --------------------------------------------------------------------------
 # decode
 # --------------------------------------------------------------------------
-def test_decode_small(orc):
-    cfg = synth.Config("dec-small", 3000, "bf16", 16, 2, 128, 128, 64, 8, 4,
-                       n_seq=3, mode="decode")
-    _say("decode small (3 sequences, ragged lengths)")
+@pytest.mark.parametrize("dtype,hq,hkv,d,B,K,lens", [
+    ("bf16", 16, 2, 128, 64, 8, [3000, 2049, 100]),     # matrix-core path
+    ("bf16", 64, 8, 128, 512, 8, [3000, 1537, 600]),    # the 1M decode shape
+    ("bf16", 32, 2, 128, 128, 5, [2000, 129, 1]),       # G = 16, one-token cache
+    ("f32", 8, 2, 64, 64, 4, [1200, 700, 65]),          # VALU path
+])
+def test_decode_small(orc, dtype, hq, hkv, d, B, K, lens):
+    T = max(lens)
+    cfg = synth.Config("dec-small", T, dtype, hq, hkv, d, 128, B, K, 4,
+                       n_seq=len(lens), mode="decode")
+    _say(f"decode {dtype} G={hq // hkv} d={d} B={B} K={K} lens={lens}")
     x = synth.decode_inputs(cfg, "cpu", 0)
-    lens = np.array([3000, 2049, 100], np.int64)
+    lens = np.array(lens, np.int64)
     B, K = cfg.block, cfg.topk
     nb_max = cfg.nb
     seq_len = torch.from_numpy(lens).to(DEV)
@@ -229,9 +260,15 @@ def test_decode_small(orc):
         nb = -(-L // B)
         kmax_o[s, :nb] = orc.pool(x["idx_k"][s, :L].numpy(), B)
         assert np.array_equal(_np(kmax_d)[s, :nb], kmax_o[s, :nb])
-    # top-K on the oracle's summaries
+    # top-K on the oracle's summaries; a second call on the same workspace
+    # agrees with the first
+    tws = torch.empty(ops.load().msa_topk_decode_workspace_bytes(cfg.n_seq, nb_max, K),
+                      dtype=torch.uint8, device=DEV)
     sel_d = _np(ops.msa_index_topk_decode(x["idx_q"].to(DEV), seq_len,
-                                          torch.from_numpy(kmax_o).to(DEV), B, K))
+                                          torch.from_numpy(kmax_o).to(DEV), B, K, ws=tws))
+    sel_d2 = _np(ops.msa_index_topk_decode(x["idx_q"].to(DEV), seq_len,
+                                           torch.from_numpy(kmax_o).to(DEV), B, K, ws=tws))
+    assert np.array_equal(sel_d, sel_d2)
     for s, L in enumerate(lens):
         pos = np.array([L - 1])
         so, gr, ga, eb = orc.select(x["idx_q"][s:s + 1].numpy(), pos, kmax_o[s], B, K)
@@ -243,17 +280,23 @@ def test_decode_small(orc):
         so, *_ = orc.select(x["idx_q"][s:s + 1].numpy(), np.array([L - 1]), kmax_o[s], B, K)
         sels.append(so[0])
     sel_o = np.stack(sels).astype(np.int32)
-    o, lse = ops.msa_sparse_gqa_decode(x["q"].to(DEV), x["k_cache"].to(DEV),
-                                       x["v_cache"].to(DEV), seq_len,
-                                       torch.from_numpy(sel_o).to(DEV), B, cfg.scale)
+    aws = torch.empty(ops.load().msa_decode_workspace_bytes(cfg.n_seq, cfg.Hq, cfg.d, B, K),
+                      dtype=torch.uint8, device=DEV)
+    for rep in range(2):                      # second call reuses the workspace
+        o, lse = ops.msa_sparse_gqa_decode(x["q"].to(DEV), x["k_cache"].to(DEV),
+                                           x["v_cache"].to(DEV), seq_len,
+                                           torch.from_numpy(sel_o).to(DEV), B, cfg.scale,
+                                           ws=aws)
     o, lse = _np(o), _np(lse)
     for s, L in enumerate(lens):
         oo, lo, _ = orc.attend(synth.host(x["q"][s:s + 1]), synth.host(x["k_cache"][s]),
                                synth.host(x["v_cache"][s]), np.array([0]),
-                               np.array([L - 1]), sel_o[s:s + 1], B, cfg.scale, 1)
+                               np.array([L - 1]), sel_o[s:s + 1], B, cfg.scale,
+                               0 if dtype == "f32" else 1)
         eo, el = max_abs(o[s], oo[0]), max_abs(lse[s], lo[0])
         _say(f"  seq {s} len {L}: max|do| {eo:.3g} max|dlse| {el:.3g}")
-        assert eo <= TOL_BF16 and el <= TOL_BF16
+        tol = TOL_F32 if dtype == "f32" else TOL_BF16
+        assert eo <= tol and el <= tol
 
 
 # --------------------------------------------------------------------------
@@ -278,3 +321,48 @@ def test_pipeline_end_to_end_tiny(orc):
     el = max_abs(_np(lse)[same], lo[same])
     _say(f"  flagged {nf}, differing {nm}; max|do| {eo:.3g} max|dlse| {el:.3g}")
     assert eo <= TOL_F32 and el <= TOL_F32
+
+
+def test_decode_steps_in_a_captured_graph(orc):
+    # A chain of decode steps captured once and replayed must give the eager
+    # results on every replay (eager work and synchronisation in between).
+    cfg = synth.Config("dec-graph", 1500, "bf16", 16, 2, 128, 128, 64, 6, 3,
+                       n_seq=2, mode="decode")
+    _say("decode graph replay")
+    x = synth.decode_inputs(cfg, "cpu", 3)
+    B, K, n_steps = cfg.block, cfg.topk, 5
+    nb_max = cfg.nb
+    d = {k_: v_.to(DEV) for k_, v_ in x.items()}
+    lens0 = [1500 - n_steps, 1000 - n_steps]
+    seq_lens = [torch.tensor([a + s_ + 1 for a in lens0], dtype=torch.int64, device=DEV)
+                for s_ in range(n_steps)]
+    kmax0 = torch.empty((cfg.n_seq, nb_max, cfg.d_idx), device=DEV)
+    ops.msa_index_pool(d["idx_k"], B, kmax=kmax0, nb_max=nb_max,
+                       seq_len=torch.tensor(lens0, dtype=torch.int64, device=DEV))
+    kmax = kmax0.clone()
+    bufs = pipeline.alloc_decode(d["q"], kmax, B, K)
+    outs = [torch.empty_like(bufs.o) for _ in range(n_steps)]
+
+    def run():
+        for s_ in range(n_steps):
+            o, _, _ = pipeline.decode_step(d["q"], d["idx_q"], d["k_cache"], d["v_cache"],
+                                           d["idx_k"], kmax, seq_lens[s_], B, K, cfg.scale,
+                                           bufs=bufs)
+            outs[s_].copy_(o)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [o_.cpu().clone() for o_ in outs]
+    kmax.copy_(kmax0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        kmax.copy_(kmax0)                       # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for s_ in range(n_steps):
+            assert torch.equal(outs[s_].cpu(), eager[s_]), f"replay {rep} step {s_}"
+
