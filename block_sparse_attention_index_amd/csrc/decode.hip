@@ -497,7 +497,7 @@ bool decode_supported(int32_t dtype, int32_t d, int32_t group) {
                     group == 16;
   if (!g_ok) return false;
   if (d == 64 || d == 128) return true;
-  return d == 256 && (dtype == 1 || group <= 8);   // LDS budget
+  return d == 256 && dtype == 1;   // fp32 rows of 256 do not fit the LDS stage
 }
 
 hipError_t launch_decode(const void *q, const void *k_cache,

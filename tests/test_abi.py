@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: every function include/msa.h declares is
+exported by libmsa.so, and argument validation returns the documented
+status before anything is enqueued (the calls below never reach a launch:
+each fails a check first, so fake non-null pointers are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+OK, EINVAL, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch  # noqa: F401  (loads the HIP runtime the library links)
+    from block_sparse_attention_index_amd import ops
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.fail("libmsa.so is not built: run __graft_entry__.build()")
+    return ops.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    from block_sparse_attention_index_amd import ops
+    assert sorted(ops.ENTRY_POINTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, word in [(OK, b"MSA_OK"), (EINVAL, b"INVALID_ARG"), (EUNSUP, b"UNSUPPORTED"),
+                       (EWS, b"WORKSPACE"), (EHIP, b"HIP")]:
+        assert word in lib.msa_status_string(code)
+    assert lib.msa_status_string(12345)
+
+
+def test_pool_validation(lib):
+    P = FAKE
+    assert lib.msa_index_pool(None, 1, 100, None, 64, 64, 0, 2, P, 2, None) == EINVAL
+    assert lib.msa_index_pool(P, 1, 100, None, 64, 60, 0, 2, P, 2, None) == EINVAL   # B % 16
+    assert lib.msa_index_pool(P, 1, 100, None, 64, 64, 0, 2, P, 1, None) == EINVAL   # nb_max
+    assert lib.msa_index_pool(P, 1, 100, None, 64, 64, 2, 2, P, 2, None) == EINVAL   # range
+    assert lib.msa_index_pool(P, 1, 100, None, 64, 64, -3, 0, P, 2, None) == EINVAL  # mode
+    assert lib.msa_index_pool(P, 1, 100, None, 2000, 64, 0, 2, P, 2, None) == EINVAL  # d_idx
+    assert lib.msa_index_pool(P, 0, 100, None, 64, 64, 0, 2, P, 2, None) == EINVAL   # n_seq
+
+
+def test_topk_validation(lib):
+    P = FAKE
+    assert lib.msa_index_topk(P, 10, 0, P, 1, 64, 64, 0, P, None) == EINVAL      # topk 0
+    assert lib.msa_index_topk(P, 10, 0, P, 1, 64, 64, 65, P, None) == EINVAL     # topk > 64
+    assert lib.msa_index_topk(P, 200, 0, P, 2, 64, 64, 4, P, None) == EINVAL     # own >= nb
+    assert lib.msa_index_topk(P, 0, 0, P, 1, 64, 64, 4, P, None) == OK           # empty: no-op
+    need = lib.msa_topk_decode_workspace_bytes(2, 100, 8)
+    assert need > 0
+    assert lib.msa_index_topk_decode(P, 2, P, P, 100, 64, 64, 8, P, P, need - 1, None) == EWS
+    assert lib.msa_index_topk_decode(P, 2, None, P, 100, 64, 64, 8, P, P, need, None) == EINVAL
+
+
+def test_invert_validation(lib):
+    P = FAKE
+    need = lib.msa_invert_workspace_bytes(5000, 8, 100)
+    assert need >= 100 * 4
+    assert lib.msa_invert_selection(P, 5000, 8, 100, P, P, P, P, need - 1, None) == EWS
+    assert lib.msa_invert_selection(P, 5000, 8, 0, P, P, P, P, need, None) == EINVAL
+    assert lib.msa_invert_selection(P, 1 << 30, 8, 100, P, P, P, P, 1 << 40, None) == EINVAL
+
+
+def test_prefill_validation(lib):
+    P = FAKE
+    f = lib.msa_sparse_gqa_prefill
+    args = lambda **kw: dict(dict(q=P, k=P, v=P, dt=1, kvs=4096, q0=0, nq=4096, hq=64, hkv=8,
+                                  d=128, B=64, sel=P, K=16, rp=P, ql=P, sl=P, sc=0.1, o=P,
+                                  lse=None, ws=P, wsb=1 << 40, st=None), **kw)
+    call = lambda a: f(a["q"], a["k"], a["v"], a["dt"], a["kvs"], a["q0"], a["nq"], a["hq"],
+                       a["hkv"], a["d"], a["B"], a["sel"], a["K"], a["rp"], a["ql"], a["sl"],
+                       a["sc"], a["o"], a["lse"], a["ws"], a["wsb"], a["st"])
+    assert call(args(q=None)) == EINVAL
+    assert call(args(hq=60)) == EINVAL                    # Hq % Hkv
+    assert call(args(dt=2)) == EINVAL                     # dtype
+    assert call(args(q0=10)) == EINVAL                    # q_pos0 + n_q > kv_stride
+    assert call(args(sc=float("inf"))) == EINVAL
+    assert call(args(d=96)) == EUNSUP                     # no kernel for d = 96
+    assert call(args(hq=24, hkv=8)) == EUNSUP             # group 3
+    need = lib.msa_prefill_workspace_bytes(0, 4096, 64, 128, 64, 16)
+    assert call(args(wsb=need - 1)) == EWS
+
+
+def test_prefill_workspace_holds_the_partials(lib):
+    # the KV-outer pass keeps one fp32 partial (d values + lse) per
+    # (non-own pair, query head); non-own pairs have a closed form
+    for q0, n, B, K in [(0, 32768, 64, 16), (1000, 3000, 128, 6), (0, 1 << 20, 512, 8)]:
+        p = sum((min(K, (pos // B) + 1) - 1) for pos in range(q0, q0 + n)) if n < 100000 else \
+            sum((min(K, b + 1) - 1) * min(B, q0 + n - b * B) for b in range((q0 + n + B - 1) // B))
+        need = lib.msa_prefill_workspace_bytes(q0, n, 64, 128, B, K)
+        assert need >= p * 64 * 129 * 4
+
+
+def test_decode_validation(lib):
+    P = FAKE
+    need = lib.msa_decode_workspace_bytes(4, 64, 128, 512, 8)
+    assert need > 0
+    f = lib.msa_sparse_gqa_decode
+    assert f(P, P, P, 1, 4, 1000, P, 64, 8, 128, 512, P, 8, 0.1, P, None, P, need - 1, None) == EWS
+    assert f(P, P, P, 1, 4, 1000, None, 64, 8, 128, 512, P, 8, 0.1, P, None, P, need, None) == EINVAL
+    assert f(P, P, P, 1, 4, 1000, P, 64, 8, 96, 512, P, 8, 0.1, P, None, P, need, None) == EUNSUP
+    assert f(P, P, P, 0, 4, 1000, P, 64, 8, 256, 512, P, 8, 0.1, P, None, P, need, None) == EUNSUP
