@@ -162,12 +162,13 @@ int msa_invert_selection(const int32_t *sel, int64_t n_q, int32_t topk,
                                       slot, ws, as_stream(stream)));
 }
 
-size_t msa_prefill_workspace_bytes(int64_t q_pos0, int64_t n_q, int32_t hq,
-                                   int32_t d, int32_t block, int32_t topk) {
-  if (q_pos0 < 0 || n_q < 0 || hq < 1 || d < 1 || !block_ok(block) ||
-      !topk_ok(topk))
+size_t msa_prefill_workspace_bytes(int32_t dtype, int64_t q_pos0, int64_t n_q,
+                                   int32_t hq, int32_t d, int32_t block,
+                                   int32_t topk) {
+  if ((dtype != MSA_F32 && dtype != MSA_BF16) || q_pos0 < 0 || n_q < 0 ||
+      hq < 1 || d < 1 || !block_ok(block) || !topk_ok(topk))
     return 0;
-  return msa::prefill_ws_bytes(q_pos0, n_q, hq, d, block, topk);
+  return msa::prefill_ws_bytes(dtype, q_pos0, n_q, hq, d, block, topk);
 }
 
 int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
@@ -186,7 +187,7 @@ int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
     return MSA_ERR_INVALID_ARG;
   if (!msa::prefill_supported(dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
   if (n_q == 0) return MSA_OK;
-  if (ws_bytes < msa::prefill_ws_bytes(q_pos0, n_q, hq, d, block, topk))
+  if (ws_bytes < msa::prefill_ws_bytes(dtype, q_pos0, n_q, hq, d, block, topk))
     return MSA_ERR_WORKSPACE;
   return status_of(msa::launch_prefill(q, k, v, dtype, kv_stride, q_pos0, n_q,
                                        hq, hkv, d, block, sel, topk, row_ptr,

@@ -38,8 +38,8 @@ hipError_t launch_invert(const int32_t *sel, int64_t n_q, int32_t topk,
 // query keeps min(K, own + 1) blocks.
 int64_t nonown_pairs(int64_t q_pos0, int64_t n_q, int32_t block, int32_t topk);
 
-size_t prefill_ws_bytes(int64_t q_pos0, int64_t n_q, int32_t hq, int32_t d,
-                        int32_t block, int32_t topk);
+size_t prefill_ws_bytes(int32_t dtype, int64_t q_pos0, int64_t n_q, int32_t hq,
+                        int32_t d, int32_t block, int32_t topk);
 bool prefill_supported(int32_t dtype, int32_t d, int32_t group);
 hipError_t launch_prefill(const void *q, const void *k, const void *v,
                           int32_t dtype, int64_t kv_stride, int64_t q_pos0,

@@ -333,10 +333,16 @@ hipError_t dispatch_g(int G, const T *q, const T *k, const T *v,
 
 }  // namespace
 
-size_t prefill_ws_bytes(int64_t q_pos0, int64_t n_q, int32_t hq, int32_t d,
-                        int32_t block, int32_t topk) {
+size_t prefill_ws_bytes(int32_t dtype, int64_t q_pos0, int64_t n_q, int32_t hq,
+                        int32_t d, int32_t block, int32_t topk) {
   const int64_t nb = (q_pos0 + n_q + block - 1) / block;
   const int64_t np = nonown_pairs(q_pos0, n_q, block, topk);
+  if (dtype == 1 && d == 128) {
+    // matrix-core path: fp16 partial outputs and (lse, exponent) float2s
+    return align256((size_t)(nb + 1) * 4) + align256((size_t)np * hq * d * 2) +
+           align256((size_t)np * hq * 8) + align256((size_t)(np / 16 + nb) * 16) +
+           align256((size_t)(np + 256 * nb) * 4);
+  }
   // + per-tile metadata of the MFMA pass A, bounded for any head group:
   //   tiles <= pairs / 16 + nb (16 = smallest tile), rows <= pairs + 256 nb.
   return align256((size_t)(nb + 1) * 4) + align256((size_t)np * hq * d * 4) +

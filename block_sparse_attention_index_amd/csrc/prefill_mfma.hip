@@ -93,6 +93,40 @@ __device__ __forceinline__ int64_t frag_off(int64_t n, int g, int hq, int G,
          hf * 4 * G + hl * 4;
 }
 
+// A partial record of one (pair, query head): the normalised output o as
+// fp16 scaled by 2^-e, where 2^e is the smallest power of two above max|o|
+// (so every stored value is below 1 in magnitude -- no overflow -- and the
+// relative precision is 2^-11 of max|o|), plus (lse, e) as a float2.  The
+// merge weight of the record is 2^(lse - M) for the normaliser and
+// 2^(lse + e - M) for the stored values.
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void put_partial(uint16_t *part_o, float2 *part_le,
+                                            int64_t n, int g, int hq, int G,
+                                            int hl, int hf, const f32x16 (&acc)[4],
+                                            float mref, float ltot) {
+  const float inv = 1.f / ltot;
+  float mabs = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mabs = fmaxf(mabs, fabsf(acc[cb][r]));
+  mabs = max_with_partner(mabs * inv);
+  int e = 0;
+  if (mabs > 0.f) (void)frexpf(mabs, &e);
+  const float f = ldexpf(inv, -e);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      float4 v = make_float4(acc[cb][4 * rg] * f, acc[cb][4 * rg + 1] * f,
+                             acc[cb][4 * rg + 2] * f, acc[cb][4 * rg + 3] * f);
+      const f16x4 hv = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+      *reinterpret_cast<f16x4 *>(part_o + frag_off(n, g, hq, G, hl, cb, rg, hf)) = hv;
+    }
+  if (hf == 0) part_le[n * hq + (int64_t)g * G + hl] = make_float2(mref + __log2f(ltot), (float)e);
+}
+
 // NB = 32-row N-blocks per wave, NW = waves per workgroup.
 template <int G, int NB, int NW, bool OWN>
 __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
@@ -102,7 +136,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
     const int32_t *__restrict__ q_list, const int32_t *__restrict__ tile_ptr,
     int64_t nb, const int32_t *__restrict__ sel, int topk,
     const int32_t *__restrict__ slot, float scale_log2,
-    float *__restrict__ part_o, float *__restrict__ part_lse, int64_t n_part,
+    uint16_t *__restrict__ part_o, float2 *__restrict__ part_le, int64_t n_part,
     float *__restrict__ o, float *__restrict__ lse) {
   constexpr int NT = 64 * NW;    // threads
   constexpr int TPN = 32 / G;    // tokens per 32-row N-block
@@ -290,16 +324,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
       const int64_t e = e0 + wave * TPW + nbk * TPN + j / G;
       const int64_t n_idx = e - own_through(b, q_pos0, n_q, B);
       if (n_idx < 0 || n_idx >= n_part) continue;
-      const float inv = 1.f / ltot;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          float4 val = make_float4(acc[nbk][cb][4 * rg] * inv, acc[nbk][cb][4 * rg + 1] * inv,
-                                   acc[nbk][cb][4 * rg + 2] * inv, acc[nbk][cb][4 * rg + 3] * inv);
-          *reinterpret_cast<float4 *>(part_o + frag_off(n_idx, g, hq, G, head[nbk], cb, rg, h)) = val;
-        }
-      if (h == 0) part_lse[n_idx * hq + hh] = mref[nbk] + __log2f(ltot);
+      put_partial(part_o, part_le, n_idx, g, hq, G, head[nbk], h, acc[nbk], mref[nbk], ltot);
     } else {
       if (!act[nbk]) continue;
       const int64_t i = qi[nbk];
@@ -312,7 +337,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
         if (bk < 0 || bk >= b) continue;
         const int64_t n_idx = xrow[kk] - own_through(bk, q_pos0, n_q, B);
         if (n_idx < 0 || n_idx >= n_part) continue;
-        mx = fmaxf(mx, part_lse[n_idx * hq + hh]);
+        mx = fmaxf(mx, part_le[n_idx * hq + hh].x);
       }
       float z = fast_exp2(own2 - mx);
       const float wo = z / ltot;
@@ -325,18 +350,19 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
         if (bk < 0 || bk >= b) continue;
         const int64_t n_idx = xrow[kk] - own_through(bk, q_pos0, n_q, B);
         if (n_idx < 0 || n_idx >= n_part) continue;
-        const float wk = fast_exp2(part_lse[n_idx * hq + hh] - mx);
-        z += wk;
+        const float2 le = part_le[n_idx * hq + hh];
+        z += fast_exp2(le.x - mx);
+        const float wk = fast_exp2(le.x + le.y - mx);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
-            const float4 pv = *reinterpret_cast<const float4 *>(
+            const f16x4 pv = *reinterpret_cast<const f16x4 *>(
                 part_o + frag_off(n_idx, g, hq, G, head[nbk], cb, rg, h));
-            acc[nbk][cb][4 * rg] = fmaf(wk, pv.x, acc[nbk][cb][4 * rg]);
-            acc[nbk][cb][4 * rg + 1] = fmaf(wk, pv.y, acc[nbk][cb][4 * rg + 1]);
-            acc[nbk][cb][4 * rg + 2] = fmaf(wk, pv.z, acc[nbk][cb][4 * rg + 2]);
-            acc[nbk][cb][4 * rg + 3] = fmaf(wk, pv.w, acc[nbk][cb][4 * rg + 3]);
+            acc[nbk][cb][4 * rg] = fmaf(wk, (float)pv.x, acc[nbk][cb][4 * rg]);
+            acc[nbk][cb][4 * rg + 1] = fmaf(wk, (float)pv.y, acc[nbk][cb][4 * rg + 1]);
+            acc[nbk][cb][4 * rg + 2] = fmaf(wk, (float)pv.z, acc[nbk][cb][4 * rg + 2]);
+            acc[nbk][cb][4 * rg + 3] = fmaf(wk, (float)pv.w, acc[nbk][cb][4 * rg + 3]);
           }
       }
       const float invz = 1.f / z;
@@ -352,6 +378,59 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
       if (lse && h == 0) lse[i * hq + hh] = (mx + __log2f(z)) * kLn2;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Asynchronous chunk staging for the persistent pass: global_load_lds_dwordx4
+// copies 16 bytes per lane straight into LDS at base + 16 * lane, so one wave
+// instruction fills four 256-byte rows; each lane picks which global segment
+// lands in its slot.  Rows are unpadded and XOR-swizzled by segment instead:
+//   K: segment s of row r at slot s ^ (r & 15)  -- the 16 rows read by a
+//      16-lane group for an A operand hit 16 distinct bank groups;
+//   V: segment s of row r at slot s ^ 2(r & 7) ^ ((r >> 3) & 1) -- the 4 rows
+//      x 2 segments of a ds_read_b64_tr_b16 group are 8 distinct slots.
+// Rows past the chunk repeat its last valid row (masked keys then meet finite
+// values: their weight is exactly 0).
+// ---------------------------------------------------------------------------
+struct AsyncSmem {
+  uint16_t Ks[kKC * kD];
+  uint16_t Vs[kKC * kD];
+};
+
+typedef __attribute__((address_space(1))) void *gptr_t;
+typedef __attribute__((address_space(3))) void *lptr_t;
+
+__device__ __forceinline__ int kswz(int r, int sgm) { return sgm ^ (r & 15); }
+__device__ __forceinline__ int vswz(int r, int sgm) {
+  return sgm ^ (2 * (r & 7)) ^ ((r >> 3) & 1);
+}
+
+template <int NW>
+__device__ __forceinline__ void async_chunk(AsyncSmem &sm, const uint16_t *k,
+                                            const uint16_t *v, int64_t row0,
+                                            int nrows) {
+  constexpr int IPW = (kKC * kD / 8) / (64 * NW);   // instructions per wave
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int inst = wave * IPW + i;
+    const int pslot = inst * 64 + lane;              // 16-byte slot in the tile
+    const int r = pslot >> 4, sp = pslot & 15;
+    const int64_t rr = row0 + (r < nrows ? r : nrows - 1);
+    __builtin_amdgcn_global_load_lds(
+        (gptr_t)(const_cast<uint16_t *>(k + rr * kD + kswz(r, sp) * 8)),
+        (lptr_t)(&sm.Ks[inst * 64 * 8]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        (gptr_t)(const_cast<uint16_t *>(v + rr * kD + vswz(r, sp) * 8)),
+        (lptr_t)(&sm.Vs[inst * 64 * 8]), 16, 0, 0);
+  }
+}
+
+// Wait for this thread's outstanding loads (the async copies included), then
+// publish the LDS tile to the workgroup.
+__device__ __forceinline__ void async_wait_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -391,12 +470,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     const uint16_t *__restrict__ v, int64_t kv_stride, int64_t q_pos0,
     int64_t n_q, int hq, int hkv, int B, const int32_t *__restrict__ tile_ptr,
     int64_t nb, const int4 *__restrict__ info, const int32_t *__restrict__ tq,
-    float scale_log2, float *__restrict__ part_o, float *__restrict__ part_lse,
+    float scale_log2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_le,
     int64_t n_part) {
-  constexpr int NT = 64 * NW;
   constexpr int TPN = 32 / G;
   constexpr int TPT = NW * TPN;
-  __shared__ MfmaSmem smb[2];
+  __shared__ AsyncSmem smb[2];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, j = lane & 31;
   const int tl = wave * TPN + j / G;  // token slot of this lane's row
@@ -433,15 +511,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
 
   bf16x8 qf[8];
   load_q(g, qraw, qf);
-  ChunkRegs<NT> cr;
   {
     const int64_t nk = kv_keys(inf.x);
-    load_chunk(cr, k + ((int64_t)g * kv_stride) * kD, v + ((int64_t)g * kv_stride) * kD,
-               (int64_t)inf.x * B, (int)(nk < kKC ? nk : kKC));
+    async_chunk<NW>(smb[0], k + ((int64_t)g * kv_stride) * kD,
+                    v + ((int64_t)g * kv_stride) * kD, (int64_t)inf.x * B,
+                    (int)(nk < kKC ? nk : kKC));
   }
   int buf = 0;
-  store_chunk(smb[0], cr);
-  __syncthreads();
+  async_wait_barrier();
 
   for (;;) {
     const int64_t wn = w + per;
@@ -471,19 +548,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
 
     for (int64_t ci = 0; ci < n_chunks; ++ci) {
       const int64_t kc = ci * kKC;
-      bool staged = true;
       if (ci + 1 < n_chunks) {
         const int64_t nxt = kc + kKC;
-        load_chunk(cr, kb, vb, b * B + nxt, (int)(nkeys - nxt < kKC ? nkeys - nxt : kKC));
+        async_chunk<NW>(smb[buf ^ 1], kb, vb, b * B + nxt,
+                        (int)(nkeys - nxt < kKC ? nkeys - nxt : kKC));
       } else if (has_next) {
         const int64_t nk = kv_keys(infn.x);
-        load_chunk(cr, k + ((int64_t)gn * kv_stride) * kD, v + ((int64_t)gn * kv_stride) * kD,
-                   (int64_t)infn.x * B, (int)(nk < kKC ? nk : kKC));
+        async_chunk<NW>(smb[buf ^ 1], k + ((int64_t)gn * kv_stride) * kD,
+                        v + ((int64_t)gn * kv_stride) * kD, (int64_t)infn.x * B,
+                        (int)(nk < kKC ? nk : kKC));
         load_q(gn, qrawn, qfn);
-      } else {
-        staged = false;
       }
-      MfmaSmem &sm = smb[buf];
+      AsyncSmem &sm = smb[buf];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const int koff0 = (int)kc + sub * 32;
@@ -493,8 +569,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
         for (int rr = 0; rr < 16; ++rr) sacc[rr] = 0.f;
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
+          const int kr = sub * 32 + j;
           const u32x4 kraw = *reinterpret_cast<const u32x4 *>(
-              &sm.Ks[(sub * 32 + j) * kKStr + cc * 16 + 8 * h]);
+              &sm.Ks[kr * kD + kswz(kr, cc * 2 + h) * 8]);
           sacc = mfma32(as_bf16x8(kraw), qf[cc], sacc);
         }
         if (koff0 + 31 >= nkeys) {
@@ -530,24 +607,26 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
         lsum += ps;
         const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
         const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+        // V^T operand: this lane's 16-lane group reads 4 keys x 16 columns;
+        // lane a16 supplies row (a16 / 4) and the 8-byte piece a16 % 4
         const int a16 = lane & 15;
-        const uint16_t *vbase = &sm.Vs[(sub * 32 + 4 * h + (a16 >> 2)) * kVStr +
-                                       16 * (j >> 4) + 4 * (a16 & 3)];
+        const int vrow0 = sub * 32 + 4 * h + (a16 >> 2);
+        const int vcol0 = 16 * (j >> 4) + 4 * (a16 & 3);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
-            const uint16_t *vr = vbase + 16 * ks * kVStr + cb * 32;
-            const u32x2 lo = lds_read_tr(vr);
-            const u32x2 hi = lds_read_tr(vr + 8 * kVStr);
+            const int col = cb * 32 + vcol0;
+            const int r0 = vrow0 + 16 * ks, r1 = r0 + 8;
+            const u32x2 lo = lds_read_tr(&sm.Vs[r0 * kD + vswz(r0, col >> 3) * 8 + (col & 7)]);
+            const u32x2 hi = lds_read_tr(&sm.Vs[r1 * kD + vswz(r1, col >> 3) * 8 + (col & 7)]);
             const u32x4 vraw = {lo[0], lo[1], hi[0], hi[1]};
             acc[cb] = mfma32(as_bf16x8(vraw), ks == 0 ? pb0 : pb1, acc[cb]);
           }
         }
       }
-      if (staged) store_chunk(smb[buf ^ 1], cr);
       buf ^= 1;
-      __syncthreads();
+      async_wait_barrier();
     }
 
     // partial output of this (query, head) for block b
@@ -556,18 +635,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     if (act) {
       const int64_t e = (int64_t)inf.y + tl;
       const int64_t n_idx = e - own_through(b, q_pos0, n_q, B);
-      if (n_idx >= 0 && n_idx < n_part) {
-        const float inv = 1.f / ltot;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            float4 val = make_float4(acc[cb][4 * rg] * inv, acc[cb][4 * rg + 1] * inv,
-                                     acc[cb][4 * rg + 2] * inv, acc[cb][4 * rg + 3] * inv);
-            *reinterpret_cast<float4 *>(part_o + frag_off(n_idx, g, hq, G, hl, cb, rg, h)) = val;
-          }
-        if (h == 0) part_lse[n_idx * hq + (int64_t)g * G + hl] = mref + __log2f(ltot);
-      }
+      if (n_idx >= 0 && n_idx < n_part)
+        put_partial(part_o, part_le, n_idx, g, hq, G, hl, h, acc, mref, ltot);
     }
     if (!has_next) break;
     w = wn;
@@ -599,7 +668,7 @@ hipError_t launch_mfma_g(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          const int32_t *row_ptr, const int32_t *q_list,
                          const int32_t *slot, float scale, float *o, float *lse,
                          int32_t *tile_ptr, int4 *info, int32_t *tq,
-                         float *part_o, float *part_lse, int64_t n_part,
+                         uint16_t *part_o, float2 *part_le, int64_t n_part,
                          hipStream_t st) {
   constexpr int TPT = NW * NB * (32 / G);
   const int64_t nb = (q_pos0 + n_q + B - 1) / B;
@@ -612,14 +681,14 @@ hipError_t launch_mfma_g(const uint16_t *q, const uint16_t *k, const uint16_t *v
     const int grid = 8 * ((num_cus() + 7) / 8);
     hipLaunchKernelGGL((prefill_nonown_persistent<G, NW>), dim3(grid), dim3(64 * NW),
                        0, st, q, k, v, kv_stride, q_pos0, n_q, hq, hkv, B, tile_ptr,
-                       nb, info, tq, sl2, part_o, part_lse, n_part);
+                       nb, info, tq, sl2, part_o, part_le, n_part);
   }
   const int64_t b_first = q_pos0 / B, b_last = (q_pos0 + n_q - 1) / B;
   const int64_t tiles = (b_last - b_first + 1) * ((B + TPT - 1) / TPT);
   hipLaunchKernelGGL((prefill_mfma_kernel<G, NB, NW, true>),
                      dim3((unsigned)tiles, hkv), dim3(64 * NW), 0, st, q, k, v,
                      kv_stride, q_pos0, n_q, hq, B, row_ptr, q_list, tile_ptr, nb,
-                     sel, topk, slot, sl2, part_o, part_lse, n_part, o, lse);
+                     sel, topk, slot, sl2, part_o, part_le, n_part, o, lse);
   return hipGetLastError();
 }
 
@@ -644,10 +713,10 @@ hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v,
   char *w = static_cast<char *>(ws);
   int32_t *tile_ptr = reinterpret_cast<int32_t *>(w);
   w += align256((size_t)(nb + 1) * 4);
-  float *part_o = reinterpret_cast<float *>(w);
-  w += align256((size_t)np * hq * d * 4);
-  float *part_lse = reinterpret_cast<float *>(w);
-  w += align256((size_t)np * hq * 4);
+  uint16_t *part_o = reinterpret_cast<uint16_t *>(w);
+  w += align256((size_t)np * hq * d * 2);
+  float2 *part_le = reinterpret_cast<float2 *>(w);
+  w += align256((size_t)np * hq * 8);
   int4 *info = reinterpret_cast<int4 *>(w);
   w += align256((size_t)(np / 16 + nb) * 16);   // same bound as the size query
   int32_t *tq = reinterpret_cast<int32_t *>(w);
@@ -659,7 +728,7 @@ hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v,
     return launch_mfma_g<GG, 1, 8>(qq, kk, vv, kv_stride, q_pos0, n_q, hq, hkv,  \
                                    block, sel, topk, row_ptr, q_list, slot,      \
                                    scale, o, lse, tile_ptr, info, tq, part_o,    \
-                                   part_lse, np, st);
+                                   part_le, np, st);
   switch (G) {
     MSA_MF(1)
     MSA_MF(2)

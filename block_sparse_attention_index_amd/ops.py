@@ -61,7 +61,7 @@ def load():
                                   ctypes.c_int),
         "msa_invert_workspace_bytes": ([i64, i32, i64], sz),
         "msa_invert_selection": ([P, i64, i32, i64, P, P, P, P, sz, P], ctypes.c_int),
-        "msa_prefill_workspace_bytes": ([i64, i64, i32, i32, i32, i32], sz),
+        "msa_prefill_workspace_bytes": ([i32, i64, i64, i32, i32, i32, i32], sz),
         "msa_sparse_gqa_prefill": ([P, P, P, i32, i64, i64, i64, i32, i32, i32, i32,
                                     P, i32, P, P, P, f32, P, P, P, sz, P],
                                    ctypes.c_int),
@@ -213,9 +213,9 @@ def msa_invert_selection(sel: torch.Tensor, n_blocks: int, row_ptr=None, q_list=
 # --------------------------------------------------------------------------
 # Sparse branch
 # --------------------------------------------------------------------------
-def prefill_workspace_bytes(q_pos0: int, n_q: int, hq: int, d: int, block: int,
-                            topk: int) -> int:
-    return load().msa_prefill_workspace_bytes(q_pos0, n_q, hq, d, block, topk)
+def prefill_workspace_bytes(dtype: int, q_pos0: int, n_q: int, hq: int, d: int,
+                            block: int, topk: int) -> int:
+    return load().msa_prefill_workspace_bytes(dtype, q_pos0, n_q, hq, d, block, topk)
 
 
 def msa_sparse_gqa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -238,7 +238,8 @@ def msa_sparse_gqa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     topk = sel.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load()
-    ws = _ws(lib.msa_prefill_workspace_bytes(q_pos0, n_q, hq, d, block, topk), q, ws)
+    ws = _ws(lib.msa_prefill_workspace_bytes(_dtype_code(q), q_pos0, n_q, hq, d, block,
+                                             topk), q, ws)
     if o is None:
         o = torch.empty((n_q, hq, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:

@@ -37,12 +37,12 @@ class PrefillBuffers:
     chunk: int
 
 
-def default_chunk(T: int, hq: int, d: int, block: int, topk: int,
+def default_chunk(dtype: int, T: int, hq: int, d: int, block: int, topk: int,
                   budget_bytes: int = 48 << 30) -> int:
     """Largest power-of-two query chunk (>= one block) whose prefill
     workspace fits ``budget_bytes``."""
     c = 1 << max(0, (T - 1).bit_length())
-    while c > block and ops.prefill_workspace_bytes(T - c if T > c else 0, min(c, T),
+    while c > block and ops.prefill_workspace_bytes(dtype, T - c if T > c else 0, min(c, T),
                                                      hq, d, block, topk) > budget_bytes:
         c //= 2
     return max(min(c, T), 1)
@@ -53,10 +53,12 @@ def alloc_prefill(q, idx_q, block: int, topk: int, chunk: int | None = None,
     T, hq, d = q.shape
     dev = q.device
     nb = -(-T // block)
-    chunk = chunk or default_chunk(T, hq, d, block, topk, budget_bytes)
+    code = ops._dtype_code(q)
+    chunk = chunk or default_chunk(code, T, hq, d, block, topk, budget_bytes)
     lib = ops.load()
     # the largest workspace is the last chunk's (most non-own pairs)
-    ws_attn = max(lib.msa_prefill_workspace_bytes(c0, min(chunk, T - c0), hq, d, block, topk)
+    ws_attn = max(lib.msa_prefill_workspace_bytes(code, c0, min(chunk, T - c0), hq, d, block,
+                                                  topk)
                   for c0 in range(0, T, chunk))
     ws_inv = lib.msa_invert_workspace_bytes(chunk, topk, nb)
     return PrefillBuffers(

@@ -166,11 +166,17 @@ int msa_invert_selection(const int32_t *sel, int64_t n_q, int32_t topk,
  *         ceil((q_pos0+n_q)/B)).  Results are undefined for other inputs
  *         (out-of-range entries are skipped, never dereferenced).
  *   o     [n_q][Hq][d] fp32;  lse [n_q][Hq] fp32 (may be NULL)
- *   ws    device scratch of msa_prefill_workspace_bytes() bytes
- *   Supported: fp32 and bf16; d in {64, 128, 256}; Hq/Hkv <= 16.
+ *   ws    device scratch of msa_prefill_workspace_bytes(dtype, ...) bytes; it
+ *         holds one partial record per (non-own pair, query head): fp32 for
+ *         fp32 inputs; for bf16 with d = 128 the output as fp16 scaled by a
+ *         power of two (values below 1; relative precision 2^-11 of the
+ *         record's max |o|) plus its fp32 log-sum-exp and exponent
+ *   Supported: fp32 and bf16 with d in {64, 128}, d = 256 with Hq/Hkv <= 4;
+ *   Hq/Hkv in {1, 2, 4, 8, 16}.
  * ------------------------------------------------------------------------ */
-size_t msa_prefill_workspace_bytes(int64_t q_pos0, int64_t n_q, int32_t hq,
-                                   int32_t d, int32_t block, int32_t topk);
+size_t msa_prefill_workspace_bytes(int32_t dtype, int64_t q_pos0, int64_t n_q,
+                                   int32_t hq, int32_t d, int32_t block,
+                                   int32_t topk);
 int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
                            int32_t dtype, int64_t kv_stride, int64_t q_pos0,
                            int64_t n_q, int32_t hq, int32_t hkv, int32_t d,

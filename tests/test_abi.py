@@ -95,18 +95,20 @@ def test_prefill_validation(lib):
     assert call(args(sc=float("inf"))) == EINVAL
     assert call(args(d=96)) == EUNSUP                     # no kernel for d = 96
     assert call(args(hq=24, hkv=8)) == EUNSUP             # group 3
-    need = lib.msa_prefill_workspace_bytes(0, 4096, 64, 128, 64, 16)
+    need = lib.msa_prefill_workspace_bytes(1, 0, 4096, 64, 128, 64, 16)
     assert call(args(wsb=need - 1)) == EWS
+    assert lib.msa_prefill_workspace_bytes(2, 0, 4096, 64, 128, 64, 16) == 0
 
 
 def test_prefill_workspace_holds_the_partials(lib):
-    # the KV-outer pass keeps one fp32 partial (d values + lse) per
-    # (non-own pair, query head); non-own pairs have a closed form
+    # the KV-outer pass keeps one partial record per (non-own pair, query
+    # head): fp32 (d values + lse) for fp32 inputs, fp16 values + (lse, e) for
+    # the bf16 d = 128 path; non-own pairs have a closed form
     for q0, n, B, K in [(0, 32768, 64, 16), (1000, 3000, 128, 6), (0, 1 << 20, 512, 8)]:
         p = sum((min(K, (pos // B) + 1) - 1) for pos in range(q0, q0 + n)) if n < 100000 else \
             sum((min(K, b + 1) - 1) * min(B, q0 + n - b * B) for b in range((q0 + n + B - 1) // B))
-        need = lib.msa_prefill_workspace_bytes(q0, n, 64, 128, B, K)
-        assert need >= p * 64 * 129 * 4
+        assert lib.msa_prefill_workspace_bytes(0, q0, n, 64, 128, B, K) >= p * 64 * 129 * 4
+        assert lib.msa_prefill_workspace_bytes(1, q0, n, 64, 128, B, K) >= p * 64 * (128 * 2 + 8)
 
 
 def test_decode_validation(lib):
