@@ -24,6 +24,8 @@
 // rescaling: the running reference max moves only when a row's max exceeds
 // it by more than 8 (so every weight is at most 2^8), which removes most O
 // rescales.
+#include <type_traits>
+
 #include "msa_internal.h"
 #include "prefill_common.h"
 #include "mfma_common.h"
@@ -387,8 +389,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
 // lands in its slot.  Rows are unpadded and XOR-swizzled by segment instead:
 //   K: segment s of row r at slot s ^ (r & 15)  -- the 16 rows read by a
 //      16-lane group for an A operand hit 16 distinct bank groups;
-//   V: segment s of row r at slot s ^ 2(r & 7) ^ ((r >> 3) & 1) -- the 4 rows
-//      x 2 segments of a ds_read_b64_tr_b16 group are 8 distinct slots.
+//   V: segment s of row r at slot s ^ 2(r & 7) -- the 4 rows x 2 segments of
+//      a ds_read_b64_tr_b16 group are 8 distinct slots, and the 8 rows one
+//      instruction reads (aligned to 8) spread over all 16 slots; rows 8
+//      apart share the pattern, so all of a lane's V reads sit at constant
+//      offsets from one address per column block.
 // Rows past the chunk repeat its last valid row (masked keys then meet finite
 // values: their weight is exactly 0).
 // ---------------------------------------------------------------------------
@@ -401,9 +406,7 @@ typedef __attribute__((address_space(1))) void *gptr_t;
 typedef __attribute__((address_space(3))) void *lptr_t;
 
 __device__ __forceinline__ int kswz(int r, int sgm) { return sgm ^ (r & 15); }
-__device__ __forceinline__ int vswz(int r, int sgm) {
-  return sgm ^ (2 * (r & 7)) ^ ((r >> 3) & 1);
-}
+__device__ __forceinline__ int vswz(int r, int sgm) { return sgm ^ (2 * (r & 7)); }
 
 template <int NW>
 __device__ __forceinline__ void async_chunk(AsyncSmem &sm, const uint16_t *k,
@@ -464,6 +467,13 @@ __global__ __launch_bounds__(256) void prefill_tile_info(
   }
 }
 
+// Query fragments of a wave's next tile, staged by LDS DMA: instruction cc
+// of the wave fills x[cc][16 * lane ...] with the 16 bytes that lane needs for
+// k-step cc, so each lane reads back exactly the slot it filled.
+struct QStage {
+  uint16_t x[8][64 * 8];
+};
+
 template <int G, int NW>
 __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -474,7 +484,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     int64_t n_part) {
   constexpr int TPN = 32 / G;
   constexpr int TPT = NW * TPN;
-  __shared__ AsyncSmem smb[2];
+  // Two distinct LDS buffers, each chunk step naming its own at compile
+  // time: the compiler can then tell that the DMA filling one buffer does not
+  // alias the transposed reads of the other, and adds no wait for it.
+  __shared__ AsyncSmem sm0;
+  __shared__ AsyncSmem sm1;
+  __shared__ QStage qst[NW];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, j = lane & 31;
   const int tl = wave * TPN + j / G;  // token slot of this lane's row
@@ -488,18 +503,21 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   int64_t w = W * xcd / 8 + r;
   if (w >= w_end) return;
 
-  // metadata of item w: head, tile info, this lane's query
-  int g = (int)(w / T);
-  int4 inf = info[w % T];
-  int32_t qraw = tq[(w % T) * TPT + tl];
-
-  auto load_q = [&](int gg, int32_t qr, bf16x8 (&dst)[8]) {
+  auto stage_q = [&](int gg, int32_t qr) {
     const bool a = qr >= 0 && qr < n_q;
     const uint16_t *qp = q + (((a ? (int64_t)qr : 0) * hq + (int64_t)gg * G + hl) * kD);
 #pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      __builtin_amdgcn_global_load_lds(
+          (gptr_t)(const_cast<uint16_t *>(qp + cc * 16 + 8 * h)),
+          (lptr_t)(&qst[wave].x[cc][0]), 16, 0, 0);
+  };
+  auto read_q = [&](int32_t qr, bf16x8 (&dst)[8]) {
+    const bool a = qr >= 0 && qr < n_q;
+#pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (a) x = *reinterpret_cast<const u32x4 *>(qp + cc * 16 + 8 * h);
+      u32x4 x = *reinterpret_cast<const u32x4 *>(&qst[wave].x[cc][8 * lane]);
+      if (!a) x = u32x4{0u, 0u, 0u, 0u};
       dst[cc] = as_bf16x8(x);
     }
   };
@@ -509,142 +527,195 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     return n;
   };
 
-  bf16x8 qf[8];
-  load_q(g, qraw, qf);
-  {
-    const int64_t nk = kv_keys(inf.x);
-    async_chunk<NW>(smb[0], k + ((int64_t)g * kv_stride) * kD,
-                    v + ((int64_t)g * kv_stride) * kD, (int64_t)inf.x * B,
-                    (int)(nk < kKC ? nk : kKC));
-  }
-  int buf = 0;
+  // current item: head, tile info, this lane's query, K/V span
+  int g = (int)(w / T);
+  int4 inf = info[w % T];
+  int32_t qraw = tq[(w % T) * TPT + tl];
+  int64_t nkeys = kv_keys(inf.x);
+  int64_t n_chunks = (nkeys + kKC - 1) / kKC;
+  int64_t ci = 0;
+  stage_q(g, qraw);
+  async_chunk<NW>(sm0, k + ((int64_t)g * kv_stride) * kD,
+                  v + ((int64_t)g * kv_stride) * kD, (int64_t)inf.x * B,
+                  (int)(nkeys < kKC ? nkeys : kKC));
+  // Metadata of the next item.  The one after it is fetched at the start of
+  // each item's last chunk, so the load completes under that chunk's
+  // compute and is only moved into place after the chunk's barrier.
+  int64_t wn = w + per;
+  bool has_next = wn < w_end;
+  int gn = 0;
+  int4 infn = make_int4(0, 0, 0, 0);
+  int32_t qrawn = -1;
+  auto fetch = [&](int64_t ww, int &gg, int4 &ii, int32_t &qq) {
+    if (ww < w_end) {
+      gg = (int)(ww / T);
+      ii = info[ww % T];
+      qq = tq[(ww % T) * TPT + tl];
+    }
+  };
+  fetch(wn, gn, infn, qrawn);
   async_wait_barrier();
 
-  for (;;) {
-    const int64_t wn = w + per;
-    const bool has_next = wn < w_end;
-    int gn = 0;
-    int4 infn = make_int4(0, 0, 0, 0);
-    int32_t qrawn = -1;
-    if (has_next) {
-      gn = (int)(wn / T);
-      infn = info[wn % T];
-      qrawn = tq[(wn % T) * TPT + tl];
+  // Byte offsets of this lane's V^T pieces in a chunk, per column block cb:
+  // its 16-lane group reads 4 keys x 16 columns; lane a16 supplies key
+  // (a16 / 4) and the 8-byte piece a16 % 4.  The second piece of a k-step is
+  // 8 keys further, the next k-step 16, the next sub-tile 32 (constant
+  // offsets: the swizzle repeats every 8 rows).  Keeping each read one
+  // constant away from the buffer base keeps the compiler's alias
+  // information for it.
+  int voff[4];
+  {
+    const int a16 = lane & 15;
+    const int vrow = 4 * h + (a16 >> 2);
+    const int vcol0 = 16 * (j >> 4) + 4 * (a16 & 3);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int col = cb * 32 + vcol0;
+      voff[cb] = (vrow * kD + vswz(vrow, col >> 3) * 8 + (col & 7)) * 2;
     }
-    bf16x8 qfn[8];
+  }
 
+  bf16x8 qf[8];
+  read_q(qraw, qf);
+  f32x16 acc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
+  float mref = -INFINITY, lsum = 0.f;
+
+  // One 64-key chunk of the current item on buffer P, with the next chunk
+  // (or the next item's first chunk and queries) streaming into the other.
+  // Returns false once this workgroup's range is done.
+  auto step = [&](auto tag) -> bool {
+    constexpr int P = decltype(tag)::value;
+    AsyncSmem &cur = P ? sm1 : sm0;
+    AsyncSmem &nxt = P ? sm0 : sm1;
     const int64_t b = inf.x;
-    const int64_t nkeys = kv_keys(b);
-    const int64_t n_chunks = (nkeys + kKC - 1) / kKC;
-    const uint16_t *kb = k + ((int64_t)g * kv_stride) * kD;
-    const uint16_t *vb = v + ((int64_t)g * kv_stride) * kD;
-
-    f32x16 acc[4];
+    const int64_t kc = ci * kKC;
+    const bool last = ci + 1 >= n_chunks;
+    int gnn = 0;
+    int4 infnn = make_int4(0, 0, 0, 0);
+    int32_t qrawnn = -1;
+    if (last && has_next) {
+      stage_q(gn, qrawn);
+      fetch(wn + per, gnn, infnn, qrawnn);
+    }
+    if (!last) {
+      const int64_t nxt_row = kc + kKC;
+      async_chunk<NW>(nxt, k + ((int64_t)g * kv_stride) * kD,
+                      v + ((int64_t)g * kv_stride) * kD, b * B + nxt_row,
+                      (int)(nkeys - nxt_row < kKC ? nkeys - nxt_row : kKC));
+    } else if (has_next) {
+      const int64_t nk = kv_keys(infn.x);
+      async_chunk<NW>(nxt, k + ((int64_t)gn * kv_stride) * kD,
+                      v + ((int64_t)gn * kv_stride) * kD, (int64_t)infn.x * B,
+                      (int)(nk < kKC ? nk : kKC));
+    }
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int sub = 0; sub < 2; ++sub) {
+      const int koff0 = (int)kc + sub * 32;
+      if (koff0 >= nkeys) break;
+      f32x16 sacc;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
-    float mref = -INFINITY, lsum = 0.f;
-
-    for (int64_t ci = 0; ci < n_chunks; ++ci) {
-      const int64_t kc = ci * kKC;
-      if (ci + 1 < n_chunks) {
-        const int64_t nxt = kc + kKC;
-        async_chunk<NW>(smb[buf ^ 1], kb, vb, b * B + nxt,
-                        (int)(nkeys - nxt < kKC ? nkeys - nxt : kKC));
-      } else if (has_next) {
-        const int64_t nk = kv_keys(infn.x);
-        async_chunk<NW>(smb[buf ^ 1], k + ((int64_t)gn * kv_stride) * kD,
-                        v + ((int64_t)gn * kv_stride) * kD, (int64_t)infn.x * B,
-                        (int)(nk < kKC ? nk : kKC));
-        load_q(gn, qrawn, qfn);
+      for (int rr = 0; rr < 16; ++rr) sacc[rr] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const int kr = sub * 32 + j;
+        const u32x4 kraw = *reinterpret_cast<const u32x4 *>(
+            &cur.Ks[kr * kD + kswz(kr, cc * 2 + h) * 8]);
+        sacc = mfma32(as_bf16x8(kraw), qf[cc], sacc);
       }
-      AsyncSmem &sm = smb[buf];
+      if (koff0 + 31 >= nkeys) {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int koff0 = (int)kc + sub * 32;
-        if (koff0 >= nkeys) break;
-        f32x16 sacc;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sacc[rr] = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const int kr = sub * 32 + j;
-          const u32x4 kraw = *reinterpret_cast<const u32x4 *>(
-              &sm.Ks[kr * kD + kswz(kr, cc * 2 + h) * 8]);
-          sacc = mfma32(as_bf16x8(kraw), qf[cc], sacc);
-        }
-        if (koff0 + 31 >= nkeys) {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int koff = koff0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-            if (koff >= nkeys) sacc[rr] = -INFINITY;
-          }
-        }
-        float mloc = sacc[0];
-#pragma unroll
-        for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, sacc[rr]);
-        mloc = max_with_partner(mloc);
-        const float mt = mloc * scale_log2;
-        if (__ballot(mt > mref + kLazy)) {
-          const float mnew = fmaxf(mref, mt);
-          const float alpha = fast_exp2(mref - mnew);
-          lsum *= alpha;
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
-          mref = mnew;
-        }
-        f32x8 p0, p1;
-        float ps = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          p0[rr] = fast_exp2(fmaf(sacc[rr], scale_log2, -mref));
-          p1[rr] = fast_exp2(fmaf(sacc[rr + 8], scale_log2, -mref));
-          ps += p0[rr] + p1[rr];
-        }
-        lsum += ps;
-        const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
-        const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
-        // V^T operand: this lane's 16-lane group reads 4 keys x 16 columns;
-        // lane a16 supplies row (a16 / 4) and the 8-byte piece a16 % 4
-        const int a16 = lane & 15;
-        const int vrow0 = sub * 32 + 4 * h + (a16 >> 2);
-        const int vcol0 = 16 * (j >> 4) + 4 * (a16 & 3);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            const int col = cb * 32 + vcol0;
-            const int r0 = vrow0 + 16 * ks, r1 = r0 + 8;
-            const u32x2 lo = lds_read_tr(&sm.Vs[r0 * kD + vswz(r0, col >> 3) * 8 + (col & 7)]);
-            const u32x2 hi = lds_read_tr(&sm.Vs[r1 * kD + vswz(r1, col >> 3) * 8 + (col & 7)]);
-            const u32x4 vraw = {lo[0], lo[1], hi[0], hi[1]};
-            acc[cb] = mfma32(as_bf16x8(vraw), ks == 0 ? pb0 : pb1, acc[cb]);
-          }
+        for (int rr = 0; rr < 16; ++rr) {
+          const int koff = koff0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+          if (koff >= nkeys) sacc[rr] = -INFINITY;
         }
       }
-      buf ^= 1;
-      async_wait_barrier();
+      float mloc = sacc[0];
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, sacc[rr]);
+      mloc = max_with_partner(mloc);
+      const float mt = mloc * scale_log2;
+      if (__ballot(mt > mref + kLazy)) {
+        const float mnew = fmaxf(mref, mt);
+        const float alpha = fast_exp2(mref - mnew);
+        lsum *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+        mref = mnew;
+      }
+      f32x8 p0, p1;
+      float ps = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        p0[rr] = fast_exp2(fmaf(sacc[rr], scale_log2, -mref));
+        p1[rr] = fast_exp2(fmaf(sacc[rr + 8], scale_log2, -mref));
+        ps += p0[rr] + p1[rr];
+      }
+      lsum += ps;
+      const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
+      const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+      const char *vbase = reinterpret_cast<const char *>(cur.Vs);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          constexpr int kRow = kD * 2;   // bytes per V row
+          const int o0 = voff[cb] + (sub * 32 + 16 * ks) * kRow;
+          const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0));
+          const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0 + 8 * kRow));
+          const u32x4 vraw = {lo[0], lo[1], hi[0], hi[1]};
+          acc[cb] = mfma32(as_bf16x8(vraw), ks == 0 ? pb0 : pb1, acc[cb]);
+        }
+      }
     }
-
-    // partial output of this (query, head) for block b
-    const bool act = qraw >= 0 && qraw < n_q;
-    const float ltot = sum_with_partner(lsum);
-    if (act) {
-      const int64_t e = (int64_t)inf.y + tl;
-      const int64_t n_idx = e - own_through(b, q_pos0, n_q, B);
-      if (n_idx >= 0 && n_idx < n_part)
-        put_partial(part_o, part_le, n_idx, g, hq, G, hl, h, acc, mref, ltot);
+    if (last) {
+      // partial output of this (query, head) for block b; stored before the
+      // barrier's wait, so the stores are done when the next item starts
+      const bool act = qraw >= 0 && qraw < n_q;
+      const float ltot = sum_with_partner(lsum);
+      if (act) {
+        const int64_t e = (int64_t)inf.y + tl;
+        const int64_t n_idx = e - own_through(b, q_pos0, n_q, B);
+        if (n_idx >= 0 && n_idx < n_part)
+          put_partial(part_o, part_le, n_idx, g, hq, G, hl, h, acc, mref, ltot);
+      }
     }
-    if (!has_next) break;
+    async_wait_barrier();
+    if (!last) {
+      ++ci;
+      return true;
+    }
+    if (!has_next) return false;
     w = wn;
     g = gn;
     inf = infn;
     qraw = qrawn;
+    wn = w + per;
+    has_next = wn < w_end;
+    gn = gnn;
+    infn = infnn;
+    qrawn = qrawnn;
+    nkeys = kv_keys(inf.x);
+    n_chunks = (nkeys + kKC - 1) / kKC;
+    ci = 0;
+    read_q(qraw, qf);
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) qf[cc] = qfn[cc];
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
+    mref = -INFINITY;
+    lsum = 0.f;
+    return true;
+  };
+
+  for (;;) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
   }
 }
 
