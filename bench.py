@@ -23,6 +23,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -33,6 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from block_sparse_attention_index_amd import ops, pipeline, synth  # noqa: E402
+
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "sparse_gqa_prefill_p1m_traffic.md")
+KERNEL_SOURCES = ("prefill_mfma.hip", "prefill_common.h", "mfma_common.h", "msa_api.cpp")
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector / MFMA)
@@ -56,6 +60,49 @@ def decode_bytes(L: int, cfg) -> int:
     elt = 2 if cfg.dtype == "bf16" else 4
     return (n_keys * cfg.Hkv * cfg.d * elt * 2 + nb * cfg.d_idx * 4 +
             cfg.Hq * cfg.d * elt + cfg.d_idx * 4 + cfg.Hq * (cfg.d + 1) * 4)
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources of the sparse-GQA prefill kernels: a stored
+    counter reading is only reported while these are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_attention_index_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per sparse-GQA prefill call from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None if the summary is
+    missing, for another workload, or older than the kernel sources."""
+    try:
+        text = open(PROFILE_TRAFFIC).read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): (\S+)\s*$", text, flags=re.M))
+    if fields.get("workload") != workload or fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mib: int) -> None:
+    """One plain device copy of `mib` MiB, repeated 3 times: the reference
+    run that scales FETCH_SIZE / WRITE_SIZE to bytes."""
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
 def cpu_baseline(x, cfg, budget_s: float = 15.0):
@@ -106,12 +153,18 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(sharding is described in DESIGN.md); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     cfg = synth.CONFIGS[args.config]
     n_dec = cfg.n_dec if args.decode_steps is None else args.decode_steps
@@ -242,7 +295,7 @@ def main():
         "roofline": {"kernel": "msa_sparse_gqa_prefill (KV-outer pass + own-block/merge pass)",
                      "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 5),
-                     "traffic": None,
+                     "traffic": stored_traffic(cfg.name),
                      "launch_ms": round(attn_ms, 3), "launches_per_step": n_calls},
     }
     if not args.no_cpu_baseline:
