@@ -105,6 +105,53 @@ def calibrate_copy(mib: int) -> None:
     print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
+def measure_dec16(dev, seed: int, reps: int = 100):
+    """Batched decode at the 16 x 256K-token cache workload: the index scan
+    (top-K over every cached block summary), split-KV attention and merge of
+    one decode step, captured once as a HIP graph of `reps` repetitions and
+    replayed; bytes are the algorithmic ones (attended K/V, summaries, q, o)."""
+    cfg = synth.CONFIGS["dec16"]
+    x = synth.decode_inputs(cfg, dev, seed)
+    kmax = ops.msa_index_pool(x["idx_k"], cfg.block, seq_len=x["seq_len"], nb_max=cfg.nb)
+    bufs = pipeline.alloc_decode(x["q"], kmax, cfg.block, cfg.topk)
+
+    def one():
+        ops.msa_index_topk_decode(x["idx_q"], x["seq_len"], kmax, cfg.block, cfg.topk,
+                                  sel=bufs.sel, ws=bufs.topk_ws)
+        ops.msa_sparse_gqa_decode(x["q"], x["k_cache"], x["v_cache"], x["seq_len"], bufs.sel,
+                                  cfg.block, cfg.scale, o=bufs.o, lse=bufs.lse,
+                                  ws=bufs.attn_ws)
+
+    one()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            one()
+    g.replay()                     # warm-up replay
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    times = []
+    for _ in range(3):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3 / reps)
+    us = min(times)
+    nbytes = cfg.n_seq * decode_bytes(cfg.T, cfg)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del x, kmax, bufs, g
+    torch.cuda.empty_cache()
+    return {"workload": "dec16: 16 sequences x 262144-token bf16 cache, Hq 64 / Hkv 8, d 128, "
+                        "block 512, top-K 8; one step (scan + attention) repeated "
+                        f"{reps}x in a graph, best of 3 replays",
+            "us_per_step": round(us, 3), "bytes_per_step": int(nbytes),
+            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(x, cfg, budget_s: float = 15.0):
     """Time the CPU oracle on a bounded sample of the same workload: the
     index branch and attention for a random sample of prefill queries."""
@@ -152,6 +199,8 @@ def main():
     ap.add_argument("--config", default="p1m", choices=["p1m", "p32k", "p128k"])
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dec16", action="store_true",
+                    help="skip the batched-decode (16 x 256K cache) measurement")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -204,22 +253,34 @@ def main():
             decode_loop()
         torch.cuda.synchronize()
 
-    ev = {"pre": [], "attn": [], "dec": []}
+    ev = {"pre": [], "attn": [], "dec": [], "pool": [], "topk": [], "invert": []}
+
+    def event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
 
     def step(record: bool):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        e0 = event()
         # prefill: pool, top-K, then per chunk CSR + sparse GQA (timed per call)
         q, k, v = x["q"][:T], x["k"], x["v"]
         ops.msa_index_pool(x["idx_k"][:T], B, kmax=bufs.kmax)
+        ep = event()
         ops.msa_index_topk(x["idx_q"][:T], bufs.kmax, B, K, sel=bufs.sel)
+        et = event()
+        if record:
+            ev["pool"].append((e0, ep))
+            ev["topk"].append((ep, et))
         for c0 in range(0, T, bufs.chunk):
             c1 = min(T, c0 + bufs.chunk)
             nbc = -(-c1 // B)
             n = c1 - c0
+            i0 = event()
             ops.msa_invert_selection(bufs.sel[c0:c1], nbc, row_ptr=bufs.row_ptr[:nbc + 1],
                                      q_list=bufs.q_list[:n * K], slot=bufs.slot[:n],
                                      ws=bufs.inv_ws)
+            if record:
+                ev["invert"].append((i0, event()))
             a0 = torch.cuda.Event(enable_timing=True)
             a1 = torch.cuda.Event(enable_timing=True)
             a0.record(stream)
@@ -292,12 +353,19 @@ def main():
         "prefill_tflops": round(fl * pre_pairs / (pre_ms * 1e-3) / 1e12, 3),
         "decode_us_per_step": round(dec_us, 3) if n_dec else None,
         "decode_hbm_gbs": round(dec_gbs, 1) if dec_gbs else None,
+        "index_ms": {"pool": round(ms(ev["pool"]) / args.steps, 3),
+                     "topk": round(ms(ev["topk"]) / args.steps, 3),
+                     "invert": round(ms(ev["invert"]) / args.steps, 3)},
         "roofline": {"kernel": "msa_sparse_gqa_prefill (KV-outer pass + own-block/merge pass)",
                      "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 5),
                      "traffic": stored_traffic(cfg.name),
                      "launch_ms": round(attn_ms, 3), "launches_per_step": n_calls},
     }
+    if not args.no_dec16:
+        print("[bench] batched decode (dec16)", file=sys.stderr, flush=True)
+        del bufs, dbufs, dec_graph
+        out["decode16"] = measure_dec16(dev, args.seed)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(x, cfg)

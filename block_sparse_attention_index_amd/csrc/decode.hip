@@ -3,18 +3,17 @@
 // M3 深度实战"; GQA over the chosen blocks only, sparse branch of "MiniMax M3
 // 模型算力成本大幅降低原因深度解析").
 //
-// Split-KV.  Work item = (sequence s, KV head g, selected slot kk, chunk of up
-// to 128 keys of that block), so even one sequence fills the chip.  The item
-// stages its K and V rows in LDS once with 16-byte loads and writes a
-// normalised partial output and its base-2 log-sum-exp for every query head
-// of group g; a second kernel merges the partials of each (sequence, head) by
-// log-sum-exp.  (A same-kernel merge by the last-arriving item was measured
-// slower: the cross-XCD release fence it needs costs more than a launch.)
-// bf16 with d = 128 computes each 32-key slice on the matrix cores -- S^T =
-// K Q^T with the heads padded to 32 MFMA columns, O^T = V^T P^T with V^T read
-// by ds_read_b64_tr_b16, as in the prefill kernel -- and combines its four
-// waves through LDS; other shapes use a VALU kernel.  HBM-bound: K and V are
-// read once.
+// Split-KV: the selected blocks of every (sequence, KV head) are cut into
+// units whose normalised partial outputs and base-2 log-sum-exps a second
+// kernel merges per (sequence, query head).  (A same-kernel merge by the
+// last-arriving unit was measured slower: the cross-XCD release fence it
+// needs costs more than a launch.)  bf16 with d = 128 runs a persistent
+// streaming kernel on the matrix cores (one workgroup per CU, K/V chunks
+// arriving by LDS DMA while the previous chunk computes); other shapes use a
+// VALU kernel with one work item per (sequence, KV head, selected block,
+// 128-key chunk).  HBM-bound: K and V are read once.
+#include <type_traits>
+
 #include "msa_internal.h"
 #include "mfma_common.h"
 
@@ -226,172 +225,303 @@ __global__ __launch_bounds__(256) void decode_attn(
 }
 
 // ---------------------------------------------------------------------------
-// bf16, d = 128: matrix-core partials.  Wave w owns keys w*32 .. w*32+31 of
-// the item's chunk.
+// bf16, d = 128: persistent streaming kernel on the matrix cores.
+//
+// Work unit u = ((s * Hkv + g) * topk + kk) * nseg + seg: keys
+// [b*B + seg*seg_len, +seg_len) of block b = sel[s][kk], clipped to the block
+// and to the query position; its partial is record u of the workspace.  One
+// workgroup per CU walks a contiguous range of units as one stream of 128-key
+// chunks: each chunk's K and V rows arrive by LDS DMA (16 bytes per lane,
+// XOR-swizzled 256-byte rows) into one of two buffers while the previous
+// chunk is computed, and the next unit's queries are staged with its first
+// chunk.  Wave w owns keys 32w .. 32w+31 of a chunk: S^T = K Q^T with the G
+// heads as MFMA columns, an online softmax per head, O^T += V^T P^T with V^T
+// read by ds_read_b64_tr_b16.  At a unit's last chunk the four waves'
+// (max, sum, O) are combined through LDS (reusing the chunk buffer just
+// consumed) into the unit's normalised partial and base-2 log-sum-exp.  The
+// two buffers are distinct LDS objects named statically by each chunk step,
+// so the compiler can tell the DMA into one from the reads of the other.
 // ---------------------------------------------------------------------------
-constexpr int kDecKStr = 128 + 8;    // K row stride in LDS (bf16), 272 B
-constexpr int kDecVStr = 128 + 16;   // V row stride in LDS (bf16), 288 B
+constexpr int kSK = 128;   // keys per streamed chunk (one per wave quarter)
 
-struct DecMfmaSmem {
-  union {
-    struct {
-      uint16_t Ks[kDK * kDecKStr];
-      uint16_t Vs[kDK * kDecVStr];
-    } kv;
-    struct {                          // after the MFMAs: per-wave partials
-      float O[4][16][128];
-      float M[4][16], L[4][16];
-    } w;
-  } u;
+struct StreamBuf {
+  uint16_t Ks[kSK * 128];
+  uint16_t Vs[kSK * 128];
+};
+
+typedef __attribute__((address_space(1))) void *dec_gptr_t;
+typedef __attribute__((address_space(3))) void *dec_lptr_t;
+
+// K: segment sg of row r at slot sg ^ (r & 15) (a 16-lane A-operand read hits
+// 16 bank groups); V: at slot sg ^ 2(r & 7) (a transposed-read group's 4 rows
+// x 2 segments are distinct slots, and rows 8 apart share the pattern).
+__device__ __forceinline__ int dkswz(int r, int sg) { return sg ^ (r & 15); }
+__device__ __forceinline__ int dvswz(int r, int sg) { return sg ^ (2 * (r & 7)); }
+
+struct DecUnit {
+  int s, g;
+  int64_t t0;   // first key of the unit
+  int nk;       // keys in the unit (0: empty)
 };
 
 template <int G>
-__global__ __launch_bounds__(256) void decode_attn_mfma(
+__global__ __launch_bounds__(256) void decode_stream(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, int64_t len_max,
-    const int64_t *__restrict__ seq_len, int hq, int B,
-    const int32_t *__restrict__ sel, int topk, int nsub, float scale_log2,
-    float *__restrict__ part_o, float *__restrict__ part_lse) {
+    const int64_t *__restrict__ seq_len, int hq, int hkv, int B,
+    const int32_t *__restrict__ sel, int topk, int nseg, int seg_len,
+    int64_t n_units, float scale_log2, float *__restrict__ part_o,
+    float *__restrict__ part_lse) {
   constexpr int D = 128;
-  __shared__ DecMfmaSmem sm;
-  const int s = blockIdx.z, g = blockIdx.y;
-  const int kk = blockIdx.x / nsub, sub = blockIdx.x % nsub;
-  const int hkv = gridDim.y, np = gridDim.x;
+  constexpr int QE = G * D < 512 ? 512 : G * D;   // staged query elements
+  __shared__ StreamBuf sb0;
+  __shared__ StreamBuf sb1;
+  __shared__ uint16_t qs[QE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, j = lane & 31;
 
-  int64_t len = seq_len[s];
-  if (len > len_max) len = len_max;
-  const int64_t pos = len - 1;
-  const int32_t b = sel[(int64_t)s * topk + kk];
-  const int64_t t0 = (int64_t)b * B + (int64_t)sub * kDK;
-  int64_t nkeys = (b < 0 || len < 1) ? 0 : pos - t0 + 1;
-  if (nkeys > kDK) nkeys = kDK;
-  if (nkeys > B - sub * kDK) nkeys = B - sub * kDK;
-  const int64_t pi = ((int64_t)s * hkv + g) * np + blockIdx.x;
-  if (nkeys <= 0) {
-    for (int x = tid; x < G * D; x += 256) part_o[pi * G * D + x] = 0.f;
-    if (tid < G) part_lse[pi * G + tid] = -INFINITY;
-    return;
-  }
+  const int64_t u_end = n_units * (blockIdx.x + 1) / gridDim.x;
 
-  // stage K and V rows (all loads in flight first)
-  const uint16_t *kb = kc + (((int64_t)s * hkv + g) * len_max + t0) * D;
-  const uint16_t *vb = vc + (((int64_t)s * hkv + g) * len_max + t0) * D;
-  u32x4 kr[8], vr[8];
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int x = tid + 256 * it, r = x >> 4, c = (x & 15) * 8;
-    kr[it] = u32x4{0u, 0u, 0u, 0u};
-    vr[it] = u32x4{0u, 0u, 0u, 0u};
-    if (r < nkeys) {
-      kr[it] = *reinterpret_cast<const u32x4 *>(kb + (int64_t)r * D + c);
-      vr[it] = *reinterpret_cast<const u32x4 *>(vb + (int64_t)r * D + c);
+  auto unit = [&](int64_t u) __attribute__((always_inline)) {
+    DecUnit d;
+    const int seg = (int)(u % nseg);
+    const int64_t r1 = u / nseg;
+    const int kk = (int)(r1 % topk);
+    const int64_t r2 = r1 / topk;
+    d.g = (int)(r2 % hkv);
+    d.s = (int)(r2 / hkv);
+    int64_t len = seq_len[d.s];
+    if (len > len_max) len = len_max;
+    const int32_t b = sel[(int64_t)d.s * topk + kk];
+    d.t0 = (int64_t)b * B + (int64_t)seg * seg_len;
+    int64_t n = (b < 0 || len < 1) ? 0 : len - d.t0;   // keys t0 .. len-1
+    if (n > seg_len) n = seg_len;
+    if (n > (int64_t)B - (int64_t)seg * seg_len) n = (int64_t)B - (int64_t)seg * seg_len;
+    d.nk = n > 0 ? (int)n : 0;
+    return d;
+  };
+  // first non-empty unit at or after u (empty ones get their neutral
+  // partial: o = 0, lse = -inf)
+  auto next_unit = [&](int64_t u, DecUnit &d) __attribute__((always_inline)) {
+    for (; u < u_end; ++u) {
+      d = unit(u);
+      if (d.nk > 0) break;
+      for (int x = tid; x < G * D; x += 256) part_o[u * G * D + x] = 0.f;
+      if (tid < G) part_lse[u * G + tid] = -INFINITY;
     }
-  }
-  // query fragments: MFMA column j = query head g*G + j (zero for j >= G)
-  bf16x8 qf[8];
-  {
-    const uint16_t *qp = q + ((int64_t)s * hq + (int64_t)g * G + (j < G ? j : 0)) * D;
+    return u;
+  };
+  auto dma_kv = [&](StreamBuf &buf, const DecUnit &d, int64_t row0, int nrows)
+      __attribute__((always_inline)) {
+    const uint16_t *kb = kc + (((int64_t)d.s * hkv + d.g) * len_max + row0) * D;
+    const uint16_t *vb = vc + (((int64_t)d.s * hkv + d.g) * len_max + row0) * D;
+    constexpr int IPW = (kSK * D / 8) / 256;   // instructions per wave per tensor
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (j < G) x = *reinterpret_cast<const u32x4 *>(qp + cc * 16 + 8 * h);
-      qf[cc] = as_bf16x8(x);
+    for (int i = 0; i < IPW; ++i) {
+      const int inst = wave * IPW + i;
+      const int pslot = inst * 64 + lane;          // 16-byte slot in the chunk
+      const int r = pslot >> 4, sp = pslot & 15;
+      const int64_t rr = r < nrows ? r : nrows - 1;   // rows past the end repeat the last
+      __builtin_amdgcn_global_load_lds(
+          (dec_gptr_t)(const_cast<uint16_t *>(kb + rr * D + dkswz(r, sp) * 8)),
+          (dec_lptr_t)(&buf.Ks[inst * 64 * 8]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (dec_gptr_t)(const_cast<uint16_t *>(vb + rr * D + dvswz(r, sp) * 8)),
+          (dec_lptr_t)(&buf.Vs[inst * 64 * 8]), 16, 0, 0);
     }
-  }
+  };
+  // the unit's G query rows (contiguous in q) copied as they are
+  auto dma_q = [&](const DecUnit &d) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const uint16_t *qb = q + ((int64_t)d.s * hq + (int64_t)d.g * G) * D;
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int x = tid + 256 * it, r = x >> 4, c = (x & 15) * 8;
-    *reinterpret_cast<u32x4 *>(&sm.u.kv.Ks[r * kDecKStr + c]) = kr[it];
-    *reinterpret_cast<u32x4 *>(&sm.u.kv.Vs[r * kDecVStr + c]) = vr[it];
-  }
-  __syncthreads();
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
-  float m = -INFINITY, l = 0.f;
-  const int k0 = wave * 32;
-  if (k0 < nkeys) {
-    f32x16 sacc;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sacc[rr] = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const u32x4 kraw = *reinterpret_cast<const u32x4 *>(
-          &sm.u.kv.Ks[(k0 + j) * kDecKStr + cc * 16 + 8 * h]);
-      sacc = mfma32(as_bf16x8(kraw), qf[cc], sacc);
-    }
-    float x[16];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int key = k0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-      x[rr] = key < nkeys ? sacc[rr] * scale_log2 : -INFINITY;
-    }
-    float mloc = x[0];
-#pragma unroll
-    for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, x[rr]);
-    m = max_with_partner(mloc);          // finite: key k0 is always valid
-    f32x8 p0, p1;
-    float ps = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      p0[rr] = fast_exp2(x[rr] - m);
-      p1[rr] = fast_exp2(x[rr + 8] - m);
-      ps += p0[rr] + p1[rr];
-    }
-    l = sum_with_partner(ps);
-    const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
-    const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
-    const int a16 = lane & 15;
-    const uint16_t *vbase = &sm.u.kv.Vs[(k0 + 4 * h + (a16 >> 2)) * kDecVStr +
-                                        16 * (j >> 4) + 4 * (a16 & 3)];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const uint16_t *vp = vbase + 16 * ks * kDecVStr + cb * 32;
-        const u32x2 lo = lds_read_tr(vp);
-        const u32x2 hi = lds_read_tr(vp + 8 * kDecVStr);
-        const u32x4 vraw = {lo[0], lo[1], hi[0], hi[1]};
-        acc[cb] = mfma32(as_bf16x8(vraw), ks == 0 ? pb0 : pb1, acc[cb]);
+      for (int i = 0; i < QE / 512; ++i) {
+        const int off = (i * 512 + lane * 8) % (G * D);
+        __builtin_amdgcn_global_load_lds((dec_gptr_t)(const_cast<uint16_t *>(qb + off)),
+                                         (dec_lptr_t)(&qs[i * 512]), 16, 0, 0);
       }
     }
+  };
+  auto kv_rows = [&](int n) __attribute__((always_inline)) { return n < kSK ? n : kSK; };
+
+  DecUnit cu;
+  int64_t u = next_unit(n_units * blockIdx.x / gridDim.x, cu);
+  if (u >= u_end) return;
+  DecUnit nu = cu;
+  int64_t un = next_unit(u + 1, nu);
+  dma_q(cu);
+  dma_kv(sb0, cu, cu.t0, kv_rows(cu.nk));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // V^T operand offsets (bytes), per column block: the 16-lane group reads 4
+  // keys x 16 columns of this wave's 32 keys; lane a16 supplies key a16/4 and
+  // the 8-byte piece a16%4.  (One offset per column block, every read a
+  // constant away from it, keeps the compiler's alias information.)
+  int voff[4];
+  {
+    const int a16 = lane & 15;
+    const int vrow = wave * 32 + 4 * h + (a16 >> 2);
+    const int vcol0 = 16 * (j >> 4) + 4 * (a16 & 3);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int col = cb * 32 + vcol0;
+      voff[cb] = (vrow * D + dvswz(vrow, col >> 3) * 8 + (col & 7)) * 2;
+    }
   }
-  __syncthreads();   // K/V no longer read: the area now holds wave partials
-  if (j < G) {
+
+  bf16x8 qf[8];
+  f32x16 acc[4];
+  float m = -INFINITY, l = 0.f;
+  int ci = 0;
+
+  auto chunk = [&](auto tag) __attribute__((always_inline)) {
+    constexpr int P = decltype(tag)::value;
+    StreamBuf &cur = P ? sb1 : sb0;
+    StreamBuf &nxt = P ? sb0 : sb1;
+    const int kc0 = ci * kSK;
+    const int nk_c = kv_rows(cu.nk - kc0);
+    const bool last = kc0 + kSK >= cu.nk;
+    if (!last) {
+      dma_kv(nxt, cu, cu.t0 + kc0 + kSK, kv_rows(cu.nk - kc0 - kSK));
+    } else if (un < u_end) {
+      dma_q(nu);
+      dma_kv(nxt, nu, nu.t0, kv_rows(nu.nk));
+    }
+    const int k0 = wave * 32;
+    if (k0 < nk_c) {
+      f32x16 sacc;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sacc[rr] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const int kr = k0 + j;
+        const u32x4 kraw = *reinterpret_cast<const u32x4 *>(
+            &cur.Ks[kr * D + dkswz(kr, cc * 2 + h) * 8]);
+        sacc = mfma32(as_bf16x8(kraw), qf[cc], sacc);
+      }
+      float x[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = k0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        x[rr] = key < nk_c ? sacc[rr] * scale_log2 : -INFINITY;
+      }
+      float mloc = x[0];
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, x[rr]);
+      const float mnew = fmaxf(m, max_with_partner(mloc));   // finite: key k0 is valid
+      const float alpha = fast_exp2(m - mnew);
+      f32x8 p0, p1;
+      float ps = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        p0[rr] = fast_exp2(x[rr] - mnew);
+        p1[rr] = fast_exp2(x[rr + 8] - mnew);
+        ps += p0[rr] + p1[rr];
+      }
+      l = fmaf(l, alpha, sum_with_partner(ps));
+      m = mnew;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+      const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
+      const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+      const char *vbase = reinterpret_cast<const char *>(cur.Vs);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          constexpr int kRow = D * 2;
+          const int o0 = voff[cb] + 16 * ks * kRow;
+          const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0));
+          const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0 + 8 * kRow));
+          const u32x4 vraw = {lo[0], lo[1], hi[0], hi[1]};
+          acc[cb] = mfma32(as_bf16x8(vraw), ks == 0 ? pb0 : pb1, acc[cb]);
+        }
+    }
+    if (last) {
+      // combine the four waves through LDS (the consumed buffer), then store
+      // the unit's partial before the chunk barrier's wait
+      __syncthreads();
+      float *mo = reinterpret_cast<float *>(&cur);   // [4][G][D]
+      float *mm = mo + 4 * G * D;                    // [4][G]
+      float *ml = mm + 4 * G;                        // [4][G]
+      if (j < G) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg)
+            *reinterpret_cast<float4 *>(&mo[(wave * G + j) * D + cb * 32 + 8 * rg + 4 * h]) =
+                make_float4(acc[cb][4 * rg], acc[cb][4 * rg + 1], acc[cb][4 * rg + 2],
+                            acc[cb][4 * rg + 3]);
+        if (h == 0) {
+          mm[wave * G + j] = m;
+          ml[wave * G + j] = l;
+        }
+      }
+      __syncthreads();
+      for (int x = tid; x < G * D; x += 256) {
+        const int hd = x / D, c = x % D;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mm[w * G + hd]);
+        float z = 0.f, ov = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float sc = fast_exp2(mm[w * G + hd] - mx);   // 0 for a wave without keys
+          z = fmaf(sc, ml[w * G + hd], z);
+          ov = fmaf(sc, mo[(w * G + hd) * D + c], ov);
+        }
+        part_o[(u * G + hd) * D + c] = ov / z;
+        if (c == 0) part_lse[u * G + hd] = mx + __log2f(z);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  // One unit whose first chunk sits in buffer P0; returns the buffer of the
+  // next unit's first chunk, or -1 when the range is done.
+  auto run_unit = [&](auto ptag) __attribute__((always_inline)) -> int {
+    constexpr int P0 = decltype(ptag)::value;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      u32x4 xq = *reinterpret_cast<const u32x4 *>(&qs[(j < G ? j : 0) * D + cc * 16 + 8 * h]);
+      if (j >= G) xq = u32x4{0u, 0u, 0u, 0u};
+      qf[cc] = as_bf16x8(xq);
+    }
+    // the staging area is rewritten by the next unit's DMA: finish these reads
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), others untouched
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg)
-        *reinterpret_cast<float4 *>(&sm.u.w.O[wave][j][cb * 32 + 8 * rg + 4 * h]) =
-            make_float4(acc[cb][4 * rg], acc[cb][4 * rg + 1], acc[cb][4 * rg + 2],
-                        acc[cb][4 * rg + 3]);
-    if (h == 0) {
-      sm.u.w.M[wave][j] = m;
-      sm.u.w.L[wave][j] = l;
+      for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
+    m = -INFINITY;
+    l = 0.f;
+    ci = 0;
+    int endp;
+    for (;;) {
+      chunk(std::integral_constant<int, P0>{});
+      if ((ci + 1) * kSK >= cu.nk) { endp = P0; break; }
+      ++ci;
+      chunk(std::integral_constant<int, 1 - P0>{});
+      if ((ci + 1) * kSK >= cu.nk) { endp = 1 - P0; break; }
+      ++ci;
     }
-  }
-  __syncthreads();
-  for (int x = tid; x < G * D; x += 256) {
-    const int hd = x / D, c = x % D;
-    float mm = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      if (w * 32 < nkeys) mm = fmaxf(mm, sm.u.w.M[w][hd]);
-    float z = 0.f, ov = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (w * 32 >= nkeys) continue;
-      const float sc = fast_exp2(sm.u.w.M[w][hd] - mm);
-      z = fmaf(sc, sm.u.w.L[w][hd], z);
-      ov = fmaf(sc, sm.u.w.O[w][hd][c], ov);
-    }
-    part_o[(pi * G + hd) * D + c] = ov / z;
-    if (c == 0) part_lse[pi * G + hd] = mm + __log2f(z);
+    if (un >= u_end) return -1;
+    u = un;
+    cu = nu;
+    un = next_unit(u + 1, nu);
+    return 1 - endp;
+  };
+
+  int par = 0;
+  for (;;) {
+    const int nx = par ? run_unit(std::integral_constant<int, 1>{})
+                       : run_unit(std::integral_constant<int, 0>{});
+    if (nx < 0) break;
+    par = nx;
   }
 }
 
@@ -423,6 +553,19 @@ __global__ __launch_bounds__(D) void decode_merge(
   if (lse && c == 0) lse[(int64_t)s * hq + hh] = (m + __log2f(z)) * kLn2;
 }
 
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 template <typename T, int G, int D>
 hipError_t launch_dec(const T *q, const T *kc, const T *vc, int32_t n_seq,
                       int64_t len_max, const int64_t *seq_len, int32_t hq,
@@ -430,18 +573,30 @@ hipError_t launch_dec(const T *q, const T *kc, const T *vc, int32_t n_seq,
                       float scale, float *o, float *lse, float *part_o,
                       float *part_lse, hipStream_t st) {
   const int nsub = (B + kDK - 1) / kDK;
-  const dim3 grid(topk * nsub, hkv, n_seq);
+  int np = topk * nsub;
   if constexpr (sizeof(T) == 2 && D == 128) {
-    hipLaunchKernelGGL((decode_attn_mfma<G>), grid, dim3(256), 0, st, q, kc, vc,
-                       len_max, seq_len, hq, B, sel, topk, nsub, scale * kLog2e,
-                       part_o, part_lse);
+    // split blocks into segments only as far as needed to give every CU a
+    // unit (at most one segment per 128-key chunk: np stays within the
+    // workspace's topk * nsub records)
+    const int cus = num_cus();
+    int nseg = 1;
+    while (nseg < nsub && (int64_t)n_seq * hkv * topk * nseg < cus) nseg *= 2;
+    if (nseg > nsub) nseg = nsub;
+    const int seg_len = ((nsub + nseg - 1) / nseg) * kSK;
+    const int64_t n_units = (int64_t)n_seq * hkv * topk * nseg;
+    const int grid = (int)(n_units < cus ? n_units : cus);
+    hipLaunchKernelGGL((decode_stream<G>), dim3(grid), dim3(256), 0, st, q, kc, vc,
+                       len_max, seq_len, hq, hkv, B, sel, topk, nseg, seg_len, n_units,
+                       scale * kLog2e, part_o, part_lse);
+    np = topk * nseg;
   } else {
+    const dim3 grid(topk * nsub, hkv, n_seq);
     hipLaunchKernelGGL((decode_attn<T, G, D>), grid, dim3(256), 0, st, q, kc, vc,
                        len_max, seq_len, hq, B, sel, topk, nsub, scale * kLog2e,
                        part_o, part_lse);
   }
   hipLaunchKernelGGL((decode_merge<D>), dim3(hq, n_seq), dim3(D), 0, st,
-                     topk * nsub, G, hkv, part_o, part_lse, o, lse);
+                     np, G, hkv, part_o, part_lse, o, lse);
   return hipGetLastError();
 }
 
