@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 from block_sparse_attention_index_amd import ops, pipeline, synth  # noqa: E402
 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "sparse_gqa_prefill_p1m_traffic.md")
-KERNEL_SOURCES = ("prefill_mfma.hip", "prefill_common.h", "mfma_common.h", "msa_api.cpp")
+KERNEL_SOURCES = ("prefill_mfma.hip", "prefill_common.h", "mfma_common.h")
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector / MFMA)
@@ -106,21 +106,26 @@ def calibrate_copy(mib: int) -> None:
 
 
 def measure_dec16(dev, seed: int, reps: int = 100):
-    """Batched decode at the 16 x 256K-token cache workload: the index scan
-    (top-K over every cached block summary), split-KV attention and merge of
-    one decode step, captured once as a HIP graph of `reps` repetitions and
-    replayed; bytes are the algorithmic ones (attended K/V, summaries, q, o)."""
+    """Batched decode at the 16 x 256K-token cache workload: one fused decode
+    step per sequence (append of the 262144th token, its block's running max,
+    the index scan over every cached block summary, top-K, split-KV attention
+    and merge), captured once as a HIP graph of `reps` repetitions and
+    replayed (each repetition appends the same token again: idempotent);
+    bytes are the algorithmic ones (attended K/V, summaries, q, o)."""
     cfg = synth.CONFIGS["dec16"]
     x = synth.decode_inputs(cfg, dev, seed)
     kmax = ops.msa_index_pool(x["idx_k"], cfg.block, seq_len=x["seq_len"], nb_max=cfg.nb)
-    bufs = pipeline.alloc_decode(x["q"], kmax, cfg.block, cfg.topk)
+    bufs = pipeline.alloc_decode_step(x["q"], kmax, cfg.block, cfg.topk)
+    L = cfg.T - 1                                    # tokens before the new one
+    before = x["seq_len"] - 1
+    k_new = x["k_cache"][:, :, L].contiguous()
+    v_new = x["v_cache"][:, :, L].contiguous()
+    ik_new = x["idx_k"][:, L].contiguous()
 
     def one():
-        ops.msa_index_topk_decode(x["idx_q"], x["seq_len"], kmax, cfg.block, cfg.topk,
-                                  sel=bufs.sel, ws=bufs.topk_ws)
-        ops.msa_sparse_gqa_decode(x["q"], x["k_cache"], x["v_cache"], x["seq_len"], bufs.sel,
-                                  cfg.block, cfg.scale, o=bufs.o, lse=bufs.lse,
-                                  ws=bufs.attn_ws)
+        pipeline.decode_append_step(x["q"], k_new, v_new, x["idx_q"], ik_new, x["k_cache"],
+                                    x["v_cache"], kmax, before, cfg.block, cfg.topk, cfg.scale,
+                                    idx_k_cache=x["idx_k"], bufs=bufs)
 
     one()
     torch.cuda.synchronize()
@@ -146,7 +151,7 @@ def measure_dec16(dev, seed: int, reps: int = 100):
     del x, kmax, bufs, g
     torch.cuda.empty_cache()
     return {"workload": "dec16: 16 sequences x 262144-token bf16 cache, Hq 64 / Hkv 8, d 128, "
-                        "block 512, top-K 8; one step (scan + attention) repeated "
+                        "block 512, top-K 8; one fused decode step repeated "
                         f"{reps}x in a graph, best of 3 replays",
             "us_per_step": round(us, 3), "bytes_per_step": int(nbytes),
             "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
@@ -232,15 +237,24 @@ def main():
     bufs.kmax = kmax_dec[0, :-(-T // B)]
     k_cache, v_cache = x["k"][None], x["v"][None]
     idx_k_cache = x["idx_k"][None]
-    seq_lens = torch.arange(T + 1, T + n_dec + 1, dtype=torch.int64, device=dev)
-    dbufs = pipeline.alloc_decode(x["q"][:1], kmax_dec, B, K) if n_dec else None
+    # decode: one fused step per new token (append at position T + s, running
+    # block max, scan, top-K, attention, merge); the new tokens' rows are
+    # gathered contiguous once, outside the timed region
+    seq_lens = torch.arange(T, T + n_dec, dtype=torch.int64, device=dev)  # before each step
+    dbufs = None
+    if n_dec:
+        k_new = x["k"][:, T:T + n_dec].permute(1, 0, 2).contiguous()      # [n_dec, Hkv, d]
+        v_new = x["v"][:, T:T + n_dec].permute(1, 0, 2).contiguous()
+        ik_new = x["idx_k"][T:T + n_dec].contiguous()
+        dbufs = pipeline.alloc_decode_step(x["q"][:1], kmax_dec, B, K)
     stream = torch.cuda.current_stream(dev)
 
     def decode_loop():
         for s in range(n_dec):
-            pipeline.decode_step(x["q"][T + s:T + s + 1], x["idx_q"][T + s:T + s + 1],
-                                 k_cache, v_cache, idx_k_cache, kmax_dec,
-                                 seq_lens[s:s + 1], B, K, cfg.scale, bufs=dbufs)
+            pipeline.decode_append_step(
+                x["q"][T + s:T + s + 1], k_new[s:s + 1], v_new[s:s + 1],
+                x["idx_q"][T + s:T + s + 1], ik_new[s:s + 1], k_cache, v_cache, kmax_dec,
+                seq_lens[s:s + 1], B, K, cfg.scale, idx_k_cache=idx_k_cache, bufs=dbufs)
 
     # The decode steps are launch-bound at batch 1: capture them once in a HIP
     # graph (no allocation or memset inside) and replay it.

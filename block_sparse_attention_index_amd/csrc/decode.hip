@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include "msa_internal.h"
+#include "index_common.h"
 #include "mfma_common.h"
 
 namespace msa {
@@ -264,23 +265,64 @@ struct DecUnit {
   int nk;       // keys in the unit (0: empty)
 };
 
-template <int G>
+// FUSED: the step of msa_decode_step -- the query sits at position
+// seq_len[s] (its key was just appended), and the selection is merged here
+// from the scan's per-chunk candidate lists (cand_s, cand_b): every workgroup
+// merges the rows of the (at most kStepSeqs) sequences its units belong to,
+// and the workgroup holding a sequence's first unit also writes the row to
+// `sel`.  Otherwise the query sits at seq_len[s] - 1 and `sel` is read.
+constexpr int kStepSeqs = 8;
+
+template <int G, bool FUSED>
 __global__ __launch_bounds__(256) void decode_stream(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, int64_t len_max,
     const int64_t *__restrict__ seq_len, int hq, int hkv, int B,
-    const int32_t *__restrict__ sel, int topk, int nseg, int seg_len,
+    int32_t *__restrict__ sel, int topk, int nseg, int seg_len,
     int64_t n_units, float scale_log2, float *__restrict__ part_o,
-    float *__restrict__ part_lse) {
+    float *__restrict__ part_lse, const float *__restrict__ cand_s,
+    const int *__restrict__ cand_b, int n_chunks, int64_t nb_max) {
   constexpr int D = 128;
   constexpr int QE = G * D < 512 ? 512 : G * D;   // staged query elements
   __shared__ StreamBuf sb0;
   __shared__ StreamBuf sb1;
   __shared__ uint16_t qs[QE];
+  __shared__ int32_t selrows[FUSED ? kStepSeqs * 64 : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, j = lane & 31;
 
+  const int64_t u_begin = n_units * blockIdx.x / gridDim.x;
   const int64_t u_end = n_units * (blockIdx.x + 1) / gridDim.x;
+  const int64_t ups = (int64_t)hkv * topk * nseg;   // units per sequence
+  const int64_t s_first = u_begin / ups;
+  // the query's length (keys 0 .. len-1 are visible)
+  auto query_len = [&](int s) __attribute__((always_inline)) {
+    int64_t len = seq_len[s] + (FUSED ? 1 : 0);
+    return len > len_max ? len_max : len;
+  };
+  if constexpr (FUSED) {
+    if (u_begin < u_end) {
+      const int64_t s_last = (u_end - 1) / ups;
+      for (int64_t s = s_first + wave; s <= s_last && s - s_first < kStepSeqs; s += 4) {
+        const int64_t len = query_len((int)s);
+        int64_t own = len >= 1 ? (len - 1) / B : 0;
+        if (own >= nb_max) own = nb_max - 1;
+        int32_t *row = &selrows[(s - s_first) * 64];
+        // scratch: a quarter of the (still unused) chunk buffers per wave
+        float *st_s = reinterpret_cast<float *>(wave < 2 ? &sb0 : &sb1) +
+                      (wave & 1) * (int)(sizeof(StreamBuf) / 8);
+        int *st_b = reinterpret_cast<int *>(st_s) + (int)(sizeof(StreamBuf) / 16);
+        decode_merge_lists(cand_s + s * n_chunks * (topk - 1), cand_b + s * n_chunks * (topk - 1),
+                           n_chunks, topk, (int)own, row, st_s, st_b,
+                           (int)(sizeof(StreamBuf) / 16));
+        if (s * ups >= u_begin) {   // this workgroup holds the sequence's first unit
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // the row's LDS writes have landed
+          if (lane < topk) sel[s * topk + lane] = row[lane];
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   auto unit = [&](int64_t u) __attribute__((always_inline)) {
     DecUnit d;
@@ -290,9 +332,12 @@ __global__ __launch_bounds__(256) void decode_stream(
     const int64_t r2 = r1 / topk;
     d.g = (int)(r2 % hkv);
     d.s = (int)(r2 / hkv);
-    int64_t len = seq_len[d.s];
-    if (len > len_max) len = len_max;
-    const int32_t b = sel[(int64_t)d.s * topk + kk];
+    const int64_t len = query_len(d.s);
+    int32_t b;
+    if constexpr (FUSED)
+      b = (d.s - s_first < kStepSeqs) ? selrows[(d.s - s_first) * 64 + kk] : -1;
+    else
+      b = sel[(int64_t)d.s * topk + kk];
     d.t0 = (int64_t)b * B + (int64_t)seg * seg_len;
     int64_t n = (b < 0 || len < 1) ? 0 : len - d.t0;   // keys t0 .. len-1
     if (n > seg_len) n = seg_len;
@@ -345,7 +390,7 @@ __global__ __launch_bounds__(256) void decode_stream(
   auto kv_rows = [&](int n) __attribute__((always_inline)) { return n < kSK ? n : kSK; };
 
   DecUnit cu;
-  int64_t u = next_unit(n_units * blockIdx.x / gridDim.x, cu);
+  int64_t u = next_unit(u_begin, cu);
   if (u >= u_end) return;
   DecUnit nu = cu;
   int64_t un = next_unit(u + 1, nu);
@@ -553,6 +598,50 @@ __global__ __launch_bounds__(D) void decode_merge(
   if (lse && c == 0) lse[(int64_t)s * hq + hh] = (m + __log2f(z)) * kLn2;
 }
 
+// ---------------------------------------------------------------------------
+// Fused decode step, stage 1: workgroup = (chunk of kDecChunk blocks,
+// sequence).  Chunk 0 appends the new token (K and V rows of every KV head,
+// the index key) at position L = seq_len[s] and folds the index key into its
+// block's running max (a fresh summary when the token opens the block);
+// every chunk scores its blocks before own = L / B for the query at L and
+// keeps its best K-1.  The scan never uses the own block's summary, so it does
+// not wait for the fold.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void dstep_scan(
+    const T *__restrict__ k_new, const T *__restrict__ v_new,
+    const float *__restrict__ idx_k_new, T *__restrict__ k_cache,
+    T *__restrict__ v_cache, float *__restrict__ idx_k_cache,
+    float *__restrict__ kmax, const float *__restrict__ idx_q,
+    const int64_t *__restrict__ seq_len, int64_t len_max, int64_t nb_max,
+    int hkv, int d, int d_idx, int B, int topk, float *__restrict__ cand_s,
+    int *__restrict__ cand_b, int n_chunks) {
+  const int s = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+  const int64_t L = seq_len[s];
+  const bool room = L >= 0 && L < len_max && L / B < nb_max;   // else: nothing is written
+  const int64_t own = room ? L / B : nb_max - 1;
+  if (ch == 0 && room) {
+    for (int x = tid; x < hkv * d; x += 256) {
+      const int g = x / d, c = x % d;
+      const int64_t dst = (((int64_t)s * hkv + g) * len_max + L) * d + c;
+      k_cache[dst] = k_new[((int64_t)s * hkv + g) * d + c];
+      v_cache[dst] = v_new[((int64_t)s * hkv + g) * d + c];
+    }
+    float *km = kmax + ((int64_t)s * nb_max + own) * d_idx;
+    const bool fresh = (L % B) == 0;
+    for (int c = tid; c < d_idx; c += 256) {
+      const float xv = idx_k_new[(int64_t)s * d_idx + c];
+      if (idx_k_cache) idx_k_cache[((int64_t)s * len_max + L) * d_idx + c] = xv;
+      km[c] = fresh ? xv : key2f(max(f2key(xv), f2key(km[c])));
+    }
+  }
+  if (topk > 1)
+    decode_scan_chunk(idx_q + (int64_t)s * d_idx, kmax + (int64_t)s * nb_max * d_idx, own,
+                      nb_max, d_idx, topk, ch,
+                      cand_s + ((int64_t)s * n_chunks + ch) * (topk - 1),
+                      cand_b + ((int64_t)s * n_chunks + ch) * (topk - 1));
+}
+
 int num_cus() {
   static int cache[64] = {0};
   int dev = 0;
@@ -566,6 +655,31 @@ int num_cus() {
   return cache[dev];
 }
 
+// Units of the streaming kernel: blocks are split into segments only as far
+// as needed to give every CU a unit (at most one segment per 128-key chunk,
+// so the partial count stays within the workspace's topk * ceil(B/128)
+// records per (sequence, query head)); at least ceil(n_seq / 6) workgroups,
+// so a workgroup's units span at most kStepSeqs sequences.
+struct StreamPlan {
+  int nseg, seg_len, grid;
+  int64_t n_units;
+};
+StreamPlan stream_plan(int32_t n_seq, int32_t hkv, int32_t B, int32_t topk) {
+  StreamPlan p;
+  const int nsub = (B + kSK - 1) / kSK;
+  const int cus = num_cus();
+  p.nseg = 1;
+  while (p.nseg < nsub && (int64_t)n_seq * hkv * topk * p.nseg < cus) p.nseg *= 2;
+  if (p.nseg > nsub) p.nseg = nsub;
+  p.seg_len = ((nsub + p.nseg - 1) / p.nseg) * kSK;
+  p.n_units = (int64_t)n_seq * hkv * topk * p.nseg;
+  int64_t grid = cus;
+  if (grid < (n_seq + 5) / 6) grid = (n_seq + 5) / 6;
+  if (grid > p.n_units) grid = p.n_units;
+  p.grid = (int)grid;
+  return p;
+}
+
 template <typename T, int G, int D>
 hipError_t launch_dec(const T *q, const T *kc, const T *vc, int32_t n_seq,
                       int64_t len_max, const int64_t *seq_len, int32_t hq,
@@ -575,20 +689,12 @@ hipError_t launch_dec(const T *q, const T *kc, const T *vc, int32_t n_seq,
   const int nsub = (B + kDK - 1) / kDK;
   int np = topk * nsub;
   if constexpr (sizeof(T) == 2 && D == 128) {
-    // split blocks into segments only as far as needed to give every CU a
-    // unit (at most one segment per 128-key chunk: np stays within the
-    // workspace's topk * nsub records)
-    const int cus = num_cus();
-    int nseg = 1;
-    while (nseg < nsub && (int64_t)n_seq * hkv * topk * nseg < cus) nseg *= 2;
-    if (nseg > nsub) nseg = nsub;
-    const int seg_len = ((nsub + nseg - 1) / nseg) * kSK;
-    const int64_t n_units = (int64_t)n_seq * hkv * topk * nseg;
-    const int grid = (int)(n_units < cus ? n_units : cus);
-    hipLaunchKernelGGL((decode_stream<G>), dim3(grid), dim3(256), 0, st, q, kc, vc,
-                       len_max, seq_len, hq, hkv, B, sel, topk, nseg, seg_len, n_units,
-                       scale * kLog2e, part_o, part_lse);
-    np = topk * nseg;
+    const StreamPlan pl = stream_plan(n_seq, hkv, B, topk);
+    hipLaunchKernelGGL((decode_stream<G, false>), dim3(pl.grid), dim3(256), 0, st, q, kc, vc,
+                       len_max, seq_len, hq, hkv, B, const_cast<int32_t *>(sel), topk, pl.nseg,
+                       pl.seg_len, pl.n_units, scale * kLog2e, part_o, part_lse, nullptr,
+                       nullptr, 0, (int64_t)0);
+    np = topk * pl.nseg;
   } else {
     const dim3 grid(topk * nsub, hkv, n_seq);
     hipLaunchKernelGGL((decode_attn<T, G, D>), grid, dim3(256), 0, st, q, kc, vc,
@@ -686,6 +792,74 @@ hipError_t launch_decode(const void *q, const void *k_cache,
   }
 #undef MSA_DARGS
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode step (append, running block max, index scan, top-K, sparse
+// GQA, merge) for bf16 with d = 128.
+// Layout: [candidate scores][candidate ids][partial o][partial lse].
+// ---------------------------------------------------------------------------
+size_t decode_step_ws_bytes(int32_t n_seq, int64_t nb_max, int32_t hq, int32_t d,
+                            int32_t block, int32_t topk) {
+  const int64_t n_chunks = (nb_max + kDecChunk - 1) / kDecChunk;
+  const size_t nc = (size_t)n_seq * n_chunks * (topk > 1 ? topk - 1 : 1);
+  return align256(nc * 4) + align256(nc * 4) + decode_ws_bytes(n_seq, hq, d, block, topk);
+}
+
+bool decode_step_supported(int32_t dtype, int32_t d, int32_t group) {
+  return dtype == 1 && d == 128 &&
+         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+}
+
+hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_new,
+                              const float *idx_q, const float *idx_k_new, void *k_cache,
+                              void *v_cache, float *idx_k_cache, float *kmax,
+                              int32_t n_seq, int64_t len_max, int64_t nb_max,
+                              const int64_t *seq_len, int32_t hq, int32_t hkv, int32_t d,
+                              int32_t d_idx, int32_t block, int32_t topk, float scale,
+                              int32_t *sel, float *o, float *lse, void *ws,
+                              hipStream_t st) {
+  const int G = hq / hkv;
+  const int n_chunks = (int)((nb_max + kDecChunk - 1) / kDecChunk);
+  const size_t nc = (size_t)n_seq * n_chunks * (topk > 1 ? topk - 1 : 1);
+  char *w = static_cast<char *>(ws);
+  float *cand_s = reinterpret_cast<float *>(w);
+  w += align256(nc * 4);
+  int *cand_b = reinterpret_cast<int *>(w);
+  w += align256(nc * 4);
+  const int64_t np_max = dec_partials(n_seq, hq, block, topk);
+  float *part_o = reinterpret_cast<float *>(w);
+  w += align256((size_t)np_max * d * 4);
+  float *part_lse = reinterpret_cast<float *>(w);
+
+  const uint16_t *qq = static_cast<const uint16_t *>(q);
+  uint16_t *kc = static_cast<uint16_t *>(k_cache);
+  uint16_t *vc = static_cast<uint16_t *>(v_cache);
+  hipLaunchKernelGGL((dstep_scan<uint16_t>), dim3(n_chunks, n_seq), dim3(256), 0, st,
+                     static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
+                     idx_k_new, kc, vc, idx_k_cache, kmax, idx_q, seq_len, len_max, nb_max,
+                     hkv, d, d_idx, block, topk, cand_s, cand_b, n_chunks);
+  const StreamPlan pl = stream_plan(n_seq, hkv, block, topk);
+#define MSA_STEP_CASE(GG)                                                               \
+  case GG:                                                                              \
+    hipLaunchKernelGGL((decode_stream<GG, true>), dim3(pl.grid), dim3(256), 0, st, qq, kc, \
+                       vc, len_max, seq_len, hq, hkv, block, sel, topk, pl.nseg,         \
+                       pl.seg_len, pl.n_units, scale * kLog2e, part_o, part_lse, cand_s,  \
+                       cand_b, n_chunks, nb_max);                                        \
+    break;
+  switch (G) {
+    MSA_STEP_CASE(1)
+    MSA_STEP_CASE(2)
+    MSA_STEP_CASE(4)
+    MSA_STEP_CASE(8)
+    MSA_STEP_CASE(16)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MSA_STEP_CASE
+  hipLaunchKernelGGL((decode_merge<128>), dim3(hq, n_seq), dim3(128), 0, st,
+                     topk * pl.nseg, G, hkv, part_o, part_lse, o, lse);
+  return hipGetLastError();
 }
 
 }  // namespace msa

@@ -226,4 +226,34 @@ int msa_sparse_gqa_decode(const void *q, const void *k_cache,
                                       as_stream(stream)));
 }
 
+size_t msa_decode_step_workspace_bytes(int32_t n_seq, int64_t nb_max, int32_t hq,
+                                       int32_t d, int32_t block, int32_t topk) {
+  if (n_seq < 1 || nb_max < 1 || hq < 1 || d < 1 || !block_ok(block) || !topk_ok(topk))
+    return 0;
+  return msa::decode_step_ws_bytes(n_seq, nb_max, hq, d, block, topk);
+}
+
+int msa_decode_step(const void *q, const void *k_new, const void *v_new,
+                    const float *idx_q, const float *idx_k_new, void *k_cache,
+                    void *v_cache, float *idx_k_cache, float *kmax, int32_t dtype,
+                    int32_t n_seq, int64_t len_max, int64_t nb_max,
+                    const int64_t *seq_len, int32_t hq, int32_t hkv, int32_t d,
+                    int32_t d_idx, int32_t block, int32_t topk, float scale,
+                    int32_t *sel, float *o, float *lse, void *ws, size_t ws_bytes,
+                    void *stream) {
+  if (!q || !k_new || !v_new || !idx_q || !idx_k_new || !k_cache || !v_cache || !kmax ||
+      !seq_len || !sel || !o || !ws || (dtype != MSA_F32 && dtype != MSA_BF16) ||
+      n_seq < 1 || n_seq > kMaxGridY || len_max < 1 || nb_max < 1 ||
+      nb_max > INT32_MAX || hq < 1 || hkv < 1 || hq % hkv != 0 || d < 1 ||
+      !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk) || !std::isfinite(scale))
+    return MSA_ERR_INVALID_ARG;
+  if (!msa::decode_step_supported(dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
+  if (ws_bytes < msa::decode_step_ws_bytes(n_seq, nb_max, hq, d, block, topk))
+    return MSA_ERR_WORKSPACE;
+  return status_of(msa::launch_decode_step(q, k_new, v_new, idx_q, idx_k_new, k_cache,
+                                           v_cache, idx_k_cache, kmax, n_seq, len_max,
+                                           nb_max, seq_len, hq, hkv, d, d_idx, block, topk,
+                                           scale, sel, o, lse, ws, as_stream(stream)));
+}
+
 }  // extern "C"

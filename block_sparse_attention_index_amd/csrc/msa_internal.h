@@ -61,6 +61,18 @@ hipError_t launch_decode(const void *q, const void *k_cache,
                          const int32_t *sel, int32_t topk, float scale,
                          float *o, float *lse, void *ws, hipStream_t st);
 
+size_t decode_step_ws_bytes(int32_t n_seq, int64_t nb_max, int32_t hq, int32_t d,
+                            int32_t block, int32_t topk);
+bool decode_step_supported(int32_t dtype, int32_t d, int32_t group);
+hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_new,
+                              const float *idx_q, const float *idx_k_new, void *k_cache,
+                              void *v_cache, float *idx_k_cache, float *kmax,
+                              int32_t n_seq, int64_t len_max, int64_t nb_max,
+                              const int64_t *seq_len, int32_t hq, int32_t hkv, int32_t d,
+                              int32_t d_idx, int32_t block, int32_t topk, float scale,
+                              int32_t *sel, float *o, float *lse, void *ws,
+                              hipStream_t st);
+
 // Round a byte count up to the 256-byte alignment used for workspace
 // sub-buffers.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -7,17 +7,10 @@
 // an order-preserving integer image of the float bits, which makes it exact,
 // order-free and puts -0 below +0.  HBM-bound: each index key is read once.
 #include "msa_internal.h"
+#include "index_common.h"
 
 namespace msa {
 namespace {
-
-__device__ __forceinline__ int f2key(float x) {
-  int i = __float_as_int(x);
-  return i ^ ((i >> 31) & 0x7fffffff);
-}
-__device__ __forceinline__ float key2f(int k) {
-  return __int_as_float(k ^ ((k >> 31) & 0x7fffffff));
-}
 
 // d_idx % 4 == 0 and d_idx <= 1024.
 __global__ __launch_bounds__(256) void pool_vec4(

@@ -14,6 +14,7 @@
 // the lanes that beat the threshold, and each is inserted with one more
 // ballot (its rank) and one lane shift.
 #include "msa_internal.h"
+#include "index_common.h"
 
 namespace msa {
 namespace {
@@ -23,56 +24,6 @@ constexpr int kCB = 64;     // blocks per chunk
 constexpr int kDC = 64;     // index columns per staged slice
 constexpr int kPad = kDC + 1;
 constexpr int kMaxList = 64;
-
-__device__ __forceinline__ float shfl_f(float x, int src) {
-  return __shfl(x, src, 64);
-}
-__device__ __forceinline__ int shfl_i(int x, int src) {
-  return __shfl(x, src, 64);
-}
-
-// Insert the lanes of `mask` (candidates s at block base+lane) into the
-// list (ls, lb) of length *cnt <= km held in lanes [0, km).
-__device__ __forceinline__ void list_insert(float s, int base, uint64_t mask,
-                                            int km, int &cnt, float &ls,
-                                            int &lb) {
-  const int lane = threadIdx.x & 63;
-  while (mask) {
-    const int src = __ffsll((unsigned long long)mask) - 1;
-    const float sj = shfl_f(s, src);
-    const int bj = base + src;
-    const int pos = __popcll(__ballot(lane < cnt && ls >= sj));
-    const float ps = shfl_f(ls, lane > 0 ? lane - 1 : 0);
-    const int pb = shfl_i(lb, lane > 0 ? lane - 1 : 0);
-    const int last = cnt < km - 1 ? cnt : km - 1;
-    if (lane > pos && lane <= last) {
-      ls = ps;
-      lb = pb;
-    }
-    if (lane == pos) {
-      ls = sj;
-      lb = bj;
-    }
-    cnt = cnt + 1 < km ? cnt + 1 : km;
-    const float thr = shfl_f(ls, km - 1);
-    mask &= ~(1ull << src);
-    mask &= __ballot(cnt < km || s > thr);
-  }
-}
-
-// Write sel row: the cnt list blocks ascending, then own, then -1.
-__device__ __forceinline__ void write_row(int32_t *row, int topk, int cnt,
-                                          int lb, int own) {
-  const int lane = threadIdx.x & 63;
-  int rank = 0;
-  for (int j = 0; j < cnt; ++j) {
-    const int bj = shfl_i(lb, j);
-    rank += (bj < lb) ? 1 : 0;
-  }
-  if (lane < cnt) row[rank] = lb;
-  if (lane == cnt) row[cnt] = own;
-  if (lane > cnt && lane < topk) row[lane] = -1;
-}
 
 // ---------------------------------------------------------------------------
 // Prefill: workgroup = 64 consecutive queries; loop over chunks of 64 blocks
@@ -183,140 +134,31 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
 // Stage 2 (one wave per sequence) merges the chunk lists in chunk order, 64
 // candidates per ballot, and writes the selection.
 // ---------------------------------------------------------------------------
-constexpr int kDecChunk = 64;
-
-// As list_insert, with explicit per-lane block ids.
-__device__ __forceinline__ void list_insert_ids(float s, int bid, uint64_t mask,
-                                                int km, int &cnt, float &ls,
-                                                int &lb) {
-  const int lane = threadIdx.x & 63;
-  while (mask) {
-    const int src = __ffsll((unsigned long long)mask) - 1;
-    const float sj = shfl_f(s, src);
-    const int bj = shfl_i(bid, src);
-    const int pos = __popcll(__ballot(lane < cnt && ls >= sj));
-    const float ps = shfl_f(ls, lane > 0 ? lane - 1 : 0);
-    const int pb = shfl_i(lb, lane > 0 ? lane - 1 : 0);
-    const int last = cnt < km - 1 ? cnt : km - 1;
-    if (lane > pos && lane <= last) {
-      ls = ps;
-      lb = pb;
-    }
-    if (lane == pos) {
-      ls = sj;
-      lb = bj;
-    }
-    cnt = cnt + 1 < km ? cnt + 1 : km;
-    const float thr = shfl_f(ls, km - 1);
-    mask &= ~(1ull << src);
-    mask &= __ballot(cnt < km || s > thr);
-  }
-}
-
 __global__ __launch_bounds__(256) void topk_decode_kernel(
     const float *__restrict__ idx_q, const int64_t *__restrict__ seq_len,
     const float *__restrict__ kmax, int64_t nb_max, int d_idx, int B, int topk,
     float *__restrict__ ws_s, int *__restrict__ ws_b, int n_chunks) {
-  __shared__ float scs[kDecChunk];
-  const int s = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int km = topk - 1;
+  const int s = blockIdx.y;
   const int64_t len = seq_len[s];
-  const int64_t own = len >= 1 ? (len - 1) / B : 0;
-  const float *qv = idx_q + (int64_t)s * d_idx;
-
-  // scores of blocks ch*64 + wave*16 + 2*it + (lane >> 5)
-  const int half = lane >> 5, l32 = lane & 31;
-  const int64_t bw = (int64_t)ch * kDecChunk + wave * 16 + half;
-  if ((d_idx & 3) == 0 && d_idx <= 128) {
-    // one float4 of the row per lane: all eight row loads in flight at once
-    const bool has = 4 * l32 < d_idx;
-    const float4 qa = has ? *reinterpret_cast<const float4 *>(qv + 4 * l32)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 x[8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {       // issued before own is known
-      const int64_t b = bw + 2 * it;
-      x[it] = (has && b < nb_max)
-                  ? *reinterpret_cast<const float4 *>(
-                        kmax + ((int64_t)s * nb_max + b) * d_idx + 4 * l32)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      float acc = qa.x * x[it].x;
-      acc = fmaf(qa.y, x[it].y, acc);
-      acc = fmaf(qa.z, x[it].z, acc);
-      acc = fmaf(qa.w, x[it].w, acc);
-#pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      const int64_t b = bw + 2 * it;
-      if (l32 == 0) scs[wave * 16 + 2 * it + half] = (b < own && b < nb_max) ? acc : -INFINITY;
-    }
-  } else {
-    for (int it = 0; it < 8; ++it) {
-      const int64_t b = bw + 2 * it;
-      float acc = 0.f;
-      const bool valid = b < own && b < nb_max;
-      if (valid) {
-        const float *row = kmax + ((int64_t)s * nb_max + b) * d_idx;
-        for (int c = l32; c < d_idx; c += 32) acc = fmaf(row[c], qv[c], acc);
-      }
-#pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      if (l32 == 0) scs[wave * 16 + 2 * it + half] = valid ? acc : -INFINITY;
-    }
-  }
-  __syncthreads();
-  if (wave == 0 && km > 0) {
-    const int64_t bb = (int64_t)ch * kDecChunk + lane;
-    const float x = scs[lane];
-    const bool valid = bb < own && bb < nb_max;
-    int cnt = 0;
-    float ls = -INFINITY;
-    int lb = -1;
-    const uint64_t mask = __ballot(valid);
-    list_insert(x, ch * kDecChunk, mask, km, cnt, ls, lb);
-    const int64_t o = ((int64_t)s * n_chunks + ch) * km;
-    if (lane < km) {
-      ws_s[o + lane] = lane < cnt ? ls : -INFINITY;
-      ws_b[o + lane] = lane < cnt ? lb : -1;
-    }
-  }
+  const int64_t own = len >= 1 ? (len - 1) / B : 0;   // the query sits at len - 1
+  decode_scan_chunk(idx_q + (int64_t)s * d_idx, kmax + (int64_t)s * nb_max * d_idx, own,
+                    nb_max, d_idx, topk, blockIdx.x,
+                    ws_s + ((int64_t)s * n_chunks + blockIdx.x) * (topk - 1),
+                    ws_b + ((int64_t)s * n_chunks + blockIdx.x) * (topk - 1));
 }
 
 __global__ __launch_bounds__(64) void topk_decode_merge(
     const int64_t *__restrict__ seq_len, int B, int topk,
     const float *__restrict__ ws_s, const int *__restrict__ ws_b, int n_chunks,
     int32_t *__restrict__ sel) {
-  const int s = blockIdx.x, lane = threadIdx.x;
-  const int km = topk - 1;
+  __shared__ float st_s[2048];
+  __shared__ int st_b[2048];
+  const int s = blockIdx.x;
   const int64_t len = seq_len[s];
   const int64_t own = len >= 1 ? (len - 1) / B : 0;
-  int cnt = 0;
-  float ls = -INFINITY;
-  int lb = INT32_MAX;
-  const int64_t nc = (int64_t)n_chunks * km;
-  const int64_t o0 = (int64_t)s * n_chunks * km;
-  constexpr int kPre = 8;   // candidate groups of 64 fetched in one round trip
-  for (int64_t base0 = 0; km > 0 && base0 < nc; base0 += 64 * kPre) {
-    float xs[kPre];
-    int xbs[kPre];
-#pragma unroll
-    for (int gi = 0; gi < kPre; ++gi) {
-      const int64_t i = base0 + 64 * gi + lane;
-      xs[gi] = i < nc ? ws_s[o0 + i] : -INFINITY;
-      xbs[gi] = i < nc ? ws_b[o0 + i] : -1;
-    }
-#pragma unroll
-    for (int gi = 0; gi < kPre; ++gi) {
-      const float thr = shfl_f(ls, km - 1);
-      const uint64_t mask = __ballot(xbs[gi] >= 0 && (cnt < km || xs[gi] > thr));
-      if (mask) list_insert_ids(xs[gi], xbs[gi], mask, km, cnt, ls, lb);
-    }
-  }
-  if (lane >= cnt) lb = INT32_MAX;
-  write_row(sel + (int64_t)s * topk, topk, cnt, lb, (int)own);
+  decode_merge_lists(ws_s + (int64_t)s * n_chunks * (topk - 1),
+                     ws_b + (int64_t)s * n_chunks * (topk - 1), n_chunks, topk, (int)own,
+                     sel + (int64_t)s * topk, st_s, st_b, 2048);
 }
 
 }  // namespace

@@ -29,6 +29,7 @@ ENTRY_POINTS = (
     "msa_invert_workspace_bytes", "msa_invert_selection",
     "msa_prefill_workspace_bytes", "msa_sparse_gqa_prefill",
     "msa_decode_workspace_bytes", "msa_sparse_gqa_decode",
+    "msa_decode_step_workspace_bytes", "msa_decode_step",
 )
 
 
@@ -68,6 +69,9 @@ def load():
         "msa_decode_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
         "msa_sparse_gqa_decode": ([P, P, P, i32, i32, i64, P, i32, i32, i32, i32, P,
                                    i32, f32, P, P, P, sz, P], ctypes.c_int),
+        "msa_decode_step_workspace_bytes": ([i32, i64, i32, i32, i32, i32], sz),
+        "msa_decode_step": ([P, P, P, P, P, P, P, P, P, i32, i32, i64, i64, P, i32, i32,
+                             i32, i32, i32, i32, f32, P, P, P, P, sz, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -285,3 +289,45 @@ def msa_sparse_gqa_decode(q: torch.Tensor, k_cache: torch.Tensor,
         _ptr(ws), ws.numel(), _stream(q))
     _check("msa_sparse_gqa_decode", st)
     return o, lse
+
+
+def msa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    idx_q: torch.Tensor, idx_k_new: torch.Tensor, k_cache: torch.Tensor,
+                    v_cache: torch.Tensor, kmax: torch.Tensor, seq_len: torch.Tensor,
+                    block: int, topk: int, scale: float | None = None,
+                    idx_k_cache: torch.Tensor | None = None, sel=None, o=None, lse=None,
+                    ws=None, want_lse: bool = True):
+    """Fused decode step: append the new token at ``seq_len[s]`` (K/V, index
+    key), update its block's running max, select and attend.  ``q`` [n_seq,
+    Hq, d]; ``k_new``/``v_new`` [n_seq, Hkv, d]; ``idx_q``/``idx_k_new``
+    [n_seq, d_idx]; caches [n_seq, Hkv, len_max, d]; ``kmax`` [n_seq, nb_max,
+    d_idx].  ``seq_len`` is not advanced.  Returns ``(o, lse, sel)``."""
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache")):
+        _dev(t, nm)
+    if not (q.dtype == k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, the new rows and the caches must share a dtype")
+    for t, nm in ((idx_q, "idx_q"), (idx_k_new, "idx_k_new"), (kmax, "kmax")):
+        _dev(t, nm, torch.float32)
+    if idx_k_cache is not None:
+        _dev(idx_k_cache, "idx_k_cache", torch.float32)
+    _dev(seq_len, "seq_len", torch.int64)
+    n_seq, hq, d = q.shape
+    _, hkv, len_max, _ = k_cache.shape
+    nb_max, d_idx = kmax.shape[1], kmax.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load()
+    ws = _ws(lib.msa_decode_step_workspace_bytes(n_seq, nb_max, hq, d, block, topk), q, ws)
+    if sel is None:
+        sel = torch.empty((n_seq, topk), dtype=torch.int32, device=q.device)
+    if o is None:
+        o = torch.empty((n_seq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((n_seq, hq), dtype=torch.float32, device=q.device)
+    st = lib.msa_decode_step(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(idx_q), _ptr(idx_k_new), _ptr(k_cache),
+        _ptr(v_cache), _ptr(idx_k_cache), _ptr(kmax), _dtype_code(q), n_seq, len_max, nb_max,
+        _ptr(seq_len), hq, hkv, d, d_idx, block, topk, scale, _ptr(sel), _ptr(o), _ptr(lse),
+        _ptr(ws), ws.numel(), _stream(q))
+    _check("msa_decode_step", st)
+    return o, lse, sel

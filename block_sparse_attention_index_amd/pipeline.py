@@ -145,3 +145,37 @@ def decode_step(q, idx_q, k_cache, v_cache, idx_k, kmax, seq_len, block: int,
     ops.msa_sparse_gqa_decode(q, k_cache, v_cache, seq_len, bufs.sel, block, scale,
                               o=bufs.o, lse=bufs.lse, ws=bufs.attn_ws)
     return bufs.o, bufs.lse, bufs.sel
+
+
+@dataclasses.dataclass
+class DecodeStepBuffers:
+    sel: torch.Tensor
+    o: torch.Tensor
+    lse: torch.Tensor
+    ws: torch.Tensor
+
+
+def alloc_decode_step(q, kmax, block: int, topk: int) -> DecodeStepBuffers:
+    n_seq, hq, d = q.shape
+    dev = q.device
+    lib = ops.load()
+    return DecodeStepBuffers(
+        sel=torch.empty((n_seq, topk), dtype=torch.int32, device=dev),
+        o=torch.empty((n_seq, hq, d), dtype=torch.float32, device=dev),
+        lse=torch.empty((n_seq, hq), dtype=torch.float32, device=dev),
+        ws=torch.empty(max(1, lib.msa_decode_step_workspace_bytes(
+            n_seq, kmax.shape[1], hq, d, block, topk)), dtype=torch.uint8, device=dev))
+
+
+def decode_append_step(q, k_new, v_new, idx_q, idx_k_new, k_cache, v_cache, kmax, seq_len,
+                       block: int, topk: int, scale: float | None = None, idx_k_cache=None,
+                       bufs: DecodeStepBuffers | None = None):
+    """One generation step with the fused entry point: the new token (K/V rows
+    ``k_new``/``v_new`` [n_seq, Hkv, d], index key ``idx_k_new``) is appended
+    at position ``seq_len[s]`` (not advanced here), its block's running max
+    updated, and its query (``q``, ``idx_q``) selects and attends.  Returns
+    ``(o, lse, sel)``; no allocation when ``bufs`` is given."""
+    bufs = bufs or alloc_decode_step(q, kmax, block, topk)
+    return ops.msa_decode_step(q, k_new, v_new, idx_q, idx_k_new, k_cache, v_cache, kmax,
+                               seq_len, block, topk, scale, idx_k_cache=idx_k_cache,
+                               sel=bufs.sel, o=bufs.o, lse=bufs.lse, ws=bufs.ws)

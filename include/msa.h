@@ -211,6 +211,45 @@ int msa_sparse_gqa_decode(const void *q, const void *k_cache,
                           float *o, float *lse, void *ws, size_t ws_bytes,
                           void *stream);
 
+/* ------------------------------------------------------------------------
+ * msa_decode_step -- one generation step of the whole path, fused
+ * [CXT 3.3: the new token is appended, its block summary updated, the query
+ * scored against the summaries, the top-K blocks attended]:
+ *   1. append the new token at position L = seq_len[s] of every sequence:
+ *      k_cache[s][g][L] = k_new[s][g], v_cache likewise, and
+ *      idx_k_cache[s][L] = idx_k_new[s] when idx_k_cache is not NULL;
+ *   2. running block max: kmax[s][L/B] = idx_k_new[s] when L % B == 0 (the
+ *      token opens a block), else the elementwise max of the two (exact, with
+ *      -0 below +0, as msa_index_pool);
+ *   3. the query at position L scores every earlier block summary and keeps
+ *      the causal top-K with its own block L/B forced (msa_index_topk_decode's
+ *      rule); the row is written to sel;
+ *   4. sparse GQA over the selected blocks, keys 0..L (msa_sparse_gqa_decode).
+ * seq_len is read, not advanced: the caller adds one per step.  All of it is
+ * enqueued on `stream` as three kernels, with no allocation and no host
+ * synchronisation, so a step can be captured in a HIP graph.
+ *   q          [n_seq][Hq][d] bf16, the new token's queries
+ *   k_new/v_new [n_seq][Hkv][d] bf16;  idx_q, idx_k_new [n_seq][d_idx] fp32
+ *   k_cache/v_cache [n_seq][Hkv][len_max][d] bf16 (written at L)
+ *   idx_k_cache [n_seq][len_max][d_idx] fp32 or NULL;  kmax [n_seq][nb_max][d_idx]
+ *   Requires L < len_max and L / B < nb_max for every sequence; a sequence
+ *   without room gets no append and unspecified outputs (nothing outside the
+ *   given buffers is written).
+ *   sel [n_seq][K] int32 out;  o [n_seq][Hq][d] fp32;  lse [n_seq][Hq] (may be NULL)
+ *   ws  device scratch of msa_decode_step_workspace_bytes() bytes
+ *   Supported: bf16, d = 128, Hq/Hkv in {1, 2, 4, 8, 16}.
+ * ------------------------------------------------------------------------ */
+size_t msa_decode_step_workspace_bytes(int32_t n_seq, int64_t nb_max, int32_t hq,
+                                       int32_t d, int32_t block, int32_t topk);
+int msa_decode_step(const void *q, const void *k_new, const void *v_new,
+                    const float *idx_q, const float *idx_k_new, void *k_cache,
+                    void *v_cache, float *idx_k_cache, float *kmax, int32_t dtype,
+                    int32_t n_seq, int64_t len_max, int64_t nb_max,
+                    const int64_t *seq_len, int32_t hq, int32_t hkv, int32_t d,
+                    int32_t d_idx, int32_t block, int32_t topk, float scale,
+                    int32_t *sel, float *o, float *lse, void *ws, size_t ws_bytes,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -366,3 +366,75 @@ def test_decode_steps_in_a_captured_graph(orc):
         for s_ in range(n_steps):
             assert torch.equal(outs[s_].cpu(), eager[s_]), f"replay {rep} step {s_}"
 
+
+
+# --------------------------------------------------------------------------
+# fused decode step (append + running block max + scan + top-K + attention)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("hq,hkv,B,K,lens", [
+    (64, 8, 64, 6, [0, 63, 64, 200, 1000]),      # empty cache, block-opening tokens
+    (16, 1, 128, 4, [1, 127, 300]),              # G = 16
+    (8, 8, 512, 8, [511, 512, 3000]),            # G = 1, the 1M-token block size
+])
+def test_decode_step_fused(orc, hq, hkv, B, K, lens):
+    n, d, di, steps = len(lens), 128, 128, 3
+    T = max(lens) + steps
+    cfg = synth.Config("dec-step", T, "bf16", hq, hkv, d, di, B, K, 4, n_seq=n, mode="decode")
+    _say(f"fused decode step G={hq // hkv} B={B} K={K} lens={lens}")
+    x = synth.decode_inputs(cfg, "cpu", 0)
+    nb_max = -(-T // B)
+    kc = x["k_cache"].to(DEV)
+    vc = x["v_cache"].to(DEV)
+    ik = x["idx_k"].to(DEV)
+    # device caches hold only the first lens[s] tokens; later rows are garbage
+    kc_d, vc_d = kc.clone(), vc.clone()
+    ik_d = ik.clone()
+    for s, L in enumerate(lens):
+        kc_d[s, :, L:] = 0.5
+        vc_d[s, :, L:] = -0.5
+        ik_d[s, L:] = 7.0
+    kmax = torch.full((n, nb_max, di), float("nan"), device=DEV)
+    seq = torch.tensor(lens, dtype=torch.int64, device=DEV)
+    for s, L in enumerate(lens):
+        if L:
+            ops.msa_index_pool(ik_d[s:s + 1, :L], B, kmax=kmax[s:s + 1],
+                               seq_len=seq[s:s + 1], nb_max=nb_max)
+    # queries of the new tokens: seed 1, so they differ from the cache's draws
+    q_all = synth._normal_rows((steps, n, hq, d), torch.bfloat16, "cpu", 1, "q")
+    iq_all = synth._normal_rows((steps, n, di), torch.float32, "cpu", 1, "idx_q")
+    ws = torch.empty(ops.load().msa_decode_step_workspace_bytes(n, nb_max, hq, d, B, K),
+                     dtype=torch.uint8, device=DEV)
+    kc_h, vc_h, ik_h = synth.host(kc), synth.host(vc), _np(ik)
+    for t in range(steps):
+        pos = np.array(lens, np.int64) + t
+        k_new = torch.stack([kc[s, :, pos[s]] for s in range(n)]).contiguous()
+        v_new = torch.stack([vc[s, :, pos[s]] for s in range(n)]).contiguous()
+        ik_new = torch.stack([ik[s, pos[s]] for s in range(n)]).contiguous()
+        q = q_all[t].to(DEV)
+        iq = iq_all[t].to(DEV)
+        o, lse, sel = ops.msa_decode_step(q, k_new, v_new, iq, ik_new, kc_d, vc_d, kmax, seq,
+                                          B, K, idx_k_cache=ik_d, ws=ws)
+        o, lse, sel = _np(o), _np(lse), _np(sel)
+        for s in range(n):
+            L = int(pos[s])
+            # the append, bit for bit
+            assert torch.equal(kc_d[s, :, L], kc[s, :, L]) and torch.equal(vc_d[s, :, L], vc[s, :, L])
+            assert torch.equal(ik_d[s, L], ik[s, L])
+            # the running summaries equal a fresh pool of the first L+1 index keys
+            kmo = orc.pool(ik_h[s, :L + 1], B)
+            nbl = -(-(L + 1) // B)
+            assert np.array_equal(_np(kmax[s, :nbl]), kmo)
+            so, gr, ga, eb = orc.select(_np(iq)[s:s + 1], np.array([L]), kmo, B, K)
+            check_selection(sel[s:s + 1], so, gr, ga, eb, _np(iq)[s:s + 1], kmo, np.array([L]), B)
+            oo, lo, _ = orc.attend(synth.host(q[s:s + 1]), kc_h[s], vc_h[s], np.array([0]),
+                                   np.array([L]), sel[s:s + 1], B, cfg.scale, orc.BF16)
+            eo, el = max_abs(o[s], oo[0]), max_abs(lse[s], lo[0])
+            assert eo <= TOL_BF16 and el <= TOL_BF16, (t, s, eo, el)
+        # the composed path on the same (now appended) cache gives the same result
+        seq1 = seq + 1
+        sel_c = ops.msa_index_topk_decode(iq, seq1, kmax, B, K)
+        o_c, lse_c = ops.msa_sparse_gqa_decode(q, kc_d, vc_d, seq1, sel_c, B)
+        assert np.array_equal(_np(sel_c), sel)
+        assert np.array_equal(_np(o_c), o) and np.array_equal(_np(lse_c), lse)
+        seq += 1
+    _say(f"  {steps} steps x {n} sequences checked")
