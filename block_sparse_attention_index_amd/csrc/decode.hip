@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void decode_stream(
     const uint16_t *__restrict__ vc, int64_t len_max,
     const int64_t *__restrict__ seq_len, int hq, int hkv, int B,
     int32_t *__restrict__ sel, int topk, int nseg, int seg_len,
-    int64_t n_units, float scale_log2, float *__restrict__ part_o,
+    uint32_t u_q, uint32_t u_r, float scale_log2, float *__restrict__ part_o,
     float *__restrict__ part_lse, const float *__restrict__ cand_s,
     const int *__restrict__ cand_b, int n_chunks, int64_t nb_max) {
   constexpr int D = 128;
@@ -291,51 +291,58 @@ __global__ __launch_bounds__(256) void decode_stream(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, j = lane & 31;
 
-  const int64_t u_begin = n_units * blockIdx.x / gridDim.x;
-  const int64_t u_end = n_units * (blockIdx.x + 1) / gridDim.x;
-  const int64_t ups = (int64_t)hkv * topk * nseg;   // units per sequence
-  const int64_t s_first = u_begin / ups;
+  // units [u_begin, u_end): u_q each, one more for the first u_r workgroups
+  // (32-bit unit arithmetic: the host keeps the unit count below 2^31)
+  const uint32_t bx = blockIdx.x;
+  const uint32_t u_begin = bx * u_q + (bx < u_r ? bx : u_r);
+  const uint32_t u_end = u_begin + u_q + (bx < u_r ? 1u : 0u);
+  const uint32_t ups = (uint32_t)(hkv * topk * nseg);   // units per sequence
+  const uint32_t s_first = u_begin / ups;
   // the query's length (keys 0 .. len-1 are visible)
-  auto query_len = [&](int s) __attribute__((always_inline)) {
+  auto query_len = [&](uint32_t s) __attribute__((always_inline)) {
     int64_t len = seq_len[s] + (FUSED ? 1 : 0);
     return len > len_max ? len_max : len;
   };
   if constexpr (FUSED) {
     if (u_begin < u_end) {
-      const int64_t s_last = (u_end - 1) / ups;
-      for (int64_t s = s_first + wave; s <= s_last && s - s_first < kStepSeqs; s += 4) {
-        const int64_t len = query_len((int)s);
-        int64_t own = len >= 1 ? (len - 1) / B : 0;
-        if (own >= nb_max) own = nb_max - 1;
+      const uint32_t s_last = (u_end - 1) / ups;
+      for (uint32_t s = s_first + wave; s <= s_last && s - s_first < kStepSeqs; s += 4) {
+        const int64_t len = query_len(s);   // in flight with the lists' loads
         int32_t *row = &selrows[(s - s_first) * 64];
         // scratch: a quarter of the (still unused) chunk buffers per wave
         float *st_s = reinterpret_cast<float *>(wave < 2 ? &sb0 : &sb1) +
                       (wave & 1) * (int)(sizeof(StreamBuf) / 8);
         int *st_b = reinterpret_cast<int *>(st_s) + (int)(sizeof(StreamBuf) / 16);
-        decode_merge_lists(cand_s + s * n_chunks * (topk - 1), cand_b + s * n_chunks * (topk - 1),
-                           n_chunks, topk, (int)own, row, st_s, st_b,
-                           (int)(sizeof(StreamBuf) / 16));
+        const size_t c0 = (size_t)s * n_chunks * (topk - 1);
+        decode_merge_lists(
+            cand_s + c0, cand_b + c0, n_chunks, topk,
+            [&] {
+              int64_t own = len >= 1 ? (len - 1) / B : 0;
+              return (int)(own >= nb_max ? nb_max - 1 : own);
+            },
+            row, st_s, st_b, (int)(sizeof(StreamBuf) / 16));
         if (s * ups >= u_begin) {   // this workgroup holds the sequence's first unit
           __builtin_amdgcn_s_waitcnt(0xC07F);   // the row's LDS writes have landed
-          if (lane < topk) sel[s * topk + lane] = row[lane];
+          if (lane < topk) sel[(size_t)s * topk + lane] = row[lane];
         }
       }
     }
     __syncthreads();
   }
 
-  auto unit = [&](int64_t u) __attribute__((always_inline)) {
+  auto unit = [&](uint32_t u) __attribute__((always_inline)) {
     DecUnit d;
-    const int seg = (int)(u % nseg);
-    const int64_t r1 = u / nseg;
-    const int kk = (int)(r1 % topk);
-    const int64_t r2 = r1 / topk;
-    d.g = (int)(r2 % hkv);
-    d.s = (int)(r2 / hkv);
+    const uint32_t r1 = u / (uint32_t)nseg;
+    const int seg = (int)(u - r1 * (uint32_t)nseg);
+    const uint32_t r2 = r1 / (uint32_t)topk;
+    const int kk = (int)(r1 - r2 * (uint32_t)topk);
+    const uint32_t r3 = r2 / (uint32_t)hkv;
+    d.g = (int)(r2 - r3 * (uint32_t)hkv);
+    d.s = (int)r3;
     const int64_t len = query_len(d.s);
     int32_t b;
     if constexpr (FUSED)
-      b = (d.s - s_first < kStepSeqs) ? selrows[(d.s - s_first) * 64 + kk] : -1;
+      b = ((uint32_t)d.s - s_first < kStepSeqs) ? selrows[((uint32_t)d.s - s_first) * 64 + kk] : -1;
     else
       b = sel[(int64_t)d.s * topk + kk];
     d.t0 = (int64_t)b * B + (int64_t)seg * seg_len;
@@ -347,12 +354,12 @@ __global__ __launch_bounds__(256) void decode_stream(
   };
   // first non-empty unit at or after u (empty ones get their neutral
   // partial: o = 0, lse = -inf)
-  auto next_unit = [&](int64_t u, DecUnit &d) __attribute__((always_inline)) {
+  auto next_unit = [&](uint32_t u, DecUnit &d) __attribute__((always_inline)) {
     for (; u < u_end; ++u) {
       d = unit(u);
       if (d.nk > 0) break;
-      for (int x = tid; x < G * D; x += 256) part_o[u * G * D + x] = 0.f;
-      if (tid < G) part_lse[u * G + tid] = -INFINITY;
+      for (int x = tid; x < G * D; x += 256) part_o[(size_t)u * G * D + x] = 0.f;
+      if (tid < G) part_lse[(size_t)u * G + tid] = -INFINITY;
     }
     return u;
   };
@@ -390,10 +397,10 @@ __global__ __launch_bounds__(256) void decode_stream(
   auto kv_rows = [&](int n) __attribute__((always_inline)) { return n < kSK ? n : kSK; };
 
   DecUnit cu;
-  int64_t u = next_unit(u_begin, cu);
+  uint32_t u = next_unit(u_begin, cu);
   if (u >= u_end) return;
   DecUnit nu = cu;
-  int64_t un = next_unit(u + 1, nu);
+  uint32_t un = next_unit(u + 1, nu);
   dma_q(cu);
   dma_kv(sb0, cu, cu.t0, kv_rows(cu.nk));
   __builtin_amdgcn_s_waitcnt(0);
@@ -518,8 +525,8 @@ __global__ __launch_bounds__(256) void decode_stream(
           z = fmaf(sc, ml[w * G + hd], z);
           ov = fmaf(sc, mo[(w * G + hd) * D + c], ov);
         }
-        part_o[(u * G + hd) * D + c] = ov / z;
-        if (c == 0) part_lse[u * G + hd] = mx + __log2f(z);
+        part_o[((size_t)u * G + hd) * D + c] = ov / z;
+        if (c == 0) part_lse[(size_t)u * G + hd] = mx + __log2f(z);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -584,7 +591,7 @@ __global__ __launch_bounds__(D) void decode_merge(
   const int hq = gridDim.x, g = hh / G, hl = hh % G;
   const int64_t base = ((int64_t)s * hkv + g) * np;
   float m = -3.0e38f, z = 0.f, acc = 0.f;
-#pragma unroll 8
+#pragma unroll 16
   for (int i = 0; i < np; ++i) {
     const float li = part_lse[(base + i) * G + hl];
     const float oi = part_o[((base + i) * G + hl) * D + c];
@@ -600,12 +607,12 @@ __global__ __launch_bounds__(D) void decode_merge(
 
 // ---------------------------------------------------------------------------
 // Fused decode step, stage 1: workgroup = (chunk of kDecChunk blocks,
-// sequence).  Chunk 0 appends the new token (K and V rows of every KV head,
-// the index key) at position L = seq_len[s] and folds the index key into its
-// block's running max (a fresh summary when the token opens the block);
-// every chunk scores its blocks before own = L / B for the query at L and
-// keeps its best K-1.  The scan never uses the own block's summary, so it does
-// not wait for the fold.
+// sequence), plus one more workgroup per sequence (x = n_chunks) that appends
+// the new token (K and V rows of every KV head, the index key) at position
+// L = seq_len[s] and folds the index key into its block's running max (a
+// fresh summary when the token opens the block).  Every chunk scores its
+// blocks before own = L / B for the query at L and keeps its best K-1.  The
+// scan never reads the own block's summary, so the append runs beside it.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void dstep_scan(
@@ -620,20 +627,29 @@ __global__ __launch_bounds__(256) void dstep_scan(
   const int64_t L = seq_len[s];
   const bool room = L >= 0 && L < len_max && L / B < nb_max;   // else: nothing is written
   const int64_t own = room ? L / B : nb_max - 1;
-  if (ch == 0 && room) {
-    for (int x = tid; x < hkv * d; x += 256) {
-      const int g = x / d, c = x % d;
+  if (ch == n_chunks) {
+    if (!room) return;
+    // 16-byte pieces of the K and V rows (d * sizeof(T) is a multiple of 16)
+    constexpr int kV = 16 / (int)sizeof(T);
+    const int vpr = d / kV;
+    for (int x = tid; x < hkv * vpr; x += 256) {
+      const int g = x / vpr, c = (x % vpr) * kV;
+      const int64_t src = ((int64_t)s * hkv + g) * d + c;
       const int64_t dst = (((int64_t)s * hkv + g) * len_max + L) * d + c;
-      k_cache[dst] = k_new[((int64_t)s * hkv + g) * d + c];
-      v_cache[dst] = v_new[((int64_t)s * hkv + g) * d + c];
+      const uint4 kx = *reinterpret_cast<const uint4 *>(k_new + src);
+      const uint4 vx = *reinterpret_cast<const uint4 *>(v_new + src);
+      *reinterpret_cast<uint4 *>(k_cache + dst) = kx;
+      *reinterpret_cast<uint4 *>(v_cache + dst) = vx;
     }
     float *km = kmax + ((int64_t)s * nb_max + own) * d_idx;
     const bool fresh = (L % B) == 0;
     for (int c = tid; c < d_idx; c += 256) {
       const float xv = idx_k_new[(int64_t)s * d_idx + c];
+      const float old = km[c];
       if (idx_k_cache) idx_k_cache[((int64_t)s * len_max + L) * d_idx + c] = xv;
-      km[c] = fresh ? xv : key2f(max(f2key(xv), f2key(km[c])));
+      km[c] = fresh ? xv : key2f(max(f2key(xv), f2key(old)));
     }
+    return;
   }
   if (topk > 1)
     decode_scan_chunk(idx_q + (int64_t)s * d_idx, kmax + (int64_t)s * nb_max * d_idx, own,
@@ -663,6 +679,7 @@ int num_cus() {
 struct StreamPlan {
   int nseg, seg_len, grid;
   int64_t n_units;
+  uint32_t u_q, u_r;   // units per workgroup, and the workgroups with one more
 };
 StreamPlan stream_plan(int32_t n_seq, int32_t hkv, int32_t B, int32_t topk) {
   StreamPlan p;
@@ -677,6 +694,8 @@ StreamPlan stream_plan(int32_t n_seq, int32_t hkv, int32_t B, int32_t topk) {
   if (grid < (n_seq + 5) / 6) grid = (n_seq + 5) / 6;
   if (grid > p.n_units) grid = p.n_units;
   p.grid = (int)grid;
+  p.u_q = (uint32_t)(p.n_units / grid);
+  p.u_r = (uint32_t)(p.n_units % grid);
   return p;
 }
 
@@ -692,7 +711,7 @@ hipError_t launch_dec(const T *q, const T *kc, const T *vc, int32_t n_seq,
     const StreamPlan pl = stream_plan(n_seq, hkv, B, topk);
     hipLaunchKernelGGL((decode_stream<G, false>), dim3(pl.grid), dim3(256), 0, st, q, kc, vc,
                        len_max, seq_len, hq, hkv, B, const_cast<int32_t *>(sel), topk, pl.nseg,
-                       pl.seg_len, pl.n_units, scale * kLog2e, part_o, part_lse, nullptr,
+                       pl.seg_len, pl.u_q, pl.u_r, scale * kLog2e, part_o, part_lse, nullptr,
                        nullptr, 0, (int64_t)0);
     np = topk * pl.nseg;
   } else {
@@ -835,7 +854,7 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
   const uint16_t *qq = static_cast<const uint16_t *>(q);
   uint16_t *kc = static_cast<uint16_t *>(k_cache);
   uint16_t *vc = static_cast<uint16_t *>(v_cache);
-  hipLaunchKernelGGL((dstep_scan<uint16_t>), dim3(n_chunks, n_seq), dim3(256), 0, st,
+  hipLaunchKernelGGL((dstep_scan<uint16_t>), dim3(n_chunks + 1, n_seq), dim3(256), 0, st,
                      static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
                      idx_k_new, kc, vc, idx_k_cache, kmax, idx_q, seq_len, len_max, nb_max,
                      hkv, d, d_idx, block, topk, cand_s, cand_b, n_chunks);
@@ -844,7 +863,7 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
   case GG:                                                                              \
     hipLaunchKernelGGL((decode_stream<GG, true>), dim3(pl.grid), dim3(256), 0, st, qq, kc, \
                        vc, len_max, seq_len, hq, hkv, block, sel, topk, pl.nseg,         \
-                       pl.seg_len, pl.n_units, scale * kLog2e, part_o, part_lse, cand_s,  \
+                       pl.seg_len, pl.u_q, pl.u_r, scale * kLog2e, part_o, part_lse, cand_s, \
                        cand_b, n_chunks, nb_max);                                        \
     break;
   switch (G) {

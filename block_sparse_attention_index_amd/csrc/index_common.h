@@ -73,7 +73,7 @@ __device__ __forceinline__ void write_row(int32_t *row, int topk, int cnt,
   if (lane > cnt && lane < topk) row[lane] = -1;
 }
 
-constexpr int kDecChunk = 16;    // blocks per decode-scan workgroup
+constexpr int kDecChunk = 64;    // blocks per decode-scan workgroup
 
 // As list_insert, with explicit per-lane block ids.
 __device__ __forceinline__ void list_insert_ids(float s, int bid, uint64_t mask,
@@ -117,98 +117,255 @@ __device__ __forceinline__ void wave_best(float &s, int &id) {
   }
 }
 
-// Decode index scan, one workgroup (256 threads) per chunk of kDecChunk = 16
-// blocks of one sequence (many small workgroups: the scan is latency-bound):
-// 16 lanes per block, each taking 8 consecutive index columns of the summary
-// row per 128-column slice (two 16-byte loads), the partial dot products
-// reduced within the 16-lane row.  The chunk's best K-1 among the blocks
-// before `own` are found by rank -- each candidate counts the candidates
-// ahead of it (score desc, block asc) -- and written at that rank to (out_s,
-// out_b), the tail padded with (-inf, -1).
+// Candidate key for the merge: an unsigned integer pair ordered like (score
+// descending, block ascending) -- hi is the score's order-preserving image
+// (-0 counted as +0, so equal scores tie as floats do), lo the complement of
+// the block id; (0, 0) stands for "no candidate".
+__device__ __forceinline__ uint32_t cand_hi(float s) {
+  return (uint32_t)f2key(s == 0.f ? 0.f : s) ^ 0x80000000u;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t x) {
+  const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+  return x > y ? x : y;
+}
+
+// Wave-wide unsigned maximum (every lane must be active): DPP steps within
+// each 16-lane row (quad swaps, half-row and row mirrors), then the four row
+// maxima read as scalars.  The result is uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = dpp_max_u32<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x = dpp_max_u32<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x = dpp_max_u32<0x141>(x);   // row_half_mirror
+  x = dpp_max_u32<0x140>(x);   // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
+
+// Wave-wide best key (hi first, then lo): two maxima, the second over the
+// lanes that hold the best hi.  Uniform result.
+__device__ __forceinline__ void wave_max_key(uint32_t &hi, uint32_t &lo) {
+  const uint32_t h = wave_max_u32(hi);
+  lo = wave_max_u32(hi == h ? lo : 0u);
+  hi = h;
+}
+
+// Decode index scan, one workgroup (256 threads) per chunk of kDecChunk = 64
+// blocks of one sequence: 16 lanes per block row, each taking 8 consecutive
+// index columns per 128-column slice (two 16-byte loads), four rows per
+// 16-lane group, the partial dot products reduced within the group.  The
+// loads depend only on nb_max, not on `own`, so they can be in flight before
+// the sequence length arrives.  The chunk's best K-1 among the blocks before
+// `own` (score desc, block asc) are then picked by one wave, one candidate
+// per lane, in K-1 rounds of a wave-wide maximum, and written in that order
+// to (out_s, out_b), the tail padded with (-inf, -1).
 __device__ __forceinline__ void decode_scan_chunk(
     const float *__restrict__ qv, const float *__restrict__ kmax_s, int64_t own,
     int64_t nb_max, int d_idx, int topk, int ch, float *__restrict__ out_s,
     int *__restrict__ out_b) {
+  constexpr int kPass = kDecChunk / 16;
   __shared__ float scs[kDecChunk];
   const int tid = threadIdx.x;
   const int km = topk - 1;
-  const int r = tid >> 4, l16 = tid & 15;   // block of the chunk, lane in its row
-  int64_t lim = own < nb_max ? own : nb_max;   // valid blocks are a prefix
-  lim -= (int64_t)ch * kDecChunk;
-  const int nv = lim < 0 ? 0 : (lim > kDecChunk ? kDecChunk : (int)lim);
-  const int64_t b = (int64_t)ch * kDecChunk + r;
-  float acc = 0.f;
-  if (r < nv) {
-    const float *row = kmax_s + b * d_idx;
-    if ((d_idx & 7) == 0) {
-      for (int c0 = 8 * l16; c0 < d_idx; c0 += 128) {
-        const float4 x0 = *reinterpret_cast<const float4 *>(row + c0);
-        const float4 x1 = *reinterpret_cast<const float4 *>(row + c0 + 4);
-        const float4 q0 = *reinterpret_cast<const float4 *>(qv + c0);
-        const float4 q1 = *reinterpret_cast<const float4 *>(qv + c0 + 4);
-        acc = fmaf(x0.x, q0.x, acc);
-        acc = fmaf(x0.y, q0.y, acc);
-        acc = fmaf(x0.z, q0.z, acc);
-        acc = fmaf(x0.w, q0.w, acc);
-        acc = fmaf(x1.x, q1.x, acc);
-        acc = fmaf(x1.y, q1.y, acc);
-        acc = fmaf(x1.z, q1.z, acc);
-        acc = fmaf(x1.w, q1.w, acc);
+  const int r0 = tid >> 4, l16 = tid & 15;   // first row of the lane group, lane in it
+  const int64_t cb0 = (int64_t)ch * kDecChunk;
+  const int64_t av = nb_max - cb0;
+  const int avail = av < 0 ? 0 : (av > kDecChunk ? kDecChunk : (int)av);
+  float acc[kPass];
+#pragma unroll
+  for (int p = 0; p < kPass; ++p) acc[p] = 0.f;
+  if ((d_idx & 7) == 0) {
+    for (int c0 = 8 * l16; c0 < d_idx; c0 += 128) {
+      const float4 q0 = *reinterpret_cast<const float4 *>(qv + c0);
+      const float4 q1 = *reinterpret_cast<const float4 *>(qv + c0 + 4);
+      float4 x0[kPass], x1[kPass];
+#pragma unroll
+      for (int p = 0; p < kPass; ++p) {
+        const int r = r0 + 16 * p;
+        x0[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        x1[p] = x0[p];
+        if (r < avail) {
+          const float *row = kmax_s + (cb0 + r) * d_idx + c0;
+          x0[p] = *reinterpret_cast<const float4 *>(row);
+          x1[p] = *reinterpret_cast<const float4 *>(row + 4);
+        }
       }
-    } else {
-      for (int c = l16; c < d_idx; c += 16) acc = fmaf(row[c], qv[c], acc);
+#pragma unroll
+      for (int p = 0; p < kPass; ++p) {
+        float a = acc[p];
+        a = fmaf(x0[p].x, q0.x, a);
+        a = fmaf(x0[p].y, q0.y, a);
+        a = fmaf(x0[p].z, q0.z, a);
+        a = fmaf(x0[p].w, q0.w, a);
+        a = fmaf(x1[p].x, q1.x, a);
+        a = fmaf(x1[p].y, q1.y, a);
+        a = fmaf(x1[p].z, q1.z, a);
+        a = fmaf(x1[p].w, q1.w, a);
+        acc[p] = a;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int r = r0 + 16 * p;
+      if (r < avail) {
+        const float *row = kmax_s + (cb0 + r) * d_idx;
+        for (int c = l16; c < d_idx; c += 16) acc[p] = fmaf(row[c], qv[c], acc[p]);
+      }
     }
   }
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (l16 == 0) scs[r] = acc;
+  for (int o = 8; o >= 1; o >>= 1)
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) acc[p] += __shfl_xor(acc[p], o, 64);
+  int64_t lim = own < nb_max ? own : nb_max;   // valid blocks are a prefix
+  lim -= cb0;
+  const int nv = lim < 0 ? 0 : (lim > kDecChunk ? kDecChunk : (int)lim);
+  if (l16 == 0)
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) scs[r0 + 16 * p] = acc[p];
   __syncthreads();
   if (km > 0 && tid < 64) {
+    // one candidate per lane; K-1 rounds each take the wave's best key
+    static_assert(kDecChunk == 64, "one scan candidate per lane");
     const int j = tid;
-    const float sj = j < nv ? scs[j] : 0.f;
-    if (j < nv) {
-      int rank = 0;
-#pragma unroll
-      for (int i = 0; i < kDecChunk; ++i) {
-        const float si = scs[i];
-        rank += (i < nv && (si > sj || (si == sj && i < j))) ? 1 : 0;
+    const float sj = scs[j];
+    uint32_t kh = j < nv ? cand_hi(sj) : 0u;
+    uint32_t kl = j < nv ? ~(uint32_t)(cb0 + j) : 0u;
+    for (int r = 0; r < km; ++r) {
+      uint32_t h = kh, l = kl;
+      wave_max_key(h, l);
+      const bool mine = kh == h && kl == l && (h | l) != 0u;
+      if (mine) {
+        out_s[r] = sj;
+        out_b[r] = (int)~l;
+        kh = 0u;
+        kl = 0u;
       }
-      if (rank < km) {
-        out_s[rank] = sj;
-        out_b[rank] = (int)((int64_t)ch * kDecChunk + j);
+      if ((h | l) == 0u && j == 0) {   // fewer than K-1 candidates: pad
+        out_s[r] = -INFINITY;
+        out_b[r] = -1;
       }
-    }
-    if (j >= nv && j < km) {
-      out_s[j] = -INFINITY;
-      out_b[j] = -1;
     }
   }
 }
 
-// Decode merge, one wave: the per-chunk lists of one sequence (each sorted,
-// score descending, padded with id -1) into the selection row: the best K-1
-// blocks ascending, then `own`, then -1.  A K-1-round tournament over the
-// list heads: lane c holds the heads of chunks c, c+64, c+128, c+192, a round
-// takes the wave-wide best head and advances that list.  `row` may point to
-// LDS.  More than 256 chunks fall back to inserting the candidates one by one
-// into a running list.
+// Merge of at most 64 chunk lists of length km <= KM, one whole wave: lane c
+// keeps chunk c's list in registers as keys; each of the K-1 rounds takes the
+// wave-wide best head and the winning lane shifts its list up.  The winners
+// are uniform, so the ascending row is ranked without any exchange.
+template <int KM, typename OwnF>
+__device__ __forceinline__ void merge_lists_regs(const float *__restrict__ g_s,
+                                                 const int *__restrict__ g_b, int n_chunks,
+                                                 int km, int topk, OwnF own_f, int32_t *row) {
+  const int lane = threadIdx.x & 63;
+  const bool has = lane < n_chunks;
+  uint32_t kh[KM], kl[KM];
+#pragma unroll
+  for (int i = 0; i < KM; ++i) {
+    float sv = 0.f;
+    int bv = -1;
+    if (has && i < km) {
+      sv = g_s[(int64_t)lane * km + i];
+      bv = g_b[(int64_t)lane * km + i];
+    }
+    kh[i] = bv >= 0 ? cand_hi(sv) : 0u;
+    kl[i] = bv >= 0 ? ~(uint32_t)bv : 0u;
+  }
+  uint32_t win[KM];
+  int cnt = 0;
+  bool done = false;
+#pragma unroll
+  for (int r = 0; r < KM; ++r) {
+    win[r] = 0u;
+    if (r < km && !done) {
+      uint32_t h = kh[0], l = kl[0];
+      wave_max_key(h, l);
+      if ((h | l) == 0u) {
+        done = true;   // every list exhausted
+      } else {
+        win[r] = ~l;
+        cnt = r + 1;
+        if (kh[0] == h && kl[0] == l) {   // this lane's head won: shift its list
+#pragma unroll
+          for (int i = 0; i + 1 < KM; ++i) {
+            kh[i] = kh[i + 1];
+            kl[i] = kl[i + 1];
+          }
+          kh[KM - 1] = 0u;
+          kl[KM - 1] = 0u;
+        }
+      }
+    }
+  }
+  const int own = own_f();
+  int mine = INT32_MAX, rank = 0;
+#pragma unroll
+  for (int i = 0; i < KM; ++i)
+    if (i < cnt && i == lane) mine = (int)win[i];
+#pragma unroll
+  for (int i = 0; i < KM; ++i) rank += (i < cnt && (int)win[i] < mine) ? 1 : 0;
+  if (lane < cnt) row[rank] = mine;
+  if (lane == cnt) row[cnt] = own;
+  if (lane > cnt && lane < topk) row[lane] = -1;
+}
+
+// Decode merge, one whole wave: the per-chunk lists of one sequence (each
+// sorted, score descending, padded with id -1) into the selection row: the
+// best K-1 blocks ascending, then `own`, then -1.  Up to 64 lists of up to 15
+// entries merge in registers (above); up to 256 lists take a K-1-round
+// tournament over the list heads: lane c holds the heads of chunks c, c+64,
+// c+128, c+192, a round takes the wave-wide best head and advances that list.
+// `row` may point to LDS.  More than 256 chunks fall back to inserting the
+// candidates one by one into a running list.  `own_f()` gives the own block;
+// it is called only after the lists' loads are issued (so a length it reads
+// can be in flight with them).
 constexpr int kMergeLanesChunks = 4;   // chunk lists per lane in the tournament
 
+template <typename OwnF>
 __device__ __forceinline__ void decode_merge_lists(
     const float *__restrict__ g_s, const int *__restrict__ g_b, int n_chunks, int topk,
-    int own, int32_t *row, float *stage_s = nullptr, int *stage_b = nullptr,
+    OwnF own_f, int32_t *row, float *stage_s = nullptr, int *stage_b = nullptr,
     int stage_cap = 0) {
   const int lane = threadIdx.x & 63;
   const int km = topk - 1;
+  if (km > 0 && n_chunks <= 64 && km <= 7) {
+    merge_lists_regs<7>(g_s, g_b, n_chunks, km, topk, own_f, row);
+    return;
+  }
+  if (km > 0 && n_chunks <= 64 && km <= 15) {
+    merge_lists_regs<15>(g_s, g_b, n_chunks, km, topk, own_f, row);
+    return;
+  }
   // copy the lists to the caller's LDS scratch when they fit: the tournament
   // then reads each advanced head at LDS latency
   const float *in_s = g_s;
   const int *in_b = g_b;
   const int64_t n_cand = (int64_t)n_chunks * (km > 0 ? km : 0);
   if (stage_s && n_cand <= stage_cap) {
-    for (int64_t i = lane; i < n_cand; i += 64) {
-      stage_s[i] = g_s[i];
-      stage_b[i] = g_b[i];
+    constexpr int kBatch = 16;   // loads per lane in flight together
+    for (int64_t i0 = 0; i0 < n_cand; i0 += 64 * kBatch) {
+      float xs[kBatch];
+      int xb[kBatch];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const int64_t i = i0 + 64 * t + lane;
+        xs[t] = i < n_cand ? g_s[i] : 0.f;
+        xb[t] = i < n_cand ? g_b[i] : 0;
+      }
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const int64_t i = i0 + 64 * t + lane;
+        if (i < n_cand) {
+          stage_s[i] = xs[t];
+          stage_b[i] = xb[t];
+        }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // the wave's LDS writes have landed
     in_s = stage_s;
@@ -259,7 +416,7 @@ __device__ __forceinline__ void decode_merge_lists(
         }
       }
     }
-    write_row(row, topk, cnt, lane < cnt ? tops : INT32_MAX, own);
+    write_row(row, topk, cnt, lane < cnt ? tops : INT32_MAX, own_f());
     return;
   }
   int cnt = 0;
@@ -284,7 +441,7 @@ __device__ __forceinline__ void decode_merge_lists(
     }
   }
   if (lane >= cnt) lb = INT32_MAX;
-  write_row(row, topk, cnt, lb, own);
+  write_row(row, topk, cnt, lb, own_f());
 }
 
 }  // namespace msa

@@ -15,6 +15,9 @@ namespace {
 constexpr int32_t kMaxBlock = 4096;
 constexpr int32_t kMaxTopk = 64;
 constexpr int64_t kMaxGridY = 65535;
+// (sequence, KV head, selected block) work items of one decode call: the
+// streaming kernel numbers their segments in 32 bits
+constexpr int64_t kMaxDecodeItems = int64_t(1) << 28;
 
 bool block_ok(int32_t b) { return b >= 16 && b <= kMaxBlock && b % 16 == 0; }
 bool topk_ok(int32_t k) { return k >= 1 && k <= kMaxTopk; }
@@ -213,7 +216,8 @@ int msa_sparse_gqa_decode(const void *q, const void *k_cache,
       (dtype != MSA_F32 && dtype != MSA_BF16) || n_seq < 1 ||
       n_seq > kMaxGridY || len_max < 1 || hq < 1 || hkv < 1 ||
       hkv > kMaxGridY || hq % hkv != 0 || d < 1 || !block_ok(block) ||
-      !topk_ok(topk) || !std::isfinite(scale))
+      !topk_ok(topk) || !std::isfinite(scale) ||
+      (int64_t)n_seq * hkv * topk > kMaxDecodeItems)
     return MSA_ERR_INVALID_ARG;
   if (!msa::decode_supported(dtype, d, hq / hkv) ||
       !msa::decode_partials_ok(dtype, d, hq / hkv, block, topk))
@@ -245,7 +249,8 @@ int msa_decode_step(const void *q, const void *k_new, const void *v_new,
       !seq_len || !sel || !o || !ws || (dtype != MSA_F32 && dtype != MSA_BF16) ||
       n_seq < 1 || n_seq > kMaxGridY || len_max < 1 || nb_max < 1 ||
       nb_max > INT32_MAX || hq < 1 || hkv < 1 || hq % hkv != 0 || d < 1 ||
-      !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk) || !std::isfinite(scale))
+      !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk) || !std::isfinite(scale) ||
+      (int64_t)n_seq * hkv * topk > kMaxDecodeItems)
     return MSA_ERR_INVALID_ARG;
   if (!msa::decode_step_supported(dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
   if (ws_bytes < msa::decode_step_ws_bytes(n_seq, nb_max, hq, d, block, topk))

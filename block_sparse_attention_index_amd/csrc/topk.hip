@@ -157,7 +157,8 @@ __global__ __launch_bounds__(64) void topk_decode_merge(
   const int64_t len = seq_len[s];
   const int64_t own = len >= 1 ? (len - 1) / B : 0;
   decode_merge_lists(ws_s + (int64_t)s * n_chunks * (topk - 1),
-                     ws_b + (int64_t)s * n_chunks * (topk - 1), n_chunks, topk, (int)own,
+                     ws_b + (int64_t)s * n_chunks * (topk - 1), n_chunks, topk,
+                     [&] { return (int)own; },
                      sel + (int64_t)s * topk, st_s, st_b, 2048);
 }
 

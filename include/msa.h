@@ -199,7 +199,8 @@ int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
  *   o        [n_seq][Hq][d] fp32;  lse [n_seq][Hq] fp32 (may be NULL)
  *   ws       device scratch of msa_decode_workspace_bytes() bytes
  *   Supported: fp32 and bf16 with d in {64, 128}, bf16 with d = 256;
- *   Hq/Hkv in {1, 2, 4, 8, 16}.
+ *   Hq/Hkv in {1, 2, 4, 8, 16}.  n_seq * Hkv * K <= 2^28 (else
+ *   MSA_ERR_INVALID_ARG).
  * ------------------------------------------------------------------------ */
 size_t msa_decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t d,
                                   int32_t block, int32_t topk);
@@ -238,6 +239,7 @@ int msa_sparse_gqa_decode(const void *q, const void *k_cache,
  *   sel [n_seq][K] int32 out;  o [n_seq][Hq][d] fp32;  lse [n_seq][Hq] (may be NULL)
  *   ws  device scratch of msa_decode_step_workspace_bytes() bytes
  *   Supported: bf16, d = 128, Hq/Hkv in {1, 2, 4, 8, 16}.
+ *   n_seq * Hkv * K <= 2^28 (else MSA_ERR_INVALID_ARG).
  * ------------------------------------------------------------------------ */
 size_t msa_decode_step_workspace_bytes(int32_t n_seq, int64_t nb_max, int32_t hq,
                                        int32_t d, int32_t block, int32_t topk);
