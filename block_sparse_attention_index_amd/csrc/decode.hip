@@ -437,6 +437,9 @@ __global__ __launch_bounds__(256) void decode_stream(
     if (!last) {
       dma_kv(nxt, cu, cu.t0 + kc0 + kSK, kv_rows(cu.nk - kc0 - kSK));
     } else if (un < u_end) {
+      // a one-chunk unit read its queries just now: every wave must be done
+      // with the staging area before the next unit's copy lands there
+      if (ci == 0) __syncthreads();
       dma_q(nu);
       dma_kv(nxt, nu, nu.t0, kv_rows(nu.nk));
     }
