@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) void decode_stream(
         int *st_b = reinterpret_cast<int *>(st_s) + (int)(sizeof(StreamBuf) / 16);
         const size_t c0 = (size_t)s * n_chunks * (topk - 1);
         decode_merge_lists(
-            cand_s + c0, cand_b + c0, n_chunks, topk,
+            cand_s + c0, cand_b + c0, n_chunks, topk, 1,
             [&] {
               int64_t own = len >= 1 ? (len - 1) / B : 0;
               return (int)(own >= nb_max ? nb_max - 1 : own);
@@ -656,7 +656,7 @@ __global__ __launch_bounds__(256) void dstep_scan(
   }
   if (topk > 1)
     decode_scan_chunk(idx_q + (int64_t)s * d_idx, kmax + (int64_t)s * nb_max * d_idx, own,
-                      nb_max, d_idx, topk, ch,
+                      nb_max, d_idx, topk - 1, ch,
                       cand_s + ((int64_t)s * n_chunks + ch) * (topk - 1),
                       cand_b + ((int64_t)s * n_chunks + ch) * (topk - 1));
 }

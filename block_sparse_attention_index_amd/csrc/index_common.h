@@ -59,18 +59,30 @@ __device__ __forceinline__ void list_insert(float s, int base, uint64_t mask,
   }
 }
 
-// Write sel row: the cnt list blocks ascending, then own, then -1.
+// Write sel row: the cnt list blocks ascending, then the forced blocks
+// first .. own (own alone without a local window), then -1.  The list blocks
+// all lie below `first`, so the row is ascending.
 __device__ __forceinline__ void write_row(int32_t *row, int topk, int cnt,
-                                          int lb, int own) {
+                                          int lb, int own, int first) {
   const int lane = threadIdx.x & 63;
   int rank = 0;
   for (int j = 0; j < cnt; ++j) {
     const int bj = shfl_i(lb, j);
     rank += (bj < lb) ? 1 : 0;
   }
+  const int nf = own - first + 1;
   if (lane < cnt) row[rank] = lb;
-  if (lane == cnt) row[cnt] = own;
-  if (lane > cnt && lane < topk) row[lane] = -1;
+  if (lane >= cnt && lane < cnt + nf) row[lane] = first + (lane - cnt);
+  if (lane >= cnt + nf && lane < topk) row[lane] = -1;
+}
+__device__ __forceinline__ void write_row(int32_t *row, int topk, int cnt,
+                                          int lb, int own) {
+  write_row(row, topk, cnt, lb, own, own);
+}
+
+// First block of the forced local window of `win` blocks ending at `own`.
+__device__ __forceinline__ int window_first(int own, int win) {
+  return own - win + 1 > 0 ? own - win + 1 : 0;
 }
 
 constexpr int kDecChunk = 64;    // blocks per decode-scan workgroup
@@ -160,18 +172,18 @@ __device__ __forceinline__ void wave_max_key(uint32_t &hi, uint32_t &lo) {
 // index columns per 128-column slice (two 16-byte loads), four rows per
 // 16-lane group, the partial dot products reduced within the group.  The
 // loads depend only on nb_max, not on `own`, so they can be in flight before
-// the sequence length arrives.  The chunk's best K-1 among the blocks before
-// `own` (score desc, block asc) are then picked by one wave, one candidate
-// per lane, in K-1 rounds of a wave-wide maximum, and written in that order
-// to (out_s, out_b), the tail padded with (-inf, -1).
+// the sequence length arrives.  The chunk's best km among the candidate
+// blocks b < cand_lim (score desc, block asc) are then picked by one wave, one
+// candidate per lane, in km rounds of a wave-wide maximum, and written in that
+// order to (out_s, out_b), the tail padded with (-inf, -1).  (Without a local
+// window cand_lim is the own block and km = K-1.)
 __device__ __forceinline__ void decode_scan_chunk(
-    const float *__restrict__ qv, const float *__restrict__ kmax_s, int64_t own,
-    int64_t nb_max, int d_idx, int topk, int ch, float *__restrict__ out_s,
+    const float *__restrict__ qv, const float *__restrict__ kmax_s, int64_t cand_lim,
+    int64_t nb_max, int d_idx, int km, int ch, float *__restrict__ out_s,
     int *__restrict__ out_b) {
   constexpr int kPass = kDecChunk / 16;
   __shared__ float scs[kDecChunk];
   const int tid = threadIdx.x;
-  const int km = topk - 1;
   const int r0 = tid >> 4, l16 = tid & 15;   // first row of the lane group, lane in it
   const int64_t cb0 = (int64_t)ch * kDecChunk;
   const int64_t av = nb_max - cb0;
@@ -223,7 +235,7 @@ __device__ __forceinline__ void decode_scan_chunk(
   for (int o = 8; o >= 1; o >>= 1)
 #pragma unroll
     for (int p = 0; p < kPass; ++p) acc[p] += __shfl_xor(acc[p], o, 64);
-  int64_t lim = own < nb_max ? own : nb_max;   // valid blocks are a prefix
+  int64_t lim = cand_lim < nb_max ? cand_lim : nb_max;   // candidates are a prefix
   lim -= cb0;
   const int nv = lim < 0 ? 0 : (lim > kDecChunk ? kDecChunk : (int)lim);
   if (l16 == 0)
@@ -262,7 +274,8 @@ __device__ __forceinline__ void decode_scan_chunk(
 template <int KM, typename OwnF>
 __device__ __forceinline__ void merge_lists_regs(const float *__restrict__ g_s,
                                                  const int *__restrict__ g_b, int n_chunks,
-                                                 int km, int topk, OwnF own_f, int32_t *row) {
+                                                 int km, int topk, int win, OwnF own_f,
+                                                 int32_t *row) {
   const int lane = threadIdx.x & 63;
   const bool has = lane < n_chunks;
   uint32_t kh[KM], kl[KM];
@@ -277,19 +290,19 @@ __device__ __forceinline__ void merge_lists_regs(const float *__restrict__ g_s,
     kh[i] = bv >= 0 ? cand_hi(sv) : 0u;
     kl[i] = bv >= 0 ? ~(uint32_t)bv : 0u;
   }
-  uint32_t win[KM];
+  uint32_t wins[KM];
   int cnt = 0;
   bool done = false;
 #pragma unroll
   for (int r = 0; r < KM; ++r) {
-    win[r] = 0u;
+    wins[r] = 0u;
     if (r < km && !done) {
       uint32_t h = kh[0], l = kl[0];
       wave_max_key(h, l);
       if ((h | l) == 0u) {
         done = true;   // every list exhausted
       } else {
-        win[r] = ~l;
+        wins[r] = ~l;
         cnt = r + 1;
         if (kh[0] == h && kl[0] == l) {   // this lane's head won: shift its list
 #pragma unroll
@@ -307,17 +320,19 @@ __device__ __forceinline__ void merge_lists_regs(const float *__restrict__ g_s,
   int mine = INT32_MAX, rank = 0;
 #pragma unroll
   for (int i = 0; i < KM; ++i)
-    if (i < cnt && i == lane) mine = (int)win[i];
+    if (i < cnt && i == lane) mine = (int)wins[i];
 #pragma unroll
-  for (int i = 0; i < KM; ++i) rank += (i < cnt && (int)win[i] < mine) ? 1 : 0;
+  for (int i = 0; i < KM; ++i) rank += (i < cnt && (int)wins[i] < mine) ? 1 : 0;
+  const int first = window_first(own, win), nf = own - first + 1;
   if (lane < cnt) row[rank] = mine;
-  if (lane == cnt) row[cnt] = own;
-  if (lane > cnt && lane < topk) row[lane] = -1;
+  if (lane >= cnt && lane < cnt + nf) row[lane] = first + (lane - cnt);
+  if (lane >= cnt + nf && lane < topk) row[lane] = -1;
 }
 
 // Decode merge, one whole wave: the per-chunk lists of one sequence (each
-// sorted, score descending, padded with id -1) into the selection row: the
-// best K-1 blocks ascending, then `own`, then -1.  Up to 64 lists of up to 15
+// sorted, score descending, padded with id -1, km = K - win entries) into the
+// selection row: the best km blocks ascending, then the forced window
+// own-win+1 .. own (clipped at block 0), then -1.  Up to 64 lists of up to 15
 // entries merge in registers (above); up to 256 lists take a K-1-round
 // tournament over the list heads: lane c holds the heads of chunks c, c+64,
 // c+128, c+192, a round takes the wave-wide best head and advances that list.
@@ -330,16 +345,16 @@ constexpr int kMergeLanesChunks = 4;   // chunk lists per lane in the tournament
 template <typename OwnF>
 __device__ __forceinline__ void decode_merge_lists(
     const float *__restrict__ g_s, const int *__restrict__ g_b, int n_chunks, int topk,
-    OwnF own_f, int32_t *row, float *stage_s = nullptr, int *stage_b = nullptr,
+    int win, OwnF own_f, int32_t *row, float *stage_s = nullptr, int *stage_b = nullptr,
     int stage_cap = 0) {
   const int lane = threadIdx.x & 63;
-  const int km = topk - 1;
+  const int km = topk - win;   // picks by score; lists hold km entries each
   if (km > 0 && n_chunks <= 64 && km <= 7) {
-    merge_lists_regs<7>(g_s, g_b, n_chunks, km, topk, own_f, row);
+    merge_lists_regs<7>(g_s, g_b, n_chunks, km, topk, win, own_f, row);
     return;
   }
   if (km > 0 && n_chunks <= 64 && km <= 15) {
-    merge_lists_regs<15>(g_s, g_b, n_chunks, km, topk, own_f, row);
+    merge_lists_regs<15>(g_s, g_b, n_chunks, km, topk, win, own_f, row);
     return;
   }
   // copy the lists to the caller's LDS scratch when they fit: the tournament
@@ -416,7 +431,8 @@ __device__ __forceinline__ void decode_merge_lists(
         }
       }
     }
-    write_row(row, topk, cnt, lane < cnt ? tops : INT32_MAX, own_f());
+    const int own = own_f();
+    write_row(row, topk, cnt, lane < cnt ? tops : INT32_MAX, own, window_first(own, win));
     return;
   }
   int cnt = 0;
@@ -441,7 +457,8 @@ __device__ __forceinline__ void decode_merge_lists(
     }
   }
   if (lane >= cnt) lb = INT32_MAX;
-  write_row(row, topk, cnt, lb, own_f());
+  const int own = own_f();
+  write_row(row, topk, cnt, lb, own, window_first(own, win));
 }
 
 }  // namespace msa

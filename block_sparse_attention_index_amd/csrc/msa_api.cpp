@@ -110,18 +110,40 @@ int msa_index_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
                                     as_stream(stream)));
 }
 
-int msa_index_topk(const float *idx_q, int64_t n_q, int64_t q_pos0,
-                   const float *kmax, int64_t nb, int32_t d_idx, int32_t block,
-                   int32_t topk, int32_t *sel, void *stream) {
+int msa_index_pool_mean(const float *idx_k, int32_t n_seq, int64_t len_max,
+                        const int64_t *seq_len, int32_t d_idx, int32_t block,
+                        int64_t blk_begin, int64_t blk_end, float *kmean,
+                        int64_t nb_max, void *stream) {
+  if (!idx_k || !kmean || n_seq < 1 || n_seq > kMaxGridY || len_max < 1 ||
+      !didx_ok(d_idx) || !block_ok(block) || nb_max < cdiv(len_max, block))
+    return MSA_ERR_INVALID_ARG;
+  if (blk_begin < -1 || (blk_begin >= 0 && (blk_end <= blk_begin || blk_end > nb_max ||
+                                             blk_end - blk_begin > INT32_MAX)))
+    return MSA_ERR_INVALID_ARG;
+  return status_of(msa::launch_pool_mean(idx_k, n_seq, len_max, seq_len, d_idx,
+                                         block, blk_begin, blk_end, kmean, nb_max,
+                                         as_stream(stream)));
+}
+
+int msa_index_topk_window(const float *idx_q, int64_t n_q, int64_t q_pos0,
+                          const float *kmax, int64_t nb, int32_t d_idx, int32_t block,
+                          int32_t topk, int32_t window, int32_t *sel, void *stream) {
   if (!idx_q || !kmax || !sel || n_q < 0 || q_pos0 < 0 || !didx_ok(d_idx) ||
-      !block_ok(block) || !topk_ok(topk) || nb < 1)
+      !block_ok(block) || !topk_ok(topk) || nb < 1 || window < 1 || window > topk)
     return MSA_ERR_INVALID_ARG;
   if (n_q == 0) return MSA_OK;
   if ((q_pos0 + n_q - 1) / block >= nb || (q_pos0 + n_q - 1) / block > INT32_MAX)
     return MSA_ERR_INVALID_ARG;
   return status_of(msa::launch_topk_prefill(idx_q, n_q, q_pos0, kmax, nb, d_idx,
-                                            block, topk, sel,
+                                            block, topk, window, sel,
                                             as_stream(stream)));
+}
+
+int msa_index_topk(const float *idx_q, int64_t n_q, int64_t q_pos0,
+                   const float *kmax, int64_t nb, int32_t d_idx, int32_t block,
+                   int32_t topk, int32_t *sel, void *stream) {
+  return msa_index_topk_window(idx_q, n_q, q_pos0, kmax, nb, d_idx, block, topk, 1, sel,
+                               stream);
 }
 
 size_t msa_topk_decode_workspace_bytes(int32_t n_seq, int64_t nb_max,
@@ -130,20 +152,30 @@ size_t msa_topk_decode_workspace_bytes(int32_t n_seq, int64_t nb_max,
   return msa::topk_decode_ws_bytes(n_seq, nb_max, topk);
 }
 
+int msa_index_topk_decode_window(const float *idx_q, int32_t n_seq,
+                                 const int64_t *seq_len, const float *kmax,
+                                 int64_t nb_max, int32_t d_idx, int32_t block,
+                                 int32_t topk, int32_t window, int32_t *sel, void *ws,
+                                 size_t ws_bytes, void *stream) {
+  if (!idx_q || !seq_len || !kmax || !sel || !ws || n_seq < 1 ||
+      n_seq > kMaxGridY || nb_max < 1 || nb_max > INT32_MAX ||
+      !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk) || window < 1 ||
+      window > topk)
+    return MSA_ERR_INVALID_ARG;
+  if (ws_bytes < msa::topk_decode_ws_bytes(n_seq, nb_max, topk))
+    return MSA_ERR_WORKSPACE;
+  return status_of(msa::launch_topk_decode(idx_q, n_seq, seq_len, kmax, nb_max,
+                                           d_idx, block, topk, window, sel, ws,
+                                           as_stream(stream)));
+}
+
 int msa_index_topk_decode(const float *idx_q, int32_t n_seq,
                           const int64_t *seq_len, const float *kmax,
                           int64_t nb_max, int32_t d_idx, int32_t block,
                           int32_t topk, int32_t *sel, void *ws,
                           size_t ws_bytes, void *stream) {
-  if (!idx_q || !seq_len || !kmax || !sel || !ws || n_seq < 1 ||
-      n_seq > kMaxGridY || nb_max < 1 || nb_max > INT32_MAX ||
-      !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk))
-    return MSA_ERR_INVALID_ARG;
-  if (ws_bytes < msa::topk_decode_ws_bytes(n_seq, nb_max, topk))
-    return MSA_ERR_WORKSPACE;
-  return status_of(msa::launch_topk_decode(idx_q, n_seq, seq_len, kmax, nb_max,
-                                           d_idx, block, topk, sel, ws,
-                                           as_stream(stream)));
+  return msa_index_topk_decode_window(idx_q, n_seq, seq_len, kmax, nb_max, d_idx, block,
+                                      topk, 1, sel, ws, ws_bytes, stream);
 }
 
 size_t msa_invert_workspace_bytes(int64_t n_q, int32_t topk, int64_t n_blocks) {

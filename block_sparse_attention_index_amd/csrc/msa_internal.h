@@ -11,6 +11,10 @@ namespace msa {
 // Launch helpers: each enqueues its kernels on `st` and returns the HIP
 // status of the launch.  Arguments were validated by the entry point.
 
+hipError_t launch_pool_mean(const float *idx_k, int32_t n_seq, int64_t len_max,
+                            const int64_t *seq_len, int32_t d_idx, int32_t block,
+                            int64_t blk_begin, int64_t blk_end, float *kmean,
+                            int64_t nb_max, hipStream_t st);
 hipError_t launch_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
                        const int64_t *seq_len, int32_t d_idx, int32_t block,
                        int64_t blk_begin, int64_t blk_end, float *kmax,
@@ -18,14 +22,14 @@ hipError_t launch_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
 
 hipError_t launch_topk_prefill(const float *idx_q, int64_t n_q, int64_t q_pos0,
                                const float *kmax, int64_t nb, int32_t d_idx,
-                               int32_t block, int32_t topk, int32_t *sel,
+                               int32_t block, int32_t topk, int32_t win, int32_t *sel,
                                hipStream_t st);
 
 size_t topk_decode_ws_bytes(int32_t n_seq, int64_t nb_max, int32_t topk);
 hipError_t launch_topk_decode(const float *idx_q, int32_t n_seq,
                               const int64_t *seq_len, const float *kmax,
                               int64_t nb_max, int32_t d_idx, int32_t block,
-                              int32_t topk, int32_t *sel, void *ws,
+                              int32_t topk, int32_t win, int32_t *sel, void *ws,
                               hipStream_t st);
 
 size_t invert_ws_bytes(int64_t n_q, int32_t topk, int64_t n_blocks);

@@ -110,7 +110,81 @@ __global__ __launch_bounds__(256) void pool_append(
   }
 }
 
+// Mean-pool variant (the block summary of section 3.3's sketch in
+// chenxutan.com's page): kmean[s][b][c] = (sum over the block's valid tokens
+// of idx_k[s][t][c]) / count, summed in fp32 -- per thread over rows r,
+// r+R, ..., then the R partial sums in row-group order -- and divided once.
+// Same grid and row split as the max-pool kernels; d_idx <= 1024 with
+// d_idx % 4 == 0, else d_idx <= 256.
+template <bool VEC4>
+__global__ __launch_bounds__(256) void pool_mean(
+    const float *__restrict__ idx_k, int64_t len_max,
+    const int64_t *__restrict__ seq_len, int d_idx, int B, int64_t blk_begin,
+    float *__restrict__ kmean, int64_t nb_max) {
+  __shared__ float4 red[256];
+  const int s = blockIdx.y;
+  int64_t len = seq_len ? seq_len[s] : len_max;
+  if (len > len_max) len = len_max;
+  if (len < 1) return;
+  const int64_t b = blk_begin < 0 ? (len - 1) / B : blk_begin + blockIdx.x;
+  const int64_t t0 = b * B;
+  if (t0 >= len || b >= nb_max) return;
+  const int64_t t1 = t0 + B < len ? t0 + B : len;
+  const int cw = VEC4 ? d_idx >> 2 : d_idx;   // column lanes
+  const int R = 256 / cw;
+  const int tid = threadIdx.x;
+  const int col = tid % cw, r = tid / cw;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (r < R) {
+    const float *src = idx_k + ((int64_t)s * len_max) * d_idx;
+    for (int64_t t = t0 + r; t < t1; t += R) {
+      if constexpr (VEC4) {
+        const float4 x = reinterpret_cast<const float4 *>(src + t * d_idx)[col];
+        a.x += x.x;
+        a.y += x.y;
+        a.z += x.z;
+        a.w += x.w;
+      } else {
+        a.x += src[t * d_idx + col];
+      }
+    }
+  }
+  red[tid] = a;
+  __syncthreads();
+  if (tid < cw) {
+    float4 m = red[tid];
+    for (int rr = 1; rr < R; ++rr) {
+      const float4 y = red[rr * cw + tid];
+      m.x += y.x;
+      m.y += y.y;
+      m.z += y.z;
+      m.w += y.w;
+    }
+    const float n = (float)(t1 - t0);
+    float *dst = kmean + ((int64_t)s * nb_max + b) * d_idx;
+    if constexpr (VEC4)
+      reinterpret_cast<float4 *>(dst)[tid] = make_float4(m.x / n, m.y / n, m.z / n, m.w / n);
+    else
+      dst[tid] = m.x / n;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pool_mean(const float *idx_k, int32_t n_seq, int64_t len_max,
+                            const int64_t *seq_len, int32_t d_idx, int32_t block,
+                            int64_t blk_begin, int64_t blk_end, float *kmean,
+                            int64_t nb_max, hipStream_t st) {
+  const int64_t nblk = blk_begin < 0 ? 1 : blk_end - blk_begin;
+  dim3 grid((unsigned)nblk, (unsigned)n_seq);
+  if (d_idx % 4 == 0)
+    hipLaunchKernelGGL(pool_mean<true>, grid, dim3(256), 0, st, idx_k, len_max, seq_len,
+                       d_idx, block, blk_begin, kmean, nb_max);
+  else
+    hipLaunchKernelGGL(pool_mean<false>, grid, dim3(256), 0, st, idx_k, len_max, seq_len,
+                       d_idx, block, blk_begin, kmean, nb_max);
+  return hipGetLastError();
+}
 
 hipError_t launch_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
                        const int64_t *seq_len, int32_t d_idx, int32_t block,

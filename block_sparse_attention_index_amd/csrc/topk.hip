@@ -5,7 +5,10 @@
 //
 // Selection rule: candidates are the blocks strictly before the query's own
 // block; keep the best K-1 by (score desc, block asc); add the own block;
-// store ascending, -1 padded.
+// store ascending, -1 padded.  With a local window of win blocks (a variant
+// after the sliding window of section 3.3's sketch in chenxutan.com's page),
+// the own block and the win-1 blocks before it are forced and the best K-win
+// of the blocks below them are kept.
 //
 // Running top list, one per query: lanes 0..K-2 of a wave hold the list
 // entries in rank order.  Candidates arrive in ascending block order, so a
@@ -33,7 +36,7 @@ constexpr int kMaxList = 64;
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void topk_prefill_kernel(
     const float *__restrict__ idx_q, int64_t n_q, int64_t q_pos0,
-    const float *__restrict__ kmax, int d_idx, int B, int topk,
+    const float *__restrict__ kmax, int d_idx, int B, int topk, int win,
     int32_t *__restrict__ sel) {
   __shared__ float qs[kQT][kPad];
   __shared__ float ks[kCB][kPad];
@@ -48,8 +51,9 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
   const int64_t tile = n_tiles - 1 - blockIdx.x;
   const int64_t q0 = tile * kQT;
   const int nq = (int)(n_q - q0 < kQT ? n_q - q0 : kQT);
-  const int km = topk - 1;
-  const int64_t own_last = (q_pos0 + q0 + nq - 1) / B;
+  const int km = topk - win;   // picks by score; the window win is forced
+  // candidates of the tile's last query: the blocks below its window
+  const int64_t cand_last = (q_pos0 + q0 + nq - 1) / B - win + 1;
 
   if (tid < kQT) lst_n[tid] = 0;
   for (int e = tid; e < kQT * kMaxList; e += 256) {
@@ -59,8 +63,8 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
   __syncthreads();
 
   const int ty = tid >> 4, tx = tid & 15;
-  for (int64_t b0 = 0; km > 0 && b0 < own_last; b0 += kCB) {
-    const int nbk = (int)(own_last - b0 < kCB ? own_last - b0 : kCB);
+  for (int64_t b0 = 0; km > 0 && b0 < cand_last; b0 += kCB) {
+    const int nbk = (int)(cand_last - b0 < kCB ? cand_last - b0 : kCB);
     float acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -97,9 +101,9 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
     for (int jq = 0; jq < 16; ++jq) {
       const int qi = wave * 16 + jq;
       if (qi >= nq) break;
-      const int64_t own = (q_pos0 + q0 + qi) / B;
+      const int64_t lim = (q_pos0 + q0 + qi) / B - win + 1;
       const float s = sc[qi][lane];
-      const bool valid = lane < nbk && b0 + lane < own;
+      const bool valid = lane < nbk && b0 + lane < lim;
       int cnt = lst_n[qi];
       float ls = lane < km ? lst_s[qi][lane] : -INFINITY;
       int lb = lane < km ? lst_b[qi][lane] : -1;
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
     const int own = (int)((q_pos0 + q0 + qi) / B);
     const int cnt = km > 0 ? lst_n[qi] : 0;
     const int lb = (lane < cnt) ? lst_b[qi][lane] : INT32_MAX;
-    write_row(sel + (q0 + qi) * topk, topk, cnt, lb, own);
+    write_row(sel + (q0 + qi) * topk, topk, cnt, lb, own, window_first(own, win));
   }
 }
 
@@ -136,29 +140,29 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void topk_decode_kernel(
     const float *__restrict__ idx_q, const int64_t *__restrict__ seq_len,
-    const float *__restrict__ kmax, int64_t nb_max, int d_idx, int B, int topk,
+    const float *__restrict__ kmax, int64_t nb_max, int d_idx, int B, int km, int win,
     float *__restrict__ ws_s, int *__restrict__ ws_b, int n_chunks) {
   const int s = blockIdx.y;
   const int64_t len = seq_len[s];
   const int64_t own = len >= 1 ? (len - 1) / B : 0;   // the query sits at len - 1
-  decode_scan_chunk(idx_q + (int64_t)s * d_idx, kmax + (int64_t)s * nb_max * d_idx, own,
-                    nb_max, d_idx, topk, blockIdx.x,
-                    ws_s + ((int64_t)s * n_chunks + blockIdx.x) * (topk - 1),
-                    ws_b + ((int64_t)s * n_chunks + blockIdx.x) * (topk - 1));
+  decode_scan_chunk(idx_q + (int64_t)s * d_idx, kmax + (int64_t)s * nb_max * d_idx,
+                    own - win + 1, nb_max, d_idx, km, blockIdx.x,
+                    ws_s + ((int64_t)s * n_chunks + blockIdx.x) * km,
+                    ws_b + ((int64_t)s * n_chunks + blockIdx.x) * km);
 }
 
 __global__ __launch_bounds__(64) void topk_decode_merge(
-    const int64_t *__restrict__ seq_len, int B, int topk,
+    const int64_t *__restrict__ seq_len, int B, int topk, int win,
     const float *__restrict__ ws_s, const int *__restrict__ ws_b, int n_chunks,
     int32_t *__restrict__ sel) {
   __shared__ float st_s[2048];
   __shared__ int st_b[2048];
   const int s = blockIdx.x;
   const int64_t len = seq_len[s];
-  const int64_t own = len >= 1 ? (len - 1) / B : 0;
-  decode_merge_lists(ws_s + (int64_t)s * n_chunks * (topk - 1),
-                     ws_b + (int64_t)s * n_chunks * (topk - 1), n_chunks, topk,
-                     [&] { return (int)own; },
+  const int km = topk - win;
+  decode_merge_lists(ws_s + (int64_t)s * n_chunks * km, ws_b + (int64_t)s * n_chunks * km,
+                     n_chunks, topk, win,
+                     [&] { return (int)(len >= 1 ? (len - 1) / B : 0); },
                      sel + (int64_t)s * topk, st_s, st_b, 2048);
 }
 
@@ -166,12 +170,12 @@ __global__ __launch_bounds__(64) void topk_decode_merge(
 
 hipError_t launch_topk_prefill(const float *idx_q, int64_t n_q, int64_t q_pos0,
                                const float *kmax, int64_t nb, int32_t d_idx,
-                               int32_t block, int32_t topk, int32_t *sel,
+                               int32_t block, int32_t topk, int32_t win, int32_t *sel,
                                hipStream_t st) {
   (void)nb;
   const int64_t n_tiles = (n_q + kQT - 1) / kQT;
   hipLaunchKernelGGL(topk_prefill_kernel, dim3((unsigned)n_tiles), dim3(256), 0,
-                     st, idx_q, n_q, q_pos0, kmax, d_idx, block, topk, sel);
+                     st, idx_q, n_q, q_pos0, kmax, d_idx, block, topk, win, sel);
   return hipGetLastError();
 }
 
@@ -185,7 +189,7 @@ size_t topk_decode_ws_bytes(int32_t n_seq, int64_t nb_max, int32_t topk) {
 hipError_t launch_topk_decode(const float *idx_q, int32_t n_seq,
                               const int64_t *seq_len, const float *kmax,
                               int64_t nb_max, int32_t d_idx, int32_t block,
-                              int32_t topk, int32_t *sel, void *ws,
+                              int32_t topk, int32_t win, int32_t *sel, void *ws,
                               hipStream_t st) {
   const int n_chunks = (int)((nb_max + kDecChunk - 1) / kDecChunk);
   const size_t n = (size_t)n_seq * n_chunks * (topk > 1 ? topk - 1 : 1);
@@ -193,13 +197,13 @@ hipError_t launch_topk_decode(const float *idx_q, int32_t n_seq,
   float *ws_s = reinterpret_cast<float *>(w);
   w += align256(n * sizeof(float));
   int *ws_b = reinterpret_cast<int *>(w);
-  if (topk > 1) {
+  if (topk > win) {
     hipLaunchKernelGGL(topk_decode_kernel, dim3(n_chunks, n_seq), dim3(256), 0, st,
-                       idx_q, seq_len, kmax, nb_max, d_idx, block, topk, ws_s,
+                       idx_q, seq_len, kmax, nb_max, d_idx, block, topk - win, win, ws_s,
                        ws_b, n_chunks);
   }
   hipLaunchKernelGGL(topk_decode_merge, dim3(n_seq), dim3(64), 0, st, seq_len,
-                     block, topk, ws_s, ws_b, n_chunks, sel);
+                     block, topk, win, ws_s, ws_b, n_chunks, sel);
   return hipGetLastError();
 }
 

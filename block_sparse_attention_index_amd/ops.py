@@ -30,6 +30,7 @@ ENTRY_POINTS = (
     "msa_prefill_workspace_bytes", "msa_sparse_gqa_prefill",
     "msa_decode_workspace_bytes", "msa_sparse_gqa_decode",
     "msa_decode_step_workspace_bytes", "msa_decode_step",
+    "msa_index_pool_mean", "msa_index_topk_window", "msa_index_topk_decode_window",
 )
 
 
@@ -56,7 +57,13 @@ def load():
     sig = {
         "msa_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "msa_index_pool": ([P, i32, i64, P, i32, i32, i64, i64, P, i64, P], ctypes.c_int),
+        "msa_index_pool_mean": ([P, i32, i64, P, i32, i32, i64, i64, P, i64, P],
+                                ctypes.c_int),
         "msa_index_topk": ([P, i64, i64, P, i64, i32, i32, i32, P, P], ctypes.c_int),
+        "msa_index_topk_window": ([P, i64, i64, P, i64, i32, i32, i32, i32, P, P],
+                                  ctypes.c_int),
+        "msa_index_topk_decode_window": ([P, i32, P, P, i64, i32, i32, i32, i32, P, P, sz,
+                                          P], ctypes.c_int),
         "msa_topk_decode_workspace_bytes": ([i32, i64, i32], sz),
         "msa_index_topk_decode": ([P, i32, P, P, i64, i32, i32, i32, P, P, sz, P],
                                   ctypes.c_int),
@@ -152,6 +159,31 @@ def msa_index_pool(idx_k: torch.Tensor, block: int, kmax: torch.Tensor | None = 
     return kmax
 
 
+def msa_index_pool_mean(idx_k: torch.Tensor, block: int, kmean: torch.Tensor | None = None,
+                        seq_len: torch.Tensor | None = None, blk_begin: int = 0,
+                        blk_end: int | None = None, nb_max: int | None = None):
+    """Block mean-pool of index keys (ablation summary); arguments and shapes
+    as :func:`msa_index_pool` (``blk_begin`` >= 0 or -1)."""
+    _dev(idx_k, "idx_k", torch.float32)
+    batched = idx_k.dim() == 3
+    n_seq = idx_k.shape[0] if batched else 1
+    L, d = idx_k.shape[-2], idx_k.shape[-1]
+    nb = -(-L // block)
+    nb_max = nb if nb_max is None else nb_max
+    if kmean is None:
+        shape = (n_seq, nb_max, d) if batched else (nb_max, d)
+        kmean = torch.empty(shape, dtype=torch.float32, device=idx_k.device)
+    _dev(kmean, "kmean", torch.float32)
+    if seq_len is not None:
+        _dev(seq_len, "seq_len", torch.int64)
+    if blk_end is None:
+        blk_end = nb
+    st = load().msa_index_pool_mean(_ptr(idx_k), n_seq, L, _ptr(seq_len), d, block,
+                                    blk_begin, blk_end, _ptr(kmean), nb_max, _stream(idx_k))
+    _check("msa_index_pool_mean", st)
+    return kmean
+
+
 def msa_index_topk(idx_q: torch.Tensor, kmax: torch.Tensor, block: int, topk: int,
                    q_pos0: int = 0, sel: torch.Tensor | None = None):
     """Prefill causal top-K: ``idx_q`` [n_q, d_idx] at positions q_pos0 + i,
@@ -165,6 +197,22 @@ def msa_index_topk(idx_q: torch.Tensor, kmax: torch.Tensor, block: int, topk: in
     st = load().msa_index_topk(_ptr(idx_q), n_q, q_pos0, _ptr(kmax), kmax.shape[0],
                                d, block, topk, _ptr(sel), _stream(idx_q))
     _check("msa_index_topk", st)
+    return sel
+
+
+def msa_index_topk_window(idx_q: torch.Tensor, kmax: torch.Tensor, block: int, topk: int,
+                          window: int, q_pos0: int = 0, sel: torch.Tensor | None = None):
+    """Prefill top-K with a forced local window of ``window`` blocks ending at
+    the own block; the other ``topk - window`` are chosen by score."""
+    _dev(idx_q, "idx_q", torch.float32)
+    _dev(kmax, "kmax", torch.float32)
+    n_q, d = idx_q.shape
+    if sel is None:
+        sel = torch.empty((n_q, topk), dtype=torch.int32, device=idx_q.device)
+    _dev(sel, "sel", torch.int32)
+    st = load().msa_index_topk_window(_ptr(idx_q), n_q, q_pos0, _ptr(kmax), kmax.shape[0],
+                                      d, block, topk, window, _ptr(sel), _stream(idx_q))
+    _check("msa_index_topk_window", st)
     return sel
 
 
@@ -187,6 +235,29 @@ def msa_index_topk_decode(idx_q: torch.Tensor, seq_len: torch.Tensor,
                                    nb_max, d, block, topk, _ptr(sel), _ptr(ws),
                                    ws.numel(), _stream(idx_q))
     _check("msa_index_topk_decode", st)
+    return sel
+
+
+def msa_index_topk_decode_window(idx_q: torch.Tensor, seq_len: torch.Tensor,
+                                 kmax: torch.Tensor, block: int, topk: int, window: int,
+                                 sel: torch.Tensor | None = None,
+                                 ws: torch.Tensor | None = None):
+    """Decode top-K with the forced local window of
+    :func:`msa_index_topk_window`."""
+    _dev(idx_q, "idx_q", torch.float32)
+    _dev(seq_len, "seq_len", torch.int64)
+    _dev(kmax, "kmax", torch.float32)
+    n_seq, d = idx_q.shape
+    nb_max = kmax.shape[1]
+    lib = load()
+    ws = _ws(lib.msa_topk_decode_workspace_bytes(n_seq, nb_max, topk), idx_q, ws)
+    if sel is None:
+        sel = torch.empty((n_seq, topk), dtype=torch.int32, device=idx_q.device)
+    _dev(sel, "sel", torch.int32)
+    st = lib.msa_index_topk_decode_window(_ptr(idx_q), n_seq, _ptr(seq_len), _ptr(kmax),
+                                          nb_max, d, block, topk, window, _ptr(sel),
+                                          _ptr(ws), ws.numel(), _stream(idx_q))
+    _check("msa_index_topk_decode_window", st)
     return sel
 
 

@@ -90,6 +90,26 @@ int msa_index_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
                    int64_t nb_max, void *stream);
 
 /* --------------------------------------------------------------------------
+ * msa_index_pool_mean -- block mean-pool of index keys, a variant of the
+ * summary for ablations: [CXT] section 3.3's sketch summarises a key block
+ * by the mean over its tokens (instead of the max-pool the index branch of
+ * [YLY] uses).
+ *
+ *   kmean[s][b][c] = (sum over t in [b*B, min(b*B+B, len_s)) of
+ *                     idx_k[s][t][c]) / (number of those t)
+ *
+ * summed in fp32 in a fixed order (so the result is deterministic but, unlike
+ * the max, carries rounding: within (n+1) * 2^-24 * sum|x| / n of the exact
+ * mean for a block of n tokens).  Arguments as msa_index_pool, except that
+ * only the range form (blk_begin >= 0) and the last-block form
+ * (blk_begin == -1) exist; blk_begin == -2 returns MSA_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------ */
+int msa_index_pool_mean(const float *idx_k, int32_t n_seq, int64_t len_max,
+                        const int64_t *seq_len, int32_t d_idx, int32_t block,
+                        int64_t blk_begin, int64_t blk_end, float *kmean,
+                        int64_t nb_max, void *stream);
+
+/* --------------------------------------------------------------------------
  * msa_index_topk -- prefill scores and causal top-K for one sequence.
  * [YLY] "索引分支（Index Branch）"; [CXT] section 3.3 "Prefilling 与 Decoding
  * 的差异化优化" (prefill scores every block for every query).
@@ -106,6 +126,20 @@ int msa_index_pool(const float *idx_k, int32_t n_seq, int64_t len_max,
 int msa_index_topk(const float *idx_q, int64_t n_q, int64_t q_pos0,
                    const float *kmax, int64_t nb, int32_t d_idx, int32_t block,
                    int32_t topk, int32_t *sel, void *stream);
+
+/* --------------------------------------------------------------------------
+ * msa_index_topk_window -- the same selection with a forced local window of
+ * `window` blocks, after [CXT] section 3.3's sketch, which always keeps the
+ * blocks nearest the query besides the top-scored ones.  For query p with
+ * own = p / B the blocks max(0, own-window+1) .. own are forced; the
+ * candidates are the blocks below them, of which the best K - window are kept
+ * by (score desc, block asc).  The row is ascending and -1 padded as before;
+ * window = 1 is msa_index_topk.  Requires 1 <= window <= K
+ * (else MSA_ERR_INVALID_ARG).
+ * ------------------------------------------------------------------------ */
+int msa_index_topk_window(const float *idx_q, int64_t n_q, int64_t q_pos0,
+                          const float *kmax, int64_t nb, int32_t d_idx, int32_t block,
+                          int32_t topk, int32_t window, int32_t *sel, void *stream);
 
 /* --------------------------------------------------------------------------
  * msa_index_topk_decode -- the same selection for one new query per
@@ -125,6 +159,13 @@ int msa_index_topk_decode(const float *idx_q, int32_t n_seq,
                           int64_t nb_max, int32_t d_idx, int32_t block,
                           int32_t topk, int32_t *sel, void *ws,
                           size_t ws_bytes, void *stream);
+/* The decode selection with the local window of msa_index_topk_window
+ * (window = 1 is msa_index_topk_decode); same workspace. */
+int msa_index_topk_decode_window(const float *idx_q, int32_t n_seq,
+                                 const int64_t *seq_len, const float *kmax,
+                                 int64_t nb_max, int32_t d_idx, int32_t block,
+                                 int32_t topk, int32_t window, int32_t *sel, void *ws,
+                                 size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
  * msa_invert_selection -- the queries that hit each KV block, as CSR.

@@ -52,7 +52,10 @@ def _load():
         i64, i32, f64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_pool.argtypes = [P, i64, i32, i32, P]
+        lib.oracle_pool_mean.argtypes = [P, i64, i32, i32, P]
         lib.oracle_select.argtypes = [P, i64, P, P, i64, i32, i32, i32, P, P, P, P]
+        lib.oracle_select_window.argtypes = [P, i64, P, P, i64, i32, i32, i32, i32, P, P,
+                                             P, P]
         lib.oracle_invert.argtypes = [P, i64, i32, i64, P, P, P]
         lib.oracle_invert.restype = ctypes.c_int64
         lib.oracle_attend.argtypes = [P, P, P, i32, i64, P, P, P, i32, i32, i32,
@@ -87,13 +90,30 @@ def pool(idx_k: np.ndarray, block: int) -> np.ndarray:
     return out
 
 
+def pool_mean(idx_k: np.ndarray, block: int) -> np.ndarray:
+    """Block mean-pool of index keys (the block summary of CXT §3.3's sketch).
+
+    ``idx_k`` [L, d_idx] fp32 -> ``kmean`` [ceil(L/B), d_idx] fp32: the mean
+    over the valid tokens of each block, summed in fp64, rounded once.
+    """
+    idx_k = np.ascontiguousarray(idx_k, dtype=np.float32)
+    L, d = idx_k.shape
+    out = np.empty(((L + block - 1) // block, d), np.float32)
+    rc = _load().oracle_pool_mean(_ptr(idx_k), L, d, block, _ptr(out))
+    if rc:
+        raise ValueError("oracle_pool_mean: invalid arguments")
+    return out
+
+
 def select(idx_q: np.ndarray, q_pos: np.ndarray, kmax: np.ndarray, block: int,
-           topk: int):
+           topk: int, window: int = 1):
     """Causal top-K per query [YLY, "索引分支（Index Branch）"; CXT §3.3].
 
     Returns ``(sel [n_q, K] int32, gap_rel, gap_abs, err_bound)``: ``sel`` is
     ascending and -1 padded; the gap arrays describe the cut between the last
     kept and the first left-out candidate (NaN when nothing is left out).
+    ``window`` > 1 forces the blocks own-window+1 .. own (the local window of
+    CXT §3.3's sketch) and ranks only the blocks below them.
     """
     idx_q = np.ascontiguousarray(idx_q, dtype=np.float32)
     kmax = np.ascontiguousarray(kmax, dtype=np.float32)
@@ -104,9 +124,9 @@ def select(idx_q: np.ndarray, q_pos: np.ndarray, kmax: np.ndarray, block: int,
     gr = np.empty(n_q, np.float64)
     ga = np.empty(n_q, np.float64)
     eb = np.empty(n_q, np.float64)
-    rc = _load().oracle_select(_ptr(idx_q), n_q, _ptr(q_pos), _ptr(kmax),
-                               kmax.shape[0], d, block, topk, _ptr(sel),
-                               _ptr(gr), _ptr(ga), _ptr(eb))
+    rc = _load().oracle_select_window(_ptr(idx_q), n_q, _ptr(q_pos), _ptr(kmax),
+                                      kmax.shape[0], d, block, topk, window, _ptr(sel),
+                                      _ptr(gr), _ptr(ga), _ptr(eb))
     if rc:
         raise ValueError("oracle_select: invalid arguments")
     return sel, gr, ga, eb

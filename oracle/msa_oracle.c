@@ -95,6 +95,27 @@ int oracle_pool(const float *idx_k, int64_t len, int32_t d_idx, int32_t block,
 }
 
 /* ------------------------------------------------------------------------
+ * Block mean-pool of index keys: the block summary of [CXT §3.3]'s sketch
+ * (the mean of the block's keys), an alternative to the max-pool above.
+ * kmean[b][c] = (sum over the valid tokens t of block b of idx_k[t][c]) / n_b,
+ * summed in fp64 and rounded to fp32 once.
+ * ---------------------------------------------------------------------- */
+int oracle_pool_mean(const float *idx_k, int64_t len, int32_t d_idx, int32_t block,
+                     float *kmean) {
+  if (!idx_k || !kmean || len < 1 || d_idx < 1 || block < 1) return ORC_EINVAL;
+  int64_t nb = (len + block - 1) / block;
+  for (int64_t b = 0; b < nb; ++b) {
+    int64_t t0 = b * block, t1 = t0 + block < len ? t0 + block : len;
+    for (int32_t c = 0; c < d_idx; ++c) {
+      double acc = 0.0;
+      for (int64_t t = t0; t < t1; ++t) acc += (double)idx_k[t * d_idx + c];
+      kmean[b * d_idx + c] = (float)(acc / (double)(t1 - t0));
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
  * Index branch, steps 2-3: scores and causal top-K.
  * [YLY, "索引分支（Index Branch）"] single-head key, block max-pool, keep the
  * Top-K blocks; [CXT §3.3 "Prefilling 与 Decoding 的差异化优化"] prefill scores
@@ -112,6 +133,13 @@ int oracle_pool(const float *idx_k, int64_t len, int32_t d_idx, int32_t block,
  *              the two dot products in any summation order.
  *   All three are NaN when there is no cut.
  * kmax: [nb_avail][d_idx]; own must be < nb_avail.
+ *
+ * Local-window variant (oracle_select_window, after the sliding window that
+ * [CXT §3.3]'s sketch always keeps): the blocks max(0, own-window+1) .. own
+ * are forced, the candidates are the blocks below them, and the first
+ * min(K-window, #candidates) by the same ranking are kept; the near-tie
+ * report then concerns ranks K-window and K-window+1.  window = 1 is the
+ * rule above.
  * ---------------------------------------------------------------------- */
 typedef struct {
   double s;
@@ -130,12 +158,12 @@ static int int_cmp(const void *x, const void *y) {
   return (a > b) - (a < b);
 }
 
-int oracle_select(const float *idx_q, int64_t n_q, const int64_t *q_pos,
-                  const float *kmax, int64_t nb_avail, int32_t d_idx,
-                  int32_t block, int32_t topk, int32_t *sel, double *gap_rel,
-                  double *gap_abs, double *err_bnd) {
+int oracle_select_window(const float *idx_q, int64_t n_q, const int64_t *q_pos,
+                         const float *kmax, int64_t nb_avail, int32_t d_idx,
+                         int32_t block, int32_t topk, int32_t window, int32_t *sel,
+                         double *gap_rel, double *gap_abs, double *err_bnd) {
   if (!idx_q || !q_pos || !kmax || !sel || n_q < 0 || d_idx < 1 || block < 1 ||
-      topk < 1)
+      topk < 1 || window < 1 || window > topk)
     return ORC_EINVAL;
   for (int64_t i = 0; i < n_q; ++i)
     if (q_pos[i] < 0 || q_pos[i] / block >= nb_avail) return ORC_EINVAL;
@@ -155,24 +183,28 @@ int oracle_select(const float *idx_q, int64_t n_q, const int64_t *q_pos,
       if (!c || !keep) continue;
       const float *q = idx_q + i * d_idx;
       int64_t own = q_pos[i] / block;
-      for (int64_t b = 0; b < own; ++b) {
+      int64_t first = own - window + 1 > 0 ? own - window + 1 : 0;  /* forced: first..own */
+      int64_t n_cand = first;                                        /* blocks below them */
+      int64_t picks = topk - window;
+      for (int64_t b = 0; b < n_cand; ++b) {
         double s = 0.0;
         for (int32_t cc = 0; cc < d_idx; ++cc)
           s += (double)q[cc] * (double)kmax[b * d_idx + cc];
         c[b].s = s;
         c[b].b = (int32_t)b;
       }
-      qsort(c, (size_t)own, sizeof(cand_t), cand_cmp);
-      int64_t m = own < topk - 1 ? own : topk - 1;
+      qsort(c, (size_t)n_cand, sizeof(cand_t), cand_cmp);
+      int64_t m = n_cand < picks ? n_cand : picks;
       for (int64_t j = 0; j < m; ++j) keep[j] = c[j].b;
       qsort(keep, (size_t)m, sizeof(int32_t), int_cmp);
       int32_t *row = sel + i * topk;
-      for (int64_t j = 0; j < m; ++j) row[j] = keep[j];
-      row[m] = (int32_t)own;
-      for (int64_t j = m + 1; j < topk; ++j) row[j] = -1;
+      int64_t w = 0;
+      for (int64_t j = 0; j < m; ++j) row[w++] = keep[j];
+      for (int64_t b = first; b <= own; ++b) row[w++] = (int32_t)b;
+      for (; w < topk; ++w) row[w] = -1;
       double gr = NAN, ga = NAN, eb = NAN;
-      if (topk >= 2 && own > topk - 1) {
-        const cand_t *a = &c[topk - 2], *z = &c[topk - 1];
+      if (picks >= 1 && n_cand > picks) {
+        const cand_t *a = &c[picks - 1], *z = &c[picks];
         ga = a->s - z->s;
         double den = fabs(a->s) > fabs(z->s) ? fabs(a->s) : fabs(z->s);
         gr = den > 0.0 ? ga / den : 0.0;
@@ -191,6 +223,14 @@ int oracle_select(const float *idx_q, int64_t n_q, const int64_t *q_pos,
     free(keep);
   }
   return bad ? ORC_EINVAL : ORC_OK;
+}
+
+int oracle_select(const float *idx_q, int64_t n_q, const int64_t *q_pos,
+                  const float *kmax, int64_t nb_avail, int32_t d_idx,
+                  int32_t block, int32_t topk, int32_t *sel, double *gap_rel,
+                  double *gap_abs, double *err_bnd) {
+  return oracle_select_window(idx_q, n_q, q_pos, kmax, nb_avail, d_idx, block, topk, 1,
+                              sel, gap_rel, gap_abs, err_bnd);
 }
 
 /* ------------------------------------------------------------------------

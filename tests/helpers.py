@@ -25,8 +25,10 @@ def flagged(gap_rel, gap_abs, err_bnd):
 
 
 def check_selection(dev_sel, orc_sel, gap_rel, gap_abs, err_bnd, idx_q, kmax,
-                    q_pos, block):
-    """Assert the acceptance rule; return (n_flagged, n_mismatch)."""
+                    q_pos, block, window=1):
+    """Assert the acceptance rule; return (n_flagged, n_mismatch).  With a
+    local window the forced blocks are own-window+1 .. own and only the
+    blocks below them are ranked."""
     dev_sel = np.asarray(dev_sel)
     orc_sel = np.asarray(orc_sel)
     assert dev_sel.shape == orc_sel.shape
@@ -39,13 +41,16 @@ def check_selection(dev_sel, orc_sel, gap_rel, gap_abs, err_bnd, idx_q, kmax,
     K = dev_sel.shape[1]
     for r in np.nonzero(diff)[0]:
         own = int(q_pos[r]) // block
-        n = min(K, own + 1)
+        first = max(0, own - window + 1)
+        n_cand = min(K - window, first)
+        n = n_cand + own - first + 1
         row = dev_sel[r]
-        assert np.all(row[n:] == -1) and row[n - 1] == own
+        assert np.all(row[n:] == -1)
+        assert row[n_cand:n].tolist() == list(range(first, own + 1))
         assert np.all(np.diff(row[:n]) > 0) and row[0] >= 0
-        s = kmax[:own].astype(np.float64) @ idx_q[r].astype(np.float64)
-        kept = set(row[:n - 1].tolist())
-        left = [b for b in range(own) if b not in kept]
+        s = kmax[:first].astype(np.float64) @ idx_q[r].astype(np.float64)
+        kept = set(row[:n_cand].tolist())
+        left = [b for b in range(first) if b not in kept]
         if kept and left:
             margin = max(REL_TIE * np.max(np.abs(s)), 2 * float(err_bnd[r]))
             assert min(s[list(kept)]) >= max(s[left]) - margin

@@ -120,3 +120,19 @@ def test_decode_validation(lib):
     assert f(P, P, P, 1, 4, 1000, None, 64, 8, 128, 512, P, 8, 0.1, P, None, P, need, None) == EINVAL
     assert f(P, P, P, 1, 4, 1000, P, 64, 8, 96, 512, P, 8, 0.1, P, None, P, need, None) == EUNSUP
     assert f(P, P, P, 0, 4, 1000, P, 64, 8, 256, 512, P, 8, 0.1, P, None, P, need, None) == EUNSUP
+
+
+def test_index_variant_validation(lib):
+    P = FAKE
+    f = lib.msa_index_topk_window
+    assert f(P, 10, 0, P, 1, 64, 64, 4, 0, P, None) == EINVAL       # window 0
+    assert f(P, 10, 0, P, 1, 64, 64, 4, 5, P, None) == EINVAL       # window > K
+    assert f(P, 0, 0, P, 1, 64, 64, 4, 4, P, None) == OK            # empty: no-op
+    g = lib.msa_index_topk_decode_window
+    need = lib.msa_topk_decode_workspace_bytes(2, 100, 8)
+    assert g(P, 2, P, P, 100, 64, 64, 8, 9, P, P, need, None) == EINVAL
+    assert g(P, 2, P, P, 100, 64, 64, 8, 2, P, P, need - 1, None) == EWS
+    m = lib.msa_index_pool_mean
+    assert m(P, 1, 100, None, 64, 64, -2, 0, P, 2, None) == EINVAL   # no append form
+    assert m(P, 1, 100, None, 64, 60, 0, 2, P, 2, None) == EINVAL    # B % 16
+    assert m(None, 1, 100, None, 64, 64, 0, 2, P, 2, None) == EINVAL
