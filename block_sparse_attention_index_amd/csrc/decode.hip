@@ -581,6 +581,641 @@ __global__ __launch_bounds__(256) void decode_stream(
 }
 
 // ---------------------------------------------------------------------------
+// Paged KV cache, bf16 or FP8 (e4m3) keys and values: the decode attention of
+// decode_stream over a page pool.  A page holds one MSA block of one KV head
+// ([n_pages][Hkv][B][d]); logical block b of sequence s lives in page
+// block_table[s][b].  FP8 pages carry one scale per (page, KV head) for K and
+// one for V: k = k_scale * e4m3(k_page), likewise v.  The units, the chunk
+// stream and the partial records are those of decode_stream (non-fused); a
+// unit never leaves its block, so its two scales are constants: the scores
+// are scaled once (folded into the softmax scale) and the partial output
+// once at the unit's end.
+//
+// decode_paged is the bf16 kernel (decode_stream's double-buffered chunk
+// stream with page addressing); decode_paged_fp8 below the FP8 one.
+// ---------------------------------------------------------------------------
+template <bool FP8>
+struct PagedBuf;
+template <>
+struct PagedBuf<false> {
+  uint16_t Ks[kSK * 128];
+  uint16_t Vs[kSK * 128];
+};
+template <>
+struct PagedBuf<true> {
+  uint8_t Ks[kSK * 128];
+  uint8_t Vs[kSK * 128];
+};
+
+struct PagedUnit {
+  int s, g;
+  int64_t row0;    // element offset of the unit's first key row in the page pool
+  int nk;          // keys in the unit (0: empty)
+  float ks, vs;    // the page's K and V scales (1 for bf16)
+};
+
+// 8 e4m3 bytes -> 8 bf16 (exact: every e4m3 value is a bf16 value)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return u32x4{
+      __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false)),
+      __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true)),
+      __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false)),
+      __builtin_bit_cast(uint32_t, (bf16x2_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true))};
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void decode_paged(
+    const uint16_t *__restrict__ q, const uint8_t *__restrict__ kpool,
+    const uint8_t *__restrict__ vpool, const float *__restrict__ k_scale,
+    const float *__restrict__ v_scale, const int32_t *__restrict__ block_table,
+    int max_blocks, int64_t n_pages, const int64_t *__restrict__ seq_len, int hq, int hkv,
+    int B, const int32_t *__restrict__ sel, int topk, int nseg, int seg_len, uint32_t u_q,
+    uint32_t u_r, float scale_log2, float *__restrict__ part_o,
+    float *__restrict__ part_lse) {
+  constexpr int D = 128;
+  constexpr int RB = D * 2;                       // bytes per row
+  constexpr int SPR = RB / 16;                    // 16-byte slots per row
+  constexpr int IPW = (kSK * SPR) / 256;          // DMA instructions per wave per tensor
+  constexpr int QE = G * D < 512 ? 512 : G * D;   // staged query elements
+  __shared__ PagedBuf<false> sb0;
+  __shared__ PagedBuf<false> sb1;
+  __shared__ uint16_t qs[QE];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, j = lane & 31;
+  const int64_t len_max = (int64_t)max_blocks * B;
+
+  const uint32_t bx = blockIdx.x;
+  const uint32_t u_begin = bx * u_q + (bx < u_r ? bx : u_r);
+  const uint32_t u_end = u_begin + u_q + (bx < u_r ? 1u : 0u);
+
+  auto unit = [&](uint32_t u) __attribute__((always_inline)) {
+    PagedUnit d;
+    const uint32_t r1 = u / (uint32_t)nseg;
+    const int seg = (int)(u - r1 * (uint32_t)nseg);
+    const uint32_t r2 = r1 / (uint32_t)topk;
+    const int kk = (int)(r1 - r2 * (uint32_t)topk);
+    const uint32_t r3 = r2 / (uint32_t)hkv;
+    d.g = (int)(r2 - r3 * (uint32_t)hkv);
+    d.s = (int)r3;
+    int64_t len = seq_len[d.s];
+    if (len > len_max) len = len_max;
+    const int32_t b = sel[(int64_t)d.s * topk + kk];
+    const int32_t page =
+        (b >= 0 && b < max_blocks) ? block_table[(int64_t)d.s * max_blocks + b] : -1;
+    const int64_t t0 = (int64_t)b * B + (int64_t)seg * seg_len;
+    int64_t n = (page < 0 || page >= n_pages || len < 1) ? 0 : len - t0;   // keys t0 .. len-1
+    if (n > seg_len) n = seg_len;
+    if (n > (int64_t)B - (int64_t)seg * seg_len) n = (int64_t)B - (int64_t)seg * seg_len;
+    d.nk = n > 0 ? (int)n : 0;
+    d.row0 = d.nk > 0 ? ((int64_t)page * hkv + d.g) * B + (int64_t)seg * seg_len : 0;
+    d.ks = 1.f;
+    d.vs = 1.f;
+    return d;
+  };
+  auto next_unit = [&](uint32_t u, PagedUnit &d) __attribute__((always_inline)) {
+    for (; u < u_end; ++u) {
+      d = unit(u);
+      if (d.nk > 0) break;
+      for (int x = tid; x < G * D; x += 256) part_o[(size_t)u * G * D + x] = 0.f;
+      if (tid < G) part_lse[(size_t)u * G + tid] = -INFINITY;
+    }
+    return u;
+  };
+  // K and V rows with decode_stream's swizzles
+  auto dma_kv = [&](PagedBuf<false> &buf, const PagedUnit &d, int64_t row, int nrows)
+      __attribute__((always_inline)) {
+    const uint8_t *kb = kpool + (d.row0 + row) * RB;
+    const uint8_t *vb = vpool + (d.row0 + row) * RB;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int inst = wave * IPW + i;
+      const int pslot = inst * 64 + lane;
+      const int r = pslot / SPR, sp = pslot % SPR;
+      const int64_t rr = r < nrows ? r : nrows - 1;   // rows past the end repeat the last
+      const int ksl = dkswz(r, sp);
+      const int vsl = dvswz(r, sp);
+      __builtin_amdgcn_global_load_lds(
+          (dec_gptr_t)(const_cast<uint8_t *>(kb + rr * RB + ksl * 16)),
+          (dec_lptr_t)(reinterpret_cast<uint8_t *>(buf.Ks) + inst * 64 * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (dec_gptr_t)(const_cast<uint8_t *>(vb + rr * RB + vsl * 16)),
+          (dec_lptr_t)(reinterpret_cast<uint8_t *>(buf.Vs) + inst * 64 * 16), 16, 0, 0);
+    }
+  };
+  auto dma_q = [&](const PagedUnit &d) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const uint16_t *qb = q + ((int64_t)d.s * hq + (int64_t)d.g * G) * D;
+#pragma unroll
+      for (int i = 0; i < QE / 512; ++i) {
+        const int off = (i * 512 + lane * 8) % (G * D);
+        __builtin_amdgcn_global_load_lds((dec_gptr_t)(const_cast<uint16_t *>(qb + off)),
+                                         (dec_lptr_t)(&qs[i * 512]), 16, 0, 0);
+      }
+    }
+  };
+  auto kv_rows = [&](int n) __attribute__((always_inline)) { return n < kSK ? n : kSK; };
+
+  PagedUnit cu;
+  uint32_t u = next_unit(u_begin, cu);
+  if (u >= u_end) return;
+  PagedUnit nu = cu;
+  uint32_t un = next_unit(u + 1, nu);
+  dma_q(cu);
+  dma_kv(sb0, cu, 0, kv_rows(cu.nk));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  int voff[4];
+  {
+    const int a16 = lane & 15;
+    const int vrow = wave * 32 + 4 * h + (a16 >> 2);
+    const int vcol0 = 16 * (j >> 4) + 4 * (a16 & 3);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int col = cb * 32 + vcol0;
+      voff[cb] = (vrow * D + dvswz(vrow, col >> 3) * 8 + (col & 7)) * 2;
+    }
+  }
+
+  bf16x8 qf[8];
+  f32x16 acc[4];
+  float m = -INFINITY, l = 0.f;
+  int ci = 0;
+
+  auto chunk = [&](auto tag) __attribute__((always_inline)) {
+    constexpr int P = decltype(tag)::value;
+    PagedBuf<false> &cur = P ? sb1 : sb0;
+    PagedBuf<false> &nxt = P ? sb0 : sb1;
+    const int kc0 = ci * kSK;
+    const int nk_c = kv_rows(cu.nk - kc0);
+    const bool last = kc0 + kSK >= cu.nk;
+    if (!last) {
+      dma_kv(nxt, cu, kc0 + kSK, kv_rows(cu.nk - kc0 - kSK));
+    } else if (un < u_end) {
+      if (ci == 0) __syncthreads();   // every wave has read this unit's queries
+      dma_q(nu);
+      dma_kv(nxt, nu, 0, kv_rows(nu.nk));
+    }
+    const int k0 = wave * 32;
+    if (k0 < nk_c) {
+      f32x16 sacc;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sacc[rr] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const int kr = k0 + j;
+        const u32x4 kraw =
+            *reinterpret_cast<const u32x4 *>(&cur.Ks[kr * D + dkswz(kr, cc * 2 + h) * 8]);
+        sacc = mfma32(as_bf16x8(kraw), qf[cc], sacc);
+      }
+      const float sl = scale_log2 * cu.ks;
+      float x[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = k0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        x[rr] = key < nk_c ? sacc[rr] * sl : -INFINITY;
+      }
+      float mloc = x[0];
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, x[rr]);
+      const float mnew = fmaxf(m, max_with_partner(mloc));
+      const float alpha = fast_exp2(m - mnew);
+      f32x8 p0, p1;
+      float ps = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        p0[rr] = fast_exp2(x[rr] - mnew);
+        p1[rr] = fast_exp2(x[rr + 8] - mnew);
+        ps += p0[rr] + p1[rr];
+      }
+      l = fmaf(l, alpha, sum_with_partner(ps));
+      m = mnew;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+      const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
+      const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+      const char *vbase = reinterpret_cast<const char *>(cur.Vs);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          constexpr int kRow = D * 2;
+          const int o0 = voff[cb] + 16 * ks * kRow;
+          const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0));
+          const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0 + 8 * kRow));
+          const u32x4 vraw = {lo[0], lo[1], hi[0], hi[1]};
+          acc[cb] = mfma32(as_bf16x8(vraw), ks == 0 ? pb0 : pb1, acc[cb]);
+        }
+    }
+    if (last) {
+      __syncthreads();
+      // the waves' (o, m, l) through LDS, in the consumed chunk buffer
+      static_assert(4 * G * D * 4 + 8 * G * 4 <= (int)sizeof(PagedBuf<false>), "");
+      float *mo = reinterpret_cast<float *>(&cur);   // [4][G][D]
+      float *mm = mo + 4 * G * D;                    // [4][G]
+      float *ml = mm + 4 * G;                        // [4][G]
+      if (j < G) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg)
+            *reinterpret_cast<float4 *>(&mo[(wave * G + j) * D + cb * 32 + 8 * rg + 4 * h]) =
+                make_float4(acc[cb][4 * rg], acc[cb][4 * rg + 1], acc[cb][4 * rg + 2],
+                            acc[cb][4 * rg + 3]);
+        if (h == 0) {
+          mm[wave * G + j] = m;
+          ml[wave * G + j] = l;
+        }
+      }
+      __syncthreads();
+      for (int x = tid; x < G * D; x += 256) {
+        const int hd = x / D, c = x % D;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mm[w * G + hd]);
+        float z = 0.f, ov = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float sc = fast_exp2(mm[w * G + hd] - mx);
+          z = fmaf(sc, ml[w * G + hd], z);
+          ov = fmaf(sc, mo[(w * G + hd) * D + c], ov);
+        }
+        part_o[((size_t)u * G + hd) * D + c] = cu.vs * (ov / z);
+        if (c == 0) part_lse[(size_t)u * G + hd] = mx + __log2f(z);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  auto run_unit = [&](auto ptag) __attribute__((always_inline)) -> int {
+    constexpr int P0 = decltype(ptag)::value;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      u32x4 xq = *reinterpret_cast<const u32x4 *>(&qs[(j < G ? j : 0) * D + cc * 16 + 8 * h]);
+      if (j >= G) xq = u32x4{0u, 0u, 0u, 0u};
+      qf[cc] = as_bf16x8(xq);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
+    m = -INFINITY;
+    l = 0.f;
+    ci = 0;
+    int endp;
+    for (;;) {
+      chunk(std::integral_constant<int, P0>{});
+      if ((ci + 1) * kSK >= cu.nk) { endp = P0; break; }
+      ++ci;
+      chunk(std::integral_constant<int, 1 - P0>{});
+      if ((ci + 1) * kSK >= cu.nk) { endp = 1 - P0; break; }
+      ++ci;
+    }
+    if (un >= u_end) return -1;
+    u = un;
+    cu = nu;
+    un = next_unit(u + 1, nu);
+    return 1 - endp;
+  };
+
+  int par = 0;
+  for (;;) {
+    const int nx = par ? run_unit(std::integral_constant<int, 1>{})
+                       : run_unit(std::integral_constant<int, 0>{});
+    if (nx < 0) break;
+    par = nx;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 pages, three chunk buffers.  An FP8 chunk of 128 keys is half the bytes
+// of a bf16 one; three 32 KiB buffers keep two chunks in flight while the
+// third is computed.  K is widened to bf16 in registers as in decode_paged;
+// V^T operands come straight from the FP8 rows by ds_read_b64_tr_b8 (a
+// 16-lane group reads 8 keys x 16 columns and each lane receives its
+// column's 8 keys, exactly one bf16 MFMA operand after widening), so no
+// staging pass is needed.  The copies and
+// waits are written out (inline assembly) rather than left to the compiler,
+// which cannot always tell a copy into one buffer from reads of another and
+// then waits for every copy in flight: each wave waits until at most the
+// loads of chunk i+2 are outstanding (loads complete in order), then a
+// fence-free barrier publishes chunk i+1.  Units, scaling and partials as
+// decode_paged.
+// ---------------------------------------------------------------------------
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 *
+// lane (lds_base is wave-uniform and goes through M0).  No register receives
+// data, so nothing is live while the copy is in flight.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// LDS-visibility barrier without a memory fence: loads in flight stay so.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// LDS offset of a shared-memory object (its local address-space pointer).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(dec_lptr_t)(const_cast<void *>(p));
+}
+// Transposed 8-bit read: within each 16-lane group, lane i supplies the
+// address of 8 bytes (row i/2, half i%2 of a 16-byte column span) and
+// receives column i's bytes from the group's 8 rows.
+typedef int dec_i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) dec_i32x2 *dec_lds_i32x2_ptr;
+__device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t *p) {
+  const dec_i32x2 r =
+      __builtin_amdgcn_ds_read_tr8_b64_v2i32((dec_lds_i32x2_ptr)(const_cast<uint8_t *>(p)));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void decode_paged_fp8(
+    const uint16_t *__restrict__ q, const uint8_t *__restrict__ kpool,
+    const uint8_t *__restrict__ vpool, const float *__restrict__ k_scale,
+    const float *__restrict__ v_scale, const int32_t *__restrict__ block_table,
+    int max_blocks, int64_t n_pages, const int64_t *__restrict__ seq_len, int hq, int hkv,
+    int B, const int32_t *__restrict__ sel, int topk, int nseg, int seg_len, uint32_t u_q,
+    uint32_t u_r, float scale_log2, float *__restrict__ part_o,
+    float *__restrict__ part_lse) {
+  constexpr int D = 128;
+  constexpr int RB = D;                           // bytes per FP8 row
+  constexpr int SPR = RB / 16;                    // 16-byte slots per row
+  constexpr int IPW = (kSK * SPR) / 256;          // copy instructions per wave per tensor
+  constexpr int kChunkOps = 2 * IPW;              // loads per wave per chunk
+  constexpr int QE = G * D < 512 ? 512 : G * D;
+  static_assert(kChunkOps < 16, "vmcnt immediate");
+  static_assert(4 * G * D * 4 <= (int)sizeof(PagedBuf<true>), "combine fits a buffer");
+  __shared__ PagedBuf<true> sb0;
+  __shared__ PagedBuf<true> sb1;
+  __shared__ PagedBuf<true> sb2;
+  __shared__ uint16_t qs[QE];
+  __shared__ float mml[2 * 4 * G];   // the waves' (max, sum) at a unit's end
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, j = lane & 31;
+  const int64_t len_max = (int64_t)max_blocks * B;
+
+  const uint32_t bx = blockIdx.x;
+  const uint32_t u_begin = bx * u_q + (bx < u_r ? bx : u_r);
+  const uint32_t u_end = u_begin + u_q + (bx < u_r ? 1u : 0u);
+
+  auto unit = [&](uint32_t u) __attribute__((always_inline)) {
+    PagedUnit d;
+    const uint32_t r1 = u / (uint32_t)nseg;
+    const int seg = (int)(u - r1 * (uint32_t)nseg);
+    const uint32_t r2 = r1 / (uint32_t)topk;
+    const int kk = (int)(r1 - r2 * (uint32_t)topk);
+    const uint32_t r3 = r2 / (uint32_t)hkv;
+    d.g = (int)(r2 - r3 * (uint32_t)hkv);
+    d.s = (int)r3;
+    int64_t len = seq_len[d.s];
+    if (len > len_max) len = len_max;
+    const int32_t b = sel[(int64_t)d.s * topk + kk];
+    const int32_t page =
+        (b >= 0 && b < max_blocks) ? block_table[(int64_t)d.s * max_blocks + b] : -1;
+    const int64_t t0 = (int64_t)b * B + (int64_t)seg * seg_len;
+    int64_t n = (page < 0 || page >= n_pages || len < 1) ? 0 : len - t0;
+    if (n > seg_len) n = seg_len;
+    if (n > (int64_t)B - (int64_t)seg * seg_len) n = (int64_t)B - (int64_t)seg * seg_len;
+    d.nk = n > 0 ? (int)n : 0;
+    d.row0 = d.nk > 0 ? ((int64_t)page * hkv + d.g) * B + (int64_t)seg * seg_len : 0;
+    d.ks = d.nk > 0 ? k_scale[(int64_t)page * hkv + d.g] : 1.f;
+    d.vs = d.nk > 0 ? v_scale[(int64_t)page * hkv + d.g] : 1.f;
+    return d;
+  };
+  auto next_unit = [&](uint32_t u, PagedUnit &d, bool empties) __attribute__((always_inline)) {
+    for (; u < u_end; ++u) {
+      d = unit(u);
+      if (d.nk > 0) break;
+      if (empties) {
+        for (int x = tid; x < G * D; x += 256) part_o[(size_t)u * G * D + x] = 0.f;
+        if (tid < G) part_lse[(size_t)u * G + tid] = -INFINITY;
+      }
+    }
+    return u;
+  };
+  auto dma_kv = [&](PagedBuf<true> &buf, const PagedUnit &d, int64_t row, int nrows)
+      __attribute__((always_inline)) {
+    const uint8_t *kb = kpool + (d.row0 + row) * RB;
+    const uint8_t *vb = vpool + (d.row0 + row) * RB;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int inst = wave * IPW + i;
+      const int pslot = inst * 64 + lane;
+      const int r = pslot / SPR, sp = pslot % SPR;
+      const int64_t rr = r < nrows ? r : nrows - 1;
+      dma16(kb + rr * RB + (sp ^ (r & 7)) * 16, lds_addr(&buf.Ks[inst * 64 * 16]));
+      dma16(vb + rr * RB + (sp ^ (r & 7)) * 16, lds_addr(&buf.Vs[inst * 64 * 16]));
+    }
+  };
+  auto dma_q = [&](const PagedUnit &d) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const uint16_t *qb = q + ((int64_t)d.s * hq + (int64_t)d.g * G) * D;
+#pragma unroll
+      for (int i = 0; i < QE / 512; ++i) {
+        const int off = (i * 512 + lane * 8) % (G * D);
+        dma16(qb + off, lds_addr(&qs[i * 512]));
+      }
+    }
+  };
+  auto kv_rows = [&](int n) __attribute__((always_inline)) { return n < kSK ? n : kSK; };
+
+  // compute cursor (unit u, chunk ci) and the next non-empty unit
+  PagedUnit cu;
+  uint32_t u = next_unit(u_begin, cu, true);
+  if (u >= u_end) return;
+  PagedUnit nu = cu;
+  uint32_t un = next_unit(u + 1, nu, true);
+  // copy cursor, two chunks ahead
+  PagedUnit du = cu;
+  uint32_t ud = u;
+  int cd = 0;
+  auto dma_item = [&](PagedBuf<true> &buf) __attribute__((always_inline)) -> bool {
+    if (ud >= u_end) return false;
+    dma_kv(buf, du, (int64_t)cd * kSK, kv_rows(du.nk - cd * kSK));
+    if (++cd * kSK >= du.nk) {
+      ud = next_unit(ud + 1, du, false);
+      cd = 0;
+    }
+    return true;
+  };
+
+  dma_q(cu);
+  dma_item(sb0);
+  if (dma_item(sb1))
+    wait_vm<kChunkOps>();   // the queries and chunk 0 landed
+  else
+    wait_vm<0>();
+  lds_barrier();
+
+  // V^T operand offsets (bytes), per column block: lane a16 of a 16-lane
+  // group supplies the group's key a16/2 and the 8-byte half a16%2 of its 16
+  // columns; rows keep their 16-byte slots XOR-swizzled by row.  The 8 keys
+  // of a lane's operand follow the score tile's row order (keys 4h .. 4h+3
+  // and 8+4h .. 8+4h+3 of the 16-key step), which the probabilities share.
+  int voff[4];
+  {
+    const int a16 = lane & 15, ri = a16 >> 1;
+    const int vrow = wave * 32 + 8 * (ri >> 2) + 4 * h + (ri & 3);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int slot = 2 * cb + (j >> 4);
+      voff[cb] = vrow * RB + ((slot ^ (vrow & 7)) << 4) + ((a16 & 1) << 3);
+    }
+  }
+
+  bf16x8 qf[8];
+  f32x16 acc[4];
+  float m = -INFINITY, l = 0.f;
+  int ci = 0;
+
+  auto step = [&](auto tag) __attribute__((always_inline)) -> bool {
+    constexpr int P = decltype(tag)::value;
+    PagedBuf<true> &cur = P == 0 ? sb0 : (P == 1 ? sb1 : sb2);
+    PagedBuf<true> &far = P == 0 ? sb2 : (P == 1 ? sb0 : sb1);   // chunk i+2
+    if (ci == 0) {
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        u32x4 xq = *reinterpret_cast<const u32x4 *>(&qs[(j < G ? j : 0) * D + cc * 16 + 8 * h]);
+        if (j >= G) xq = u32x4{0u, 0u, 0u, 0u};
+        qf[cc] = as_bf16x8(xq);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
+      m = -INFINITY;
+      l = 0.f;
+      if (un < u_end) {
+        lds_barrier();   // every wave holds its queries: the staging area is free
+        dma_q(nu);
+      }
+    }
+    const bool has2 = dma_item(far);
+    const int kc0 = ci * kSK;
+    const int nk_c = kv_rows(cu.nk - kc0);
+    const bool last = kc0 + kSK >= cu.nk;
+    const int k0 = wave * 32;
+    if (k0 < nk_c) {
+      f32x16 sacc;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sacc[rr] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const int kr = k0 + j;
+        const u32x2 r8 = *reinterpret_cast<const u32x2 *>(
+            &cur.Ks[kr * RB + ((cc ^ (kr & 7)) * 16) + 8 * h]);
+        sacc = mfma32(as_bf16x8(fp8x8_to_bf16x8(r8[0], r8[1])), qf[cc], sacc);
+      }
+      const float sl = scale_log2 * cu.ks;
+      float x[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = k0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        x[rr] = key < nk_c ? sacc[rr] * sl : -INFINITY;
+      }
+      float mloc = x[0];
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, x[rr]);
+      const float mnew = fmaxf(m, max_with_partner(mloc));
+      const float alpha = fast_exp2(m - mnew);
+      f32x8 p0, p1;
+      float ps = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        p0[rr] = fast_exp2(x[rr] - mnew);
+        p1[rr] = fast_exp2(x[rr + 8] - mnew);
+        ps += p0[rr] + p1[rr];
+      }
+      l = fmaf(l, alpha, sum_with_partner(ps));
+      m = mnew;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+      const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
+      const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const u32x2 v8 = lds_read_tr8(&cur.Vs[voff[cb] + 16 * ks * RB]);
+          acc[cb] = mfma32(as_bf16x8(fp8x8_to_bf16x8(v8[0], v8[1])), ks == 0 ? pb0 : pb1,
+                           acc[cb]);
+        }
+    }
+    // chunk i+1 (and the next unit's queries, copied before chunk i+2) landed
+    if (has2)
+      wait_vm<kChunkOps>();
+    else
+      wait_vm<0>();
+    if (last) {
+      lds_barrier();
+      float *mo = reinterpret_cast<float *>(&cur);      // [4][G][D]
+      float *mm = mml;                                  // [4][G]
+      float *ml = mml + 4 * G;                          // [4][G]
+      if (j < G) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg)
+            *reinterpret_cast<float4 *>(&mo[(wave * G + j) * D + cb * 32 + 8 * rg + 4 * h]) =
+                make_float4(acc[cb][4 * rg], acc[cb][4 * rg + 1], acc[cb][4 * rg + 2],
+                            acc[cb][4 * rg + 3]);
+        if (h == 0) {
+          mm[wave * G + j] = m;
+          ml[wave * G + j] = l;
+        }
+      }
+      lds_barrier();
+      for (int x = tid; x < G * D; x += 256) {
+        const int hd = x / D, c = x % D;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mm[w * G + hd]);
+        float z = 0.f, ov = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float sc = fast_exp2(mm[w * G + hd] - mx);
+          z = fmaf(sc, ml[w * G + hd], z);
+          ov = fmaf(sc, mo[(w * G + hd) * D + c], ov);
+        }
+        part_o[((size_t)u * G + hd) * D + c] = cu.vs * (ov / z);
+        if (c == 0) part_lse[(size_t)u * G + hd] = mx + __log2f(z);
+      }
+    }
+    lds_barrier();   // chunk i+1 visible to every wave; buffer P reusable
+    if (!last) {
+      ++ci;
+      return true;
+    }
+    if (un >= u_end) return false;
+    u = un;
+    cu = nu;
+    un = next_unit(u + 1, nu, true);
+    ci = 0;
+    return true;
+  };
+
+  for (;;) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
+    if (!step(std::integral_constant<int, 2>{})) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge: one workgroup per (query head, sequence), one thread per column.
 // Online log-sum-exp over the np partials, branch-free so the loads of
 // consecutive partials can be in flight together.
@@ -814,6 +1449,73 @@ hipError_t launch_decode(const void *q, const void *k_cache,
   }
 #undef MSA_DARGS
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Paged (bf16 or FP8) decode: same workspace as launch_decode.
+// ---------------------------------------------------------------------------
+template <int G>
+void launch_paged_g(int32_t kv_dtype, const StreamPlan &pl, const uint16_t *q,
+                    const uint8_t *kp, const uint8_t *vp, const float *k_scale,
+                    const float *v_scale, const int32_t *block_table, int32_t max_blocks,
+                    int64_t n_pages, const int64_t *seq_len, int32_t hq, int32_t hkv,
+                    int32_t block, const int32_t *sel, int32_t topk, float scale,
+                    float *part_o, float *part_lse, hipStream_t st) {
+  if (kv_dtype == 2)
+    hipLaunchKernelGGL((decode_paged_fp8<G>), dim3(pl.grid), dim3(256), 0, st, q, kp, vp,
+                       k_scale, v_scale, block_table, max_blocks, n_pages, seq_len, hq, hkv,
+                       block, sel, topk, pl.nseg, pl.seg_len, pl.u_q, pl.u_r, scale * kLog2e,
+                       part_o, part_lse);
+  else
+    hipLaunchKernelGGL((decode_paged<G>), dim3(pl.grid), dim3(256), 0, st, q, kp, vp,
+                       k_scale, v_scale, block_table, max_blocks, n_pages, seq_len, hq, hkv,
+                       block, sel, topk, pl.nseg, pl.seg_len, pl.u_q, pl.u_r, scale * kLog2e,
+                       part_o, part_lse);
+}
+
+bool decode_paged_supported(int32_t kv_dtype, int32_t d, int32_t group) {
+  return (kv_dtype == 1 || kv_dtype == 2) && d == 128 &&
+         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+}
+
+hipError_t launch_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                               int32_t kv_dtype, const float *k_scale, const float *v_scale,
+                               int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                               int32_t n_seq, const int64_t *seq_len, int32_t hq, int32_t hkv,
+                               int32_t block, const int32_t *sel, int32_t topk, float scale,
+                               float *o, float *lse, void *ws, hipStream_t st) {
+  const int G = hq / hkv;
+  const int64_t np = dec_partials(n_seq, hq, block, topk);
+  char *w = static_cast<char *>(ws);
+  float *part_o = reinterpret_cast<float *>(w);
+  w += align256((size_t)np * 128 * 4);
+  float *part_lse = reinterpret_cast<float *>(w);
+  const StreamPlan pl = stream_plan(n_seq, hkv, block, topk);
+  const uint16_t *qq = static_cast<const uint16_t *>(q);
+  const uint8_t *kp = static_cast<const uint8_t *>(k_pages);
+  const uint8_t *vp = static_cast<const uint8_t *>(v_pages);
+  switch (G) {
+    case 1: launch_paged_g<1>(kv_dtype, pl, qq, kp, vp, k_scale, v_scale, block_table,
+                              max_blocks, n_pages, seq_len, hq, hkv, block, sel, topk, scale,
+                              part_o, part_lse, st); break;
+    case 2: launch_paged_g<2>(kv_dtype, pl, qq, kp, vp, k_scale, v_scale, block_table,
+                              max_blocks, n_pages, seq_len, hq, hkv, block, sel, topk, scale,
+                              part_o, part_lse, st); break;
+    case 4: launch_paged_g<4>(kv_dtype, pl, qq, kp, vp, k_scale, v_scale, block_table,
+                              max_blocks, n_pages, seq_len, hq, hkv, block, sel, topk, scale,
+                              part_o, part_lse, st); break;
+    case 8: launch_paged_g<8>(kv_dtype, pl, qq, kp, vp, k_scale, v_scale, block_table,
+                              max_blocks, n_pages, seq_len, hq, hkv, block, sel, topk, scale,
+                              part_o, part_lse, st); break;
+    case 16: launch_paged_g<16>(kv_dtype, pl, qq, kp, vp, k_scale, v_scale, block_table,
+                                max_blocks, n_pages, seq_len, hq, hkv, block, sel, topk, scale,
+                                part_o, part_lse, st); break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((decode_merge<128>), dim3(hq, n_seq), dim3(128), 0, st,
+                     topk * pl.nseg, G, hkv, part_o, part_lse, o, lse);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

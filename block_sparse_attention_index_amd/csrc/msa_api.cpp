@@ -262,6 +262,30 @@ int msa_sparse_gqa_decode(const void *q, const void *k_cache,
                                       as_stream(stream)));
 }
 
+int msa_sparse_gqa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                                int32_t kv_dtype, const float *k_scale,
+                                const float *v_scale, int64_t n_pages,
+                                const int32_t *block_table, int32_t max_blocks,
+                                int32_t n_seq, const int64_t *seq_len, int32_t hq,
+                                int32_t hkv, int32_t d, int32_t block,
+                                const int32_t *sel, int32_t topk, float scale, float *o,
+                                float *lse, void *ws, size_t ws_bytes, void *stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seq_len || !sel || !o || !ws ||
+      (kv_dtype == MSA_FP8_E4M3 && (!k_scale || !v_scale)) ||
+      (kv_dtype != MSA_BF16 && kv_dtype != MSA_FP8_E4M3) || n_pages < 1 ||
+      max_blocks < 1 || n_seq < 1 || n_seq > kMaxGridY || hq < 1 || hkv < 1 ||
+      hq % hkv != 0 || d < 1 || !block_ok(block) || !topk_ok(topk) ||
+      !std::isfinite(scale) || (int64_t)n_seq * hkv * topk > kMaxDecodeItems ||
+      (int64_t)n_pages * hkv * block > (int64_t(1) << 40))
+    return MSA_ERR_INVALID_ARG;
+  if (!msa::decode_paged_supported(kv_dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
+  if (ws_bytes < msa::decode_ws_bytes(n_seq, hq, d, block, topk)) return MSA_ERR_WORKSPACE;
+  return status_of(msa::launch_decode_paged(q, k_pages, v_pages, kv_dtype, k_scale, v_scale,
+                                            n_pages, block_table, max_blocks, n_seq, seq_len,
+                                            hq, hkv, block, sel, topk, scale, o, lse, ws,
+                                            as_stream(stream)));
+}
+
 size_t msa_decode_step_workspace_bytes(int32_t n_seq, int64_t nb_max, int32_t hq,
                                        int32_t d, int32_t block, int32_t topk) {
   if (n_seq < 1 || nb_max < 1 || hq < 1 || d < 1 || !block_ok(block) || !topk_ok(topk))

@@ -65,6 +65,13 @@ hipError_t launch_decode(const void *q, const void *k_cache,
                          const int32_t *sel, int32_t topk, float scale,
                          float *o, float *lse, void *ws, hipStream_t st);
 
+bool decode_paged_supported(int32_t kv_dtype, int32_t d, int32_t group);
+hipError_t launch_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                               int32_t kv_dtype, const float *k_scale, const float *v_scale,
+                               int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                               int32_t n_seq, const int64_t *seq_len, int32_t hq, int32_t hkv,
+                               int32_t block, const int32_t *sel, int32_t topk, float scale,
+                               float *o, float *lse, void *ws, hipStream_t st);
 size_t decode_step_ws_bytes(int32_t n_seq, int64_t nb_max, int32_t hq, int32_t d,
                             int32_t block, int32_t topk);
 bool decode_step_supported(int32_t dtype, int32_t d, int32_t group);

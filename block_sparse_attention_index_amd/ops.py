@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmsa.so")
 _lib = None
 
-MSA_F32, MSA_BF16 = 0, 1
+MSA_F32, MSA_BF16, MSA_FP8_E4M3 = 0, 1, 2
 _STATUS = {0: "MSA_OK", -1: "MSA_ERR_INVALID_ARG", -2: "MSA_ERR_UNSUPPORTED",
            -3: "MSA_ERR_WORKSPACE", -4: "MSA_ERR_HIP"}
 
@@ -31,6 +31,7 @@ ENTRY_POINTS = (
     "msa_decode_workspace_bytes", "msa_sparse_gqa_decode",
     "msa_decode_step_workspace_bytes", "msa_decode_step",
     "msa_index_pool_mean", "msa_index_topk_window", "msa_index_topk_decode_window",
+    "msa_sparse_gqa_decode_paged",
 )
 
 
@@ -76,6 +77,8 @@ def load():
         "msa_decode_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
         "msa_sparse_gqa_decode": ([P, P, P, i32, i32, i64, P, i32, i32, i32, i32, P,
                                    i32, f32, P, P, P, sz, P], ctypes.c_int),
+        "msa_sparse_gqa_decode_paged": ([P, P, P, i32, P, P, i64, P, i32, i32, P, i32, i32,
+                                         i32, i32, P, i32, f32, P, P, P, sz, P], ctypes.c_int),
         "msa_decode_step_workspace_bytes": ([i32, i64, i32, i32, i32, i32], sz),
         "msa_decode_step": ([P, P, P, P, P, P, P, P, P, i32, i32, i64, i64, P, i32, i32,
                              i32, i32, i32, i32, f32, P, P, P, P, sz, P], ctypes.c_int),
@@ -361,6 +364,49 @@ def msa_sparse_gqa_decode(q: torch.Tensor, k_cache: torch.Tensor,
     _check("msa_sparse_gqa_decode", st)
     return o, lse
 
+
+
+def msa_sparse_gqa_decode_paged(q, k_pages, v_pages, block_table, seq_len, sel, block: int,
+                                scale: float | None = None, k_scale=None, v_scale=None,
+                                o=None, lse=None, ws=None, want_lse: bool = True):
+    """Sparse GQA decode over a paged cache.  ``q`` [n_seq, Hq, d] bf16;
+    ``k_pages``/``v_pages`` [n_pages, Hkv, B, d] bf16 or float8_e4m3fn (then
+    ``k_scale``/``v_scale`` [n_pages, Hkv] fp32); ``block_table``
+    [n_seq, max_blocks] int32.  Returns ``(o, lse)`` as msa_sparse_gqa_decode."""
+    for t, nm in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _dev(t, nm)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_len, "seq_len", torch.int64)
+    _dev(sel, "sel", torch.int32)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q must be bf16")
+    if k_pages.dtype != v_pages.dtype:
+        raise ValueError("k_pages and v_pages must share a dtype")
+    if k_pages.dtype == torch.bfloat16:
+        kvd = MSA_BF16
+    elif k_pages.dtype == torch.float8_e4m3fn:
+        kvd = MSA_FP8_E4M3
+        _dev(k_scale, "k_scale", torch.float32)
+        _dev(v_scale, "v_scale", torch.float32)
+    else:
+        raise ValueError("pages must be bf16 or float8_e4m3fn")
+    n_seq, hq, d = q.shape
+    n_pages, hkv = k_pages.shape[0], k_pages.shape[1]
+    topk = sel.shape[1]
+    scale = d ** -0.5 if scale is None else scale
+    lib = load()
+    ws = _ws(lib.msa_decode_workspace_bytes(n_seq, hq, d, block, topk), q, ws)
+    if o is None:
+        o = torch.empty((n_seq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((n_seq, hq), dtype=torch.float32, device=q.device)
+    st = lib.msa_sparse_gqa_decode_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), kvd, _ptr(k_scale if kvd == MSA_FP8_E4M3 else None),
+        _ptr(v_scale if kvd == MSA_FP8_E4M3 else None), n_pages, _ptr(block_table),
+        block_table.shape[1], n_seq, _ptr(seq_len), hq, hkv, d, block, _ptr(sel), topk,
+        scale, _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(q))
+    _check("msa_sparse_gqa_decode_paged", st)
+    return o, lse
 
 def msa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                     idx_q: torch.Tensor, idx_k_new: torch.Tensor, k_cache: torch.Tensor,

@@ -56,7 +56,9 @@ typedef enum {
   MSA_ERR_HIP = -4          /* a HIP launch or runtime call failed         */
 } msa_status;
 
-typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1, MSA_FP8_E4M3 = 2 } msa_dtype;
+/* MSA_FP8_E4M3 (OCP e4m3: 4 exponent bits, bias 7, 3 mantissa bits, no
+ * infinities) is accepted only as the KV dtype of msa_sparse_gqa_decode_paged. */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *msa_status_string(int status);
@@ -252,6 +254,35 @@ int msa_sparse_gqa_decode(const void *q, const void *k_cache,
                           const int32_t *sel, int32_t topk, float scale,
                           float *o, float *lse, void *ws, size_t ws_bytes,
                           void *stream);
+
+/* --------------------------------------------------------------------------
+ * msa_sparse_gqa_decode_paged -- msa_sparse_gqa_decode over a paged KV cache,
+ * with bf16 or FP8 keys and values ([CXT] section 3.3's KV cache management:
+ * block-granular allocation, and KV kept in reduced precision).  A page holds
+ * one MSA block of one KV head:
+ *
+ *   k_pages, v_pages  [n_pages][Hkv][B][d], kv_dtype MSA_BF16 or MSA_FP8_E4M3
+ *   k_scale, v_scale  [n_pages][Hkv] fp32 (FP8 only; ignored for bf16):
+ *                     key row = k_scale[page][g] * e4m3 value, likewise v
+ *   block_table       [n_seq][max_blocks] int32: logical block b of sequence
+ *                     s (keys b*B .. b*B+B-1) lives in page block_table[s][b]
+ *   q                 [n_seq][Hq][d] bf16; seq_len, sel, o, lse, ws, scale as
+ *                     msa_sparse_gqa_decode (ws: msa_decode_workspace_bytes),
+ *                     with len_s <= max_blocks * B
+ * Only the table entries of selected blocks are read; an entry outside
+ * [0, n_pages) makes that block count as attending no keys (nothing outside
+ * the pool is read).  Dequantisation is exact up to fp32 rounding of the
+ * scaled scores and outputs (e4m3 values are exact in bf16).
+ * Supported: d = 128, Hq/Hkv in {1, 2, 4, 8, 16}; n_seq * Hkv * K <= 2^28.
+ * ------------------------------------------------------------------------ */
+int msa_sparse_gqa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                                int32_t kv_dtype, const float *k_scale,
+                                const float *v_scale, int64_t n_pages,
+                                const int32_t *block_table, int32_t max_blocks,
+                                int32_t n_seq, const int64_t *seq_len, int32_t hq,
+                                int32_t hkv, int32_t d, int32_t block,
+                                const int32_t *sel, int32_t topk, float scale, float *o,
+                                float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * msa_decode_step -- one generation step of the whole path, fused

@@ -136,3 +136,18 @@ def test_index_variant_validation(lib):
     assert m(P, 1, 100, None, 64, 64, -2, 0, P, 2, None) == EINVAL   # no append form
     assert m(P, 1, 100, None, 64, 60, 0, 2, P, 2, None) == EINVAL    # B % 16
     assert m(None, 1, 100, None, 64, 64, 0, 2, P, 2, None) == EINVAL
+
+
+def test_paged_decode_validation(lib):
+    P = FAKE
+    f = lib.msa_sparse_gqa_decode_paged
+    need = lib.msa_decode_workspace_bytes(4, 64, 128, 512, 8)
+    a = dict(q=P, kp=P, vp=P, dt=2, ks=P, vs=P, npg=100, bt=P, mb=10, n=4, sl=P, hq=64, hkv=8,
+             d=128, B=512, sel=P, K=8, sc=0.1, o=P, lse=None, ws=P, wsb=need)
+    call = lambda **kw: f(*dict(a, **kw).values(), None)
+    assert call(wsb=need - 1) == EWS
+    assert call(dt=0) == EINVAL                  # fp32 pages: no
+    assert call(ks=None) == EINVAL               # FP8 needs scales
+    assert call(npg=0) == EINVAL
+    assert call(d=64) == EUNSUP
+    assert call(hq=24) == EUNSUP                 # group 3
