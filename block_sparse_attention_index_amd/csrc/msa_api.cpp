@@ -5,6 +5,7 @@
 // unsupported shape is reported as MSA_ERR_UNSUPPORTED.
 #include "msa.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -228,6 +229,109 @@ int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
                                        hq, hkv, d, block, sel, topk, row_ptr,
                                        q_list, slot, scale, o, lse, ws,
                                        as_stream(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// Several sequences in one call: the prefill path per sequence, in order, on
+// one stream, sharing one workspace (stream order makes the reuse safe).
+// ---------------------------------------------------------------------------
+namespace {
+struct VarlenLayout {
+  size_t kmax, row_ptr, q_list, slot, inv, attn, total;
+};
+
+bool varlen_lens_ok(int32_t n_seq, const int64_t *cu_q, const int64_t *cu_kv) {
+  if (!cu_q || !cu_kv || n_seq < 1 || n_seq > kMaxGridY || cu_q[0] != 0 || cu_kv[0] != 0)
+    return false;
+  for (int32_t s = 0; s < n_seq; ++s) {
+    const int64_t qn = cu_q[s + 1] - cu_q[s], kvn = cu_kv[s + 1] - cu_kv[s];
+    if (qn < 0 || kvn < 0 || qn > kvn || qn * (int64_t)kMaxTopk >= INT32_MAX) return false;
+  }
+  return true;
+}
+
+VarlenLayout varlen_layout(int32_t dtype, int32_t n_seq, const int64_t *cu_q,
+                           const int64_t *cu_kv, int32_t hq, int32_t d, int32_t d_idx,
+                           int32_t block, int32_t topk) {
+  int64_t nb_max = 1, q_max = 1;
+  size_t inv = 0, attn = 0;
+  for (int32_t s = 0; s < n_seq; ++s) {
+    const int64_t qn = cu_q[s + 1] - cu_q[s], kvn = cu_kv[s + 1] - cu_kv[s];
+    if (qn == 0) continue;
+    const int64_t nb = cdiv(kvn, block);
+    nb_max = std::max(nb_max, nb);
+    q_max = std::max(q_max, qn);
+    inv = std::max(inv, msa::invert_ws_bytes(qn, topk, nb));
+    attn = std::max(attn, msa::prefill_ws_bytes(dtype, kvn - qn, qn, hq, d, block, topk));
+  }
+  auto a256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  VarlenLayout L;
+  size_t off = 0;
+  L.kmax = off;    off += a256((size_t)nb_max * d_idx * 4);
+  L.row_ptr = off; off += a256((size_t)(nb_max + 1) * 4);
+  L.q_list = off;  off += a256((size_t)q_max * topk * 4);
+  L.slot = off;    off += a256((size_t)q_max * topk * 4);
+  L.inv = off;     off += a256(std::max<size_t>(inv, 1));
+  L.attn = off;    off += a256(std::max<size_t>(attn, 1));
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t msa_prefill_varlen_workspace_bytes(int32_t dtype, int32_t n_seq, const int64_t *cu_q,
+                                          const int64_t *cu_kv, int32_t hq, int32_t d,
+                                          int32_t d_idx, int32_t block, int32_t topk) {
+  if ((dtype != MSA_F32 && dtype != MSA_BF16) || !varlen_lens_ok(n_seq, cu_q, cu_kv) ||
+      hq < 1 || d < 1 || !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk))
+    return 0;
+  return varlen_layout(dtype, n_seq, cu_q, cu_kv, hq, d, d_idx, block, topk).total;
+}
+
+int msa_prefill_varlen(const void *q, const void *k, const void *v, const float *idx_q,
+                       const float *idx_k, int32_t dtype, int32_t n_seq, const int64_t *cu_q,
+                       const int64_t *cu_kv, int32_t hq, int32_t hkv, int32_t d,
+                       int32_t d_idx, int32_t block, int32_t topk, float scale, int32_t *sel,
+                       float *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
+  if (!q || !k || !v || !idx_q || !idx_k || !sel || !o || !ws ||
+      (dtype != MSA_F32 && dtype != MSA_BF16) || !varlen_lens_ok(n_seq, cu_q, cu_kv) ||
+      hq < 1 || hkv < 1 || hkv > kMaxGridY || hq % hkv != 0 || d < 1 || !didx_ok(d_idx) ||
+      !block_ok(block) || !topk_ok(topk) || !std::isfinite(scale))
+    return MSA_ERR_INVALID_ARG;
+  if (!msa::prefill_supported(dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
+  const VarlenLayout L = varlen_layout(dtype, n_seq, cu_q, cu_kv, hq, d, d_idx, block, topk);
+  if (ws_bytes < L.total) return MSA_ERR_WORKSPACE;
+  char *w = static_cast<char *>(ws);
+  float *kmax = reinterpret_cast<float *>(w + L.kmax);
+  int32_t *row_ptr = reinterpret_cast<int32_t *>(w + L.row_ptr);
+  int32_t *q_list = reinterpret_cast<int32_t *>(w + L.q_list);
+  int32_t *slot = reinterpret_cast<int32_t *>(w + L.slot);
+  void *inv_ws = w + L.inv;
+  void *attn_ws = w + L.attn;
+  const hipStream_t st = as_stream(stream);
+  const int64_t es = dtype == MSA_BF16 ? 2 : 4;   // bytes per q/k/v element
+  const int64_t total_kv = cu_kv[n_seq];
+  for (int32_t s = 0; s < n_seq; ++s) {
+    const int64_t qn = cu_q[s + 1] - cu_q[s], kvn = cu_kv[s + 1] - cu_kv[s];
+    if (qn == 0) continue;
+    const int64_t q0 = kvn - qn, nb = cdiv(kvn, block);
+    const char *qs = static_cast<const char *>(q) + cu_q[s] * hq * d * es;
+    const char *ks = static_cast<const char *>(k) + cu_kv[s] * d * es;
+    const char *vs = static_cast<const char *>(v) + cu_kv[s] * d * es;
+    int32_t *sel_s = sel + cu_q[s] * topk;
+    hipError_t e = msa::launch_pool(idx_k + cu_kv[s] * d_idx, 1, kvn, nullptr, d_idx, block, 0,
+                                    nb, kmax, nb, st);
+    if (e == hipSuccess)
+      e = msa::launch_topk_prefill(idx_q + cu_q[s] * d_idx, qn, q0, kmax, nb, d_idx, block,
+                                   topk, 1, sel_s, st);
+    if (e == hipSuccess)
+      e = msa::launch_invert(sel_s, qn, topk, nb, row_ptr, q_list, slot, inv_ws, st);
+    if (e == hipSuccess)
+      e = msa::launch_prefill(qs, ks, vs, dtype, total_kv, q0, qn, hq, hkv, d, block, sel_s,
+                              topk, row_ptr, q_list, slot, scale, o + cu_q[s] * hq * d,
+                              lse ? lse + cu_q[s] * hq : nullptr, attn_ws, st);
+    if (e != hipSuccess) return MSA_ERR_HIP;
+  }
+  return MSA_OK;
 }
 
 size_t msa_decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t d,

@@ -31,7 +31,8 @@ ENTRY_POINTS = (
     "msa_decode_workspace_bytes", "msa_sparse_gqa_decode",
     "msa_decode_step_workspace_bytes", "msa_decode_step",
     "msa_index_pool_mean", "msa_index_topk_window", "msa_index_topk_decode_window",
-    "msa_sparse_gqa_decode_paged",
+    "msa_sparse_gqa_decode_paged", "msa_prefill_varlen_workspace_bytes",
+    "msa_prefill_varlen",
 )
 
 
@@ -79,6 +80,9 @@ def load():
                                    i32, f32, P, P, P, sz, P], ctypes.c_int),
         "msa_sparse_gqa_decode_paged": ([P, P, P, i32, P, P, i64, P, i32, i32, P, i32, i32,
                                          i32, i32, P, i32, f32, P, P, P, sz, P], ctypes.c_int),
+        "msa_prefill_varlen_workspace_bytes": ([i32, i32, P, P, i32, i32, i32, i32, i32], sz),
+        "msa_prefill_varlen": ([P, P, P, P, P, i32, i32, P, P, i32, i32, i32, i32, i32, i32,
+                                f32, P, P, P, P, sz, P], ctypes.c_int),
         "msa_decode_step_workspace_bytes": ([i32, i64, i32, i32, i32, i32], sz),
         "msa_decode_step": ([P, P, P, P, P, P, P, P, P, i32, i32, i64, i64, P, i32, i32,
                              i32, i32, i32, i32, f32, P, P, P, P, sz, P], ctypes.c_int),
@@ -364,6 +368,45 @@ def msa_sparse_gqa_decode(q: torch.Tensor, k_cache: torch.Tensor,
     _check("msa_sparse_gqa_decode", st)
     return o, lse
 
+
+
+def msa_prefill_varlen(q, k, v, idx_q, idx_k, cu_q, cu_kv, block: int, topk: int,
+                       scale: float | None = None, sel=None, o=None, lse=None, ws=None,
+                       want_lse: bool = True):
+    """Prefill of several sequences in one call.  ``q`` [Nq, Hq, d], ``idx_q``
+    [Nq, d_idx] packed by ``cu_q``; ``k``/``v`` [Hkv, Nkv, d], ``idx_k``
+    [Nkv, d_idx] packed by ``cu_kv`` (host integer sequences of n_seq + 1
+    offsets); each sequence's queries are its last tokens.  Returns
+    ``(o, lse, sel)``."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm)
+    _dev(idx_q, "idx_q", torch.float32)
+    _dev(idx_k, "idx_k", torch.float32)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share a dtype")
+    code = _dtype_code(q)
+    nq, hq, d = q.shape
+    hkv = k.shape[0]
+    cq = (ctypes.c_int64 * len(cu_q))(*[int(x) for x in cu_q])
+    ckv = (ctypes.c_int64 * len(cu_kv))(*[int(x) for x in cu_kv])
+    n_seq = len(cu_q) - 1
+    if len(cu_kv) != n_seq + 1:
+        raise ValueError("cu_q and cu_kv must have the same length")
+    scale = d ** -0.5 if scale is None else scale
+    lib = load()
+    ws = _ws(lib.msa_prefill_varlen_workspace_bytes(code, n_seq, cq, ckv, hq, d,
+                                                    idx_q.shape[1], block, topk), q, ws)
+    if sel is None:
+        sel = torch.empty((nq, topk), dtype=torch.int32, device=q.device)
+    if o is None:
+        o = torch.empty((nq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((nq, hq), dtype=torch.float32, device=q.device)
+    st = lib.msa_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(idx_q), _ptr(idx_k), code,
+                                n_seq, cq, ckv, hq, hkv, d, idx_q.shape[1], block, topk, scale,
+                                _ptr(sel), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(q))
+    _check("msa_prefill_varlen", st)
+    return o, lse, sel
 
 
 def msa_sparse_gqa_decode_paged(q, k_pages, v_pages, block_table, seq_len, sel, block: int,

@@ -230,6 +230,37 @@ int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
                            void *stream);
 
 /* --------------------------------------------------------------------------
+ * msa_prefill_varlen -- the whole prefill path (pool, top-K, CSR, sparse
+ * GQA with merge) for several sequences in one call, each a chunk of queries
+ * against its own cache ([CXT] section 3.3: prefill over a batch of
+ * requests of different lengths; the queries of a chunk attend to the
+ * blocks already in the cache).  Packed layouts with host offsets:
+ *
+ *   cu_q, cu_kv  HOST int64 [n_seq+1], cu_q[0] = cu_kv[0] = 0, nondecreasing;
+ *                sequence s has qn = cu_q[s+1]-cu_q[s] queries and
+ *                kvn = cu_kv[s+1]-cu_kv[s] >= qn cached tokens, its queries
+ *                being the last qn tokens (positions kvn-qn .. kvn-1)
+ *   q            [cu_q[n]][Hq][d] dtype;  idx_q [cu_q[n]][d_idx] fp32
+ *   k, v         [Hkv][cu_kv[n]][d] dtype;  idx_k [cu_kv[n]][d_idx] fp32
+ *   sel          [cu_q[n]][K] int32 out (each sequence's own block indices)
+ *   o, lse       [cu_q[n]][Hq][d], [cu_q[n]][Hq] fp32 out (lse may be NULL)
+ *   ws           device scratch of msa_prefill_varlen_workspace_bytes()
+ * The sequences run one after another on `stream` with the single-sequence
+ * kernels (enqueued by the library; nothing is synchronised).  The workspace
+ * holds one sequence's summaries, CSR and partial records at a time, so a
+ * long sequence is best split by the caller into query chunks.
+ * Supported as msa_sparse_gqa_prefill.
+ * ------------------------------------------------------------------------ */
+size_t msa_prefill_varlen_workspace_bytes(int32_t dtype, int32_t n_seq, const int64_t *cu_q,
+                                          const int64_t *cu_kv, int32_t hq, int32_t d,
+                                          int32_t d_idx, int32_t block, int32_t topk);
+int msa_prefill_varlen(const void *q, const void *k, const void *v, const float *idx_q,
+                       const float *idx_k, int32_t dtype, int32_t n_seq, const int64_t *cu_q,
+                       const int64_t *cu_kv, int32_t hq, int32_t hkv, int32_t d,
+                       int32_t d_idx, int32_t block, int32_t topk, float scale, int32_t *sel,
+                       float *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
  * msa_sparse_gqa_decode -- one new query per sequence over its selected
  * blocks ([CXT] section 3.3, decode), split over (block, key chunk) and
  * merged by log-sum-exp.  Sequence s's query sits at position seq_len[s]-1;

@@ -151,3 +151,24 @@ def test_paged_decode_validation(lib):
     assert call(npg=0) == EINVAL
     assert call(d=64) == EUNSUP
     assert call(hq=24) == EUNSUP                 # group 3
+
+
+def test_varlen_validation(lib):
+    P = FAKE
+    c = lambda xs: (ctypes.c_int64 * len(xs))(*xs)
+    wsb = lib.msa_prefill_varlen_workspace_bytes
+    assert wsb(1, 2, c([0, 100, 300]), c([0, 100, 500]), 64, 128, 128, 64, 8) > 0
+    assert wsb(1, 2, c([1, 100, 300]), c([0, 100, 500]), 64, 128, 128, 64, 8) == 0   # cu[0]
+    assert wsb(1, 2, c([0, 200, 300]), c([0, 100, 500]), 64, 128, 128, 64, 8) == 0   # qn > kvn
+    assert wsb(1, 2, c([0, 100, 90]), c([0, 100, 500]), 64, 128, 128, 64, 8) == 0    # decreasing
+    f = lib.msa_prefill_varlen
+    cq, ckv = c([0, 100, 300]), c([0, 100, 500])
+    need = wsb(1, 2, cq, ckv, 64, 128, 128, 64, 8)
+    args = [P, P, P, P, P, 1, 2, cq, ckv, 64, 8, 128, 128, 64, 8, 0.1, P, P, None, P]
+    assert f(*args, need - 1, None) == EWS
+    bad = list(args)
+    bad[7] = c([0, 200, 300])
+    assert f(*bad, need, None) == EINVAL
+    bad = list(args)
+    bad[11] = 96                                   # d = 96: no kernel
+    assert f(*bad, need, None) == EUNSUP
