@@ -333,39 +333,98 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
       const int32_t *srow = sel + i * topk;
       const int32_t *xrow = slot + i * topk;
       const float own2 = mref[nbk] + __log2f(ltot);
-      float mx = own2;
-      for (int kk = 0; kk < topk; ++kk) {
-        const int32_t bk = srow[kk];
-        if (bk < 0 || bk >= b) continue;
-        const int64_t n_idx = xrow[kk] - own_through(bk, q_pos0, n_q, B);
-        if (n_idx < 0 || n_idx >= n_part) continue;
-        mx = fmaxf(mx, part_le[n_idx * hq + hh].x);
-      }
-      float z = fast_exp2(own2 - mx);
-      const float wo = z / ltot;
+      float z, mx = own2;
+      if (topk <= 16) {
+        // the query's non-own records, every load of a stage issued together
+        // (K <= 16): the record indices, then all (lse, e) pairs, then the fp16
+        // outputs two records at a time; larger K merges record by record
+        constexpr int kMaxM = 16;
+        int64_t nid[kMaxM];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+        for (int kk = 0; kk < kMaxM; ++kk) {
+          nid[kk] = -1;
+          if (kk < topk) {
+            const int32_t bk = srow[kk], x = xrow[kk];
+            if (bk >= 0 && bk < b) {
+              const int64_t n = x - own_through(bk, q_pos0, n_q, B);
+              if (n >= 0 && n < n_part) nid[kk] = n;
+            }
+          }
+        }
+        float2 le[kMaxM];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[nbk][cb][r] *= wo;
-      for (int kk = 0; kk < topk; ++kk) {
-        const int32_t bk = srow[kk];
-        if (bk < 0 || bk >= b) continue;
-        const int64_t n_idx = xrow[kk] - own_through(bk, q_pos0, n_q, B);
-        if (n_idx < 0 || n_idx >= n_part) continue;
-        const float2 le = part_le[n_idx * hq + hh];
-        z += fast_exp2(le.x - mx);
-        const float wk = fast_exp2(le.x + le.y - mx);
+        for (int kk = 0; kk < kMaxM; ++kk)
+          le[kk] = nid[kk] >= 0 ? part_le[nid[kk] * hq + hh] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int kk = 0; kk < kMaxM; ++kk) mx = fmaxf(mx, le[kk].x);
+        z = fast_exp2(own2 - mx);
+        const float wo = z / ltot;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            const f16x4 pv = *reinterpret_cast<const f16x4 *>(
-                part_o + frag_off(n_idx, g, hq, G, head[nbk], cb, rg, h));
-            acc[nbk][cb][4 * rg] = fmaf(wk, (float)pv.x, acc[nbk][cb][4 * rg]);
-            acc[nbk][cb][4 * rg + 1] = fmaf(wk, (float)pv.y, acc[nbk][cb][4 * rg + 1]);
-            acc[nbk][cb][4 * rg + 2] = fmaf(wk, (float)pv.z, acc[nbk][cb][4 * rg + 2]);
-            acc[nbk][cb][4 * rg + 3] = fmaf(wk, (float)pv.w, acc[nbk][cb][4 * rg + 3]);
+          for (int r = 0; r < 16; ++r) acc[nbk][cb][r] *= wo;
+#pragma unroll
+        for (int k0 = 0; k0 < kMaxM; k0 += 2) {
+          if (k0 >= topk) break;
+          f16x4 pv[2][16];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int f = 0; f < 16; ++f) {
+              pv[u][f] = f16x4{0, 0, 0, 0};
+              if (nid[k0 + u] >= 0)
+                pv[u][f] = *reinterpret_cast<const f16x4 *>(
+                    part_o + frag_off(nid[k0 + u], g, hq, G, head[nbk], f >> 2, f & 3, h));
+            }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            if (nid[k0 + u] < 0) continue;
+            z += fast_exp2(le[k0 + u].x - mx);
+            const float wk = fast_exp2(le[k0 + u].x + le[k0 + u].y - mx);
+#pragma unroll
+            for (int f = 0; f < 16; ++f) {
+              const int cb = f >> 2, rg = f & 3;
+              acc[nbk][cb][4 * rg] = fmaf(wk, (float)pv[u][f].x, acc[nbk][cb][4 * rg]);
+              acc[nbk][cb][4 * rg + 1] = fmaf(wk, (float)pv[u][f].y, acc[nbk][cb][4 * rg + 1]);
+              acc[nbk][cb][4 * rg + 2] = fmaf(wk, (float)pv[u][f].z, acc[nbk][cb][4 * rg + 2]);
+              acc[nbk][cb][4 * rg + 3] = fmaf(wk, (float)pv[u][f].w, acc[nbk][cb][4 * rg + 3]);
+            }
           }
+        }
+      } else {
+        for (int kk = 0; kk < topk; ++kk) {
+          const int32_t bk = srow[kk];
+          if (bk < 0 || bk >= b) continue;
+          const int64_t n_idx = xrow[kk] - own_through(bk, q_pos0, n_q, B);
+          if (n_idx < 0 || n_idx >= n_part) continue;
+          mx = fmaxf(mx, part_le[n_idx * hq + hh].x);
+        }
+        z = fast_exp2(own2 - mx);
+        const float wo = z / ltot;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[nbk][cb][r] *= wo;
+        for (int kk = 0; kk < topk; ++kk) {
+          const int32_t bk = srow[kk];
+          if (bk < 0 || bk >= b) continue;
+          const int64_t n_idx = xrow[kk] - own_through(bk, q_pos0, n_q, B);
+          if (n_idx < 0 || n_idx >= n_part) continue;
+          const float2 le = part_le[n_idx * hq + hh];
+          z += fast_exp2(le.x - mx);
+          const float wk = fast_exp2(le.x + le.y - mx);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+              const f16x4 pv = *reinterpret_cast<const f16x4 *>(
+                  part_o + frag_off(n_idx, g, hq, G, head[nbk], cb, rg, h));
+              acc[nbk][cb][4 * rg] = fmaf(wk, (float)pv.x, acc[nbk][cb][4 * rg]);
+              acc[nbk][cb][4 * rg + 1] = fmaf(wk, (float)pv.y, acc[nbk][cb][4 * rg + 1]);
+              acc[nbk][cb][4 * rg + 2] = fmaf(wk, (float)pv.z, acc[nbk][cb][4 * rg + 2]);
+              acc[nbk][cb][4 * rg + 3] = fmaf(wk, (float)pv.w, acc[nbk][cb][4 * rg + 3]);
+            }
+        }
       }
       const float invz = 1.f / z;
       float *dst = o + (i * hq + hh) * (int64_t)kD;

@@ -220,6 +220,7 @@ def test_prefill_tiny_config_full(orc):
     ("bf16-G16-B48", dict(T=1300, Hq=32, Hkv=2, block=48, topk=5, n_hot=2), 200, 1000, 300),
     ("bf16-G1-B64", dict(T=1200, Hq=4, Hkv=4, block=64, topk=4, n_hot=2), 0, None, None),
     ("bf16-G2-B16", dict(T=900, Hq=8, Hkv=4, block=16, topk=9, n_hot=2), 0, None, None),
+    ("bf16-K24-B16", dict(T=1200, block=16, topk=24, n_hot=2), 300, 900, 300),   # merge of > 16 records
 ])
 def test_prefill_shapes(orc, name, over, q0, nq, sample):
     _say(f"prefill {name}")
