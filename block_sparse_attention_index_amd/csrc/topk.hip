@@ -43,6 +43,7 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
   __shared__ float lst_s[kQT][kMaxList];
   __shared__ int lst_b[kQT][kMaxList];
   __shared__ int lst_n[kQT];
+  __shared__ float lst_t[kQT];   // entry threshold: the (K-1)-th score, -inf until full
   float(*sc)[kPad] = qs;  // scores alias the query slice (phases are fenced)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -55,7 +56,10 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
   // candidates of the tile's last query: the blocks below its window
   const int64_t cand_last = (q_pos0 + q0 + nq - 1) / B - win + 1;
 
-  if (tid < kQT) lst_n[tid] = 0;
+  if (tid < kQT) {
+    lst_n[tid] = 0;
+    lst_t[tid] = -INFINITY;
+  }
   for (int e = tid; e < kQT * kMaxList; e += 256) {
     lst_s[e / kMaxList][e % kMaxList] = -INFINITY;
     lst_b[e / kMaxList][e % kMaxList] = -1;
@@ -97,25 +101,43 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) sc[ty + 16 * a][tx + 16 * j] = acc[a][j];
     __syncthreads();
-    // Merge: wave w owns queries 16w .. 16w+15.
+    // Merge: wave w owns queries 16w .. 16w+15.  First, for all 16 at once
+    // (every load in flight together), which queries have a candidate above
+    // their list's entry threshold; then insert only for those -- after the
+    // first chunks most lists are full and few candidates beat them.
+    uint32_t need = 0;
+    uint64_t masks[16];
+#pragma unroll
     for (int jq = 0; jq < 16; ++jq) {
       const int qi = wave * 16 + jq;
-      if (qi >= nq) break;
       const int64_t lim = (q_pos0 + q0 + qi) / B - win + 1;
       const float s = sc[qi][lane];
-      const bool valid = lane < nbk && b0 + lane < lim;
+      const float t = lst_t[qi];
+      const bool valid = qi < nq && lane < nbk && b0 + lane < lim;
+      masks[jq] = __ballot(valid && s > t);
+      if (masks[jq]) need |= 1u << jq;
+    }
+    while (need) {
+      const int jq = __ffs(need) - 1;
+      need &= need - 1;
+      const int qi = wave * 16 + jq;
+      const float s = sc[qi][lane];
       int cnt = lst_n[qi];
       float ls = lane < km ? lst_s[qi][lane] : -INFINITY;
       int lb = lane < km ? lst_b[qi][lane] : -1;
+      uint64_t mask = 0;
+#pragma unroll
+      for (int x = 0; x < 16; ++x)
+        if (x == jq) mask = masks[x];
+      list_insert(s, (int)b0, mask, km, cnt, ls, lb);
+      if (lane < km) {
+        lst_s[qi][lane] = ls;
+        lst_b[qi][lane] = lb;
+      }
       const float thr = shfl_f(ls, km - 1);
-      const uint64_t mask = __ballot(valid && (cnt < km || s > thr));
-      if (mask) {
-        list_insert(s, (int)b0, mask, km, cnt, ls, lb);
-        if (lane < km) {
-          lst_s[qi][lane] = ls;
-          lst_b[qi][lane] = lb;
-        }
-        if (lane == 0) lst_n[qi] = cnt;
+      if (lane == 0) {
+        lst_n[qi] = cnt;
+        lst_t[qi] = cnt < km ? -INFINITY : thr;
       }
     }
   }
