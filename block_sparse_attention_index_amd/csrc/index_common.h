@@ -8,7 +8,8 @@
 // candidate enters only if it beats the current (K-1)-th score strictly (an
 // equal score already in the list has a lower block index); a ballot picks
 // the lanes that beat the threshold, and each is inserted with one more
-// ballot (its rank) and one lane shift.
+// ballot (its rank) and one lane shift.  Cross-lane reads here are
+// v_readlane (a wave-uniform source lane) and DPP moves, never LDS permutes.
 #pragma once
 #include "msa_internal.h"
 
@@ -23,11 +24,19 @@ __device__ __forceinline__ float key2f(int k) {
   return __int_as_float(k ^ ((k >> 31) & 0x7fffffff));
 }
 
-__device__ __forceinline__ float shfl_f(float x, int src) {
-  return __shfl(x, src, 64);
+// Value of lane `src`, src the same in every lane (v_readlane: no LDS trip).
+__device__ __forceinline__ float lane_f(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
 }
-__device__ __forceinline__ int shfl_i(int x, int src) {
-  return __shfl(x, src, 64);
+__device__ __forceinline__ int lane_i(int x, int src) {
+  return __builtin_amdgcn_readlane(x, src);
+}
+// Value of lane l-1 (lane 0 keeps its own): a DPP wave_shr:1 move.
+__device__ __forceinline__ int prev_lane_i(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, 0x138, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float prev_lane_f(float x) {
+  return __int_as_float(prev_lane_i(__float_as_int(x)));
 }
 
 // Insert the lanes of `mask` (candidates s at block base+lane) into the
@@ -38,11 +47,11 @@ __device__ __forceinline__ void list_insert(float s, int base, uint64_t mask,
   const int lane = threadIdx.x & 63;
   while (mask) {
     const int src = __ffsll((unsigned long long)mask) - 1;
-    const float sj = shfl_f(s, src);
+    const float sj = lane_f(s, src);
     const int bj = base + src;
     const int pos = __popcll(__ballot(lane < cnt && ls >= sj));
-    const float ps = shfl_f(ls, lane > 0 ? lane - 1 : 0);
-    const int pb = shfl_i(lb, lane > 0 ? lane - 1 : 0);
+    const float ps = prev_lane_f(ls);
+    const int pb = prev_lane_i(lb);
     const int last = cnt < km - 1 ? cnt : km - 1;
     if (lane > pos && lane <= last) {
       ls = ps;
@@ -53,7 +62,7 @@ __device__ __forceinline__ void list_insert(float s, int base, uint64_t mask,
       lb = bj;
     }
     cnt = cnt + 1 < km ? cnt + 1 : km;
-    const float thr = shfl_f(ls, km - 1);
+    const float thr = lane_f(ls, km - 1);
     mask &= ~(1ull << src);
     mask &= __ballot(cnt < km || s > thr);
   }
@@ -67,7 +76,7 @@ __device__ __forceinline__ void write_row(int32_t *row, int topk, int cnt,
   const int lane = threadIdx.x & 63;
   int rank = 0;
   for (int j = 0; j < cnt; ++j) {
-    const int bj = shfl_i(lb, j);
+    const int bj = lane_i(lb, j);
     rank += (bj < lb) ? 1 : 0;
   }
   const int nf = own - first + 1;
@@ -94,11 +103,11 @@ __device__ __forceinline__ void list_insert_ids(float s, int bid, uint64_t mask,
   const int lane = threadIdx.x & 63;
   while (mask) {
     const int src = __ffsll((unsigned long long)mask) - 1;
-    const float sj = shfl_f(s, src);
-    const int bj = shfl_i(bid, src);
+    const float sj = lane_f(s, src);
+    const int bj = lane_i(bid, src);
     const int pos = __popcll(__ballot(lane < cnt && ls >= sj));
-    const float ps = shfl_f(ls, lane > 0 ? lane - 1 : 0);
-    const int pb = shfl_i(lb, lane > 0 ? lane - 1 : 0);
+    const float ps = prev_lane_f(ls);
+    const int pb = prev_lane_i(lb);
     const int last = cnt < km - 1 ? cnt : km - 1;
     if (lane > pos && lane <= last) {
       ls = ps;
@@ -109,7 +118,7 @@ __device__ __forceinline__ void list_insert_ids(float s, int bid, uint64_t mask,
       lb = bj;
     }
     cnt = cnt + 1 < km ? cnt + 1 : km;
-    const float thr = shfl_f(ls, km - 1);
+    const float thr = lane_f(ls, km - 1);
     mask &= ~(1ull << src);
     mask &= __ballot(cnt < km || s > thr);
   }
@@ -451,7 +460,7 @@ __device__ __forceinline__ void decode_merge_lists(
     }
 #pragma unroll
     for (int gi = 0; gi < kPre; ++gi) {
-      const float thr = shfl_f(ls, km - 1);
+      const float thr = lane_f(ls, km - 1);
       const uint64_t mask = __ballot(xbs[gi] >= 0 && (cnt < km || xs[gi] > thr));
       if (mask) list_insert_ids(xs[gi], xbs[gi], mask, km, cnt, ls, lb);
     }

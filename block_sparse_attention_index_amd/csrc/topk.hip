@@ -24,27 +24,43 @@ namespace {
 
 constexpr int kQT = 64;     // queries per workgroup (prefill)
 constexpr int kCB = 64;     // blocks per chunk
-constexpr int kDC = 64;     // index columns per staged slice
-constexpr int kPad = kDC + 1;
-constexpr int kMaxList = 64;
+constexpr int kDC = 64;     // index columns per staged slice (d_idx > kDFull)
+constexpr int kDFull = 128; // d_idx up to this: the whole row staged at once
+
+typedef float f32x16s __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
-// Prefill: workgroup = 64 consecutive queries; loop over chunks of 64 blocks
-// below the workgroup's last own block.  Scores by a 4x4 register tile per
-// thread over LDS-staged slices of 64 index columns; then each wave merges 16
-// queries' 64 new scores into their lists.
+// Prefill: workgroup = 64 consecutive queries (4 waves); loop over chunks of
+// 64 blocks below the workgroup's last own block.  Scores on the fp32 matrix
+// cores: wave w computes the 32 x 32 quadrant (queries 32*(w/2).., blocks
+// 32*(w%2)..) with v_mfma_f32_32x32x2_f32 from LDS-staged rows (fp32 products
+// and sums, as a dot product in any summation order).  The query tile is
+// staged once when d_idx <= kDFull (else slice by slice with the blocks).
+// Then each wave merges 16 queries' 64 new scores into their lists: first,
+// for all 16 at once, which queries have a candidate above their list's
+// entry threshold; then insertion only for those -- after the first chunks
+// most lists are full and few candidates beat them.
+//
+// LDS rows are padded to an odd stride (kDFull + 1, kDC + 1 floats), so the
+// 32 lanes of a half-wave reading one column of 32 rows hit 32 banks.
+// KMAX bounds the list length (K - window).
 // ---------------------------------------------------------------------------
+template <int KMAX, bool FULL>
 __global__ __launch_bounds__(256) void topk_prefill_kernel(
     const float *__restrict__ idx_q, int64_t n_q, int64_t q_pos0,
     const float *__restrict__ kmax, int d_idx, int B, int topk, int win,
     int32_t *__restrict__ sel) {
+  constexpr int kW = FULL ? kDFull : kDC;   // staged columns
+  constexpr int kPad = kW + 1;
   __shared__ float qs[kQT][kPad];
   __shared__ float ks[kCB][kPad];
-  __shared__ float lst_s[kQT][kMaxList];
-  __shared__ int lst_b[kQT][kMaxList];
+  __shared__ float lst_s[kQT][KMAX];
+  __shared__ int lst_b[kQT][KMAX];
   __shared__ int lst_n[kQT];
   __shared__ float lst_t[kQT];   // entry threshold: the (K-1)-th score, -inf until full
-  float(*sc)[kPad] = qs;  // scores alias the query slice (phases are fenced)
+  // scores alias the block rows (written after the MFMAs' last read of them,
+  // read before the next chunk's staging; both sides fenced)
+  float(*sc)[kPad] = ks;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Heavier (later) tiles first.
@@ -55,56 +71,69 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
   const int km = topk - win;   // picks by score; the window win is forced
   // candidates of the tile's last query: the blocks below its window
   const int64_t cand_last = (q_pos0 + q0 + nq - 1) / B - win + 1;
+  // 16-byte loads when every row starts 16-byte aligned
+  const bool vq = (d_idx & 3) == 0 && (reinterpret_cast<uintptr_t>(idx_q) & 15) == 0;
+  const bool vk = (d_idx & 3) == 0 && (reinterpret_cast<uintptr_t>(kmax) & 15) == 0;
+
+  // rows [r0, r0 + nr) x columns [c0, c0 + dc) of a [*, d_idx] fp32 matrix
+  // into dst (zero beyond nr / dc, up to kW columns)
+  auto stage = [&](float (*dst)[kPad], const float *src, bool vec, int64_t r0, int nr,
+                   int c0, int dc) {
+    if (vec) {
+      constexpr int kV = kW / 4;
+      for (int e = tid; e < kQT * kV; e += 256) {
+        const int r = e / kV, c = 4 * (e % kV);
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < nr && c < dc)
+          x = *reinterpret_cast<const float4 *>(src + (r0 + r) * d_idx + c0 + c);
+        dst[r][c] = x.x;
+        dst[r][c + 1] = x.y;
+        dst[r][c + 2] = x.z;
+        dst[r][c + 3] = x.w;
+      }
+    } else {
+      for (int e = tid; e < kQT * kW; e += 256) {
+        const int r = e / kW, c = e % kW;
+        dst[r][c] = (r < nr && c < dc) ? src[(r0 + r) * d_idx + c0 + c] : 0.f;
+      }
+    }
+  };
 
   if (tid < kQT) {
     lst_n[tid] = 0;
     lst_t[tid] = -INFINITY;
   }
-  for (int e = tid; e < kQT * kMaxList; e += 256) {
-    lst_s[e / kMaxList][e % kMaxList] = -INFINITY;
-    lst_b[e / kMaxList][e % kMaxList] = -1;
+  for (int e = tid; e < kQT * KMAX; e += 256) {
+    lst_s[e / KMAX][e % KMAX] = -INFINITY;
+    lst_b[e / KMAX][e % KMAX] = -1;
   }
+  if (FULL) stage(qs, idx_q, vq, q0, nq, 0, d_idx);
   __syncthreads();
 
-  const int ty = tid >> 4, tx = tid & 15;
+  const int qw = wave >> 1, bw = wave & 1;
+  const int h = lane >> 5, j = lane & 31;
   for (int64_t b0 = 0; km > 0 && b0 < cand_last; b0 += kCB) {
     const int nbk = (int)(cand_last - b0 < kCB ? cand_last - b0 : kCB);
-    float acc[4][4];
+    f32x16s d;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[a][c] = 0.f;
-    for (int c0 = 0; c0 < d_idx; c0 += kDC) {
-      const int dc = d_idx - c0 < kDC ? d_idx - c0 : kDC;
+    for (int r = 0; r < 16; ++r) d[r] = 0.f;
+    for (int c0 = 0; c0 < d_idx; c0 += kW) {
+      const int dc = d_idx - c0 < kW ? d_idx - c0 : kW;
+      if (!FULL) stage(qs, idx_q, vq, q0, nq, c0, dc);
+      stage(ks, kmax, vk, b0, nbk, c0, dc);
       __syncthreads();
-      for (int e = tid; e < kQT * kDC; e += 256) {
-        const int r = e / kDC, c = e % kDC;
-        qs[r][c] = (r < nq && c < dc) ? idx_q[(q0 + r) * d_idx + c0 + c] : 0.f;
-        ks[r][c] = (r < nbk && c < dc) ? kmax[(b0 + r) * d_idx + c0 + c] : 0.f;
+      const int dce = (dc + 1) & ~1;   // K = 2 per step; column dc is zero
+      for (int kk = 0; kk < dce; kk += 2) {
+        const float a = qs[32 * qw + j][kk + h];
+        const float b = ks[32 * bw + j][kk + h];
+        d = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, d, 0, 0, 0);
       }
       __syncthreads();
-      for (int c = 0; c < dc; ++c) {
-        float qv[4], kv[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) qv[a] = qs[ty + 16 * a][c];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kv[j] = ks[tx + 16 * j][c];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[a][j] = fmaf(qv[a], kv[j], acc[a][j]);
-      }
     }
-    __syncthreads();
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sc[ty + 16 * a][tx + 16 * j] = acc[a][j];
+    for (int r = 0; r < 16; ++r) sc[32 * qw + 8 * (r >> 2) + 4 * h + (r & 3)][32 * bw + j] = d[r];
     __syncthreads();
-    // Merge: wave w owns queries 16w .. 16w+15.  First, for all 16 at once
-    // (every load in flight together), which queries have a candidate above
-    // their list's entry threshold; then insert only for those -- after the
-    // first chunks most lists are full and few candidates beat them.
+    // Merge: wave w owns queries 16w .. 16w+15.
     uint32_t need = 0;
     uint64_t masks[16];
 #pragma unroll
@@ -134,14 +163,14 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
         lst_s[qi][lane] = ls;
         lst_b[qi][lane] = lb;
       }
-      const float thr = shfl_f(ls, km - 1);
+      const float thr = lane_f(ls, km - 1);
       if (lane == 0) {
         lst_n[qi] = cnt;
         lst_t[qi] = cnt < km ? -INFINITY : thr;
       }
     }
+    __syncthreads();   // sc (aliasing ks) is read above; the next staging overwrites it
   }
-  __syncthreads();
   for (int jq = 0; jq < 16; ++jq) {
     const int qi = wave * 16 + jq;
     if (qi >= nq) break;
@@ -196,8 +225,23 @@ hipError_t launch_topk_prefill(const float *idx_q, int64_t n_q, int64_t q_pos0,
                                hipStream_t st) {
   (void)nb;
   const int64_t n_tiles = (n_q + kQT - 1) / kQT;
-  hipLaunchKernelGGL(topk_prefill_kernel, dim3((unsigned)n_tiles), dim3(256), 0,
-                     st, idx_q, n_q, q_pos0, kmax, d_idx, block, topk, win, sel);
+  const dim3 grid((unsigned)n_tiles), wg(256);
+  const bool full = d_idx <= kDFull;
+  if (topk - win <= 16) {
+    if (full)
+      hipLaunchKernelGGL((topk_prefill_kernel<16, true>), grid, wg, 0, st, idx_q, n_q,
+                         q_pos0, kmax, d_idx, block, topk, win, sel);
+    else
+      hipLaunchKernelGGL((topk_prefill_kernel<16, false>), grid, wg, 0, st, idx_q, n_q,
+                         q_pos0, kmax, d_idx, block, topk, win, sel);
+  } else {
+    if (full)
+      hipLaunchKernelGGL((topk_prefill_kernel<64, true>), grid, wg, 0, st, idx_q, n_q,
+                         q_pos0, kmax, d_idx, block, topk, win, sel);
+    else
+      hipLaunchKernelGGL((topk_prefill_kernel<64, false>), grid, wg, 0, st, idx_q, n_q,
+                         q_pos0, kmax, d_idx, block, topk, win, sel);
+  }
   return hipGetLastError();
 }
 

@@ -118,12 +118,35 @@ def test_topk_tiny_config(orc):
     (3000, 16, 1, 32, 0, 0),        # K = 1: own block only
     (2500, 32, 64, 24, 100, 0),     # K = 64 (max), d_idx not a multiple of 64
     (5000, 128, 16, 128, 1234, 6),  # chunk not aligned to anything
+    (3000, 32, 8, 200, 0, 4),       # d_idx above one staged row: 64-column slices
+    (2000, 32, 6, 130, 50, 3),      # sliced, d_idx not a multiple of 4 (scalar staging)
+    (2000, 32, 5, 77, 0, 3),        # whole row staged, odd d_idx (zero-padded K step)
+    (2500, 16, 20, 256, 0, 4),      # list longer than 16, sliced rows
 ])
 def test_topk_shapes(orc, T, B, K, d, q0, hot):
     _say(f"topk T={T} B={B} K={K} d={d} q0={q0}")
     cfg = synth.Config("t", T, "f32", 1, 1, 64, d, B, K, hot)
     x = synth.sequence_inputs(cfg, "cpu", 1)
     _topk_case(orc, x["idx_q"].numpy()[q0:], x["idx_k"].numpy(), B, K, q_pos0=q0)
+
+
+def test_topk_misaligned_rows(orc):
+    """Row pointers that are not 16-byte aligned take the 4-byte staging path."""
+    cfg = synth.Config("t", 3000, "f32", 1, 1, 64, 128, 64, 8, 4)
+    x = synth.sequence_inputs(cfg, "cpu", 2)
+    idx_q, idx_k = x["idx_q"].numpy(), x["idx_k"].numpy()
+    B, K = cfg.block, cfg.topk
+    kmax = orc.pool(idx_k, B)
+    pos = np.arange(idx_q.shape[0], dtype=np.int64)
+    sel_o, gr, ga, eb = orc.select(idx_q, pos, kmax, B, K)
+    qbuf = torch.zeros(idx_q.size + 1, device=DEV)
+    qbuf[1:] = torch.from_numpy(idx_q.ravel()).to(DEV)
+    kbuf = torch.zeros(kmax.size + 1, device=DEV)
+    kbuf[1:] = torch.from_numpy(kmax.ravel()).to(DEV)
+    q_view, k_view = qbuf[1:].view(idx_q.shape), kbuf[1:].view(kmax.shape)
+    assert q_view.data_ptr() % 16 != 0 and k_view.data_ptr() % 16 != 0
+    sel_d = ops.msa_index_topk(q_view, k_view, B, K)
+    check_selection(_np(sel_d), sel_o, gr, ga, eb, idx_q, kmax, pos, B)
 
 
 def test_topk_ties_go_low(orc):
