@@ -3,17 +3,18 @@
 // as the VALU kernels in prefill.hip (sparse branch of "MiniMax M3模型算力成本
 // 大幅降低原因深度解析"; section 2.2 "KV Outer Gather Q：MSA 的关键设计" of
 // chenxutan.com's "MiniMax M3 深度实战"):
-//   pass A  one workgroup per (KV block b, KV head g, tile of 256/G queries
-//           from row b's non-own list): K[g,b] and V[g,b] are staged through
-//           LDS in 64-key chunks and applied to all 256 gathered query rows
-//           (tile tokens x the G query heads of group g);
-//   pass B  one workgroup per (block b, head g, tile of b's own tokens):
-//           causal attention inside the own block, then the log-sum-exp merge
-//           with pass A's partials; writes O and LSE.
+//   pass A  work items (KV block b, KV head g, tile of 256/G queries from
+//           row b's non-own list), walked by a persistent grid of 8-wave
+//           workgroups: K[g,b] and V[g,b] are streamed into LDS in 128-key
+//           chunks and applied to all 256 gathered query rows (tile tokens x
+//           the G query heads of group g);
+//   pass B  one 4-wave workgroup per (block b, head g, tile of b's own
+//           tokens): causal attention inside the own block (64-key chunks),
+//           then the log-sum-exp merge with pass A's partials; writes O and
+//           LSE.
 //
-// Each wave owns NB 32-row N-blocks; with NB = 1 and 8 waves a workgroup
-// holds 256 query rows and each SIMD runs two waves, so one wave's softmax
-// overlaps the other's MFMAs.  Scores are computed transposed, S^T = K Q^T
+// Each wave owns NB = 1 32-row N-block, and each SIMD runs two waves, so one
+// wave's softmax overlaps the other's MFMAs.  Scores are computed transposed, S^T = K Q^T
 // (keys = MFMA rows), so a lane holds 16 keys of ONE query row: the row max
 // needs one v_permlane32_swap with lane l^32 and the softmax statistics stay
 // per lane.  P^T leaves the accumulator already in the B-operand layout of
@@ -129,9 +130,11 @@ __device__ __forceinline__ void put_partial(uint16_t *part_o, float2 *part_le,
   if (hf == 0) part_le[n * hq + (int64_t)g * G + hl] = make_float2(mref + __log2f(ltot), (float)e);
 }
 
-// NB = 32-row N-blocks per wave, NW = waves per workgroup.
+// NB = 32-row N-blocks per wave, NW = waves per workgroup.  At most 256
+// registers per lane (two waves per SIMD): with NW = 4, two workgroups share
+// a CU, so one's merge loads overlap the other's matrix-core work.
 template <int G, int NB, int NW, bool OWN>
-__global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, int64_t kv_stride, int64_t q_pos0,
     int64_t n_q, int hq, int B, const int32_t *__restrict__ row_ptr,
@@ -454,11 +457,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(
 //      apart share the pattern, so all of a lane's V reads sit at constant
 //      offsets from one address per column block.
 // Rows past the chunk repeat its last valid row (masked keys then meet finite
-// values: their weight is exactly 0).
+// values: their weight is exactly 0).  Chunks are kKA = 128 keys (64 KiB of
+// K and V), two in LDS: one computed while the next streams in.
 // ---------------------------------------------------------------------------
+constexpr int kKA = 128;   // keys per staged chunk, persistent pass
+
 struct AsyncSmem {
-  uint16_t Ks[kKC * kD];
-  uint16_t Vs[kKC * kD];
+  uint16_t Ks[kKA * kD];
+  uint16_t Vs[kKA * kD];
 };
 
 typedef __attribute__((address_space(1))) void *gptr_t;
@@ -471,7 +477,7 @@ template <int NW>
 __device__ __forceinline__ void async_chunk(AsyncSmem &sm, const uint16_t *k,
                                             const uint16_t *v, int64_t row0,
                                             int nrows) {
-  constexpr int IPW = (kKC * kD / 8) / (64 * NW);   // instructions per wave
+  constexpr int IPW = (kKA * kD / 8) / (64 * NW);   // instructions per wave
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
@@ -526,13 +532,6 @@ __global__ __launch_bounds__(256) void prefill_tile_info(
   }
 }
 
-// Query fragments of a wave's next tile, staged by LDS DMA: instruction cc
-// of the wave fills x[cc][16 * lane ...] with the 16 bytes that lane needs for
-// k-step cc, so each lane reads back exactly the slot it filled.
-struct QStage {
-  uint16_t x[8][64 * 8];
-};
-
 template <int G, int NW>
 __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -548,7 +547,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   // alias the transposed reads of the other, and adds no wait for it.
   __shared__ AsyncSmem sm0;
   __shared__ AsyncSmem sm1;
-  __shared__ QStage qst[NW];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, j = lane & 31;
   const int tl = wave * TPN + j / G;  // token slot of this lane's row
@@ -562,20 +560,21 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   int64_t w = W * xcd / 8 + r;
   if (w >= w_end) return;
 
+  // Query fragments of the next item: plain loads into registers, issued at
+  // the start of the current item's last chunk and first used after that
+  // chunk's barrier (whose wait covers them).
+  u32x4 qn[8];
   auto stage_q = [&](int gg, int32_t qr) {
     const bool a = qr >= 0 && qr < n_q;
     const uint16_t *qp = q + (((a ? (int64_t)qr : 0) * hq + (int64_t)gg * G + hl) * kD);
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc)
-      __builtin_amdgcn_global_load_lds(
-          (gptr_t)(const_cast<uint16_t *>(qp + cc * 16 + 8 * h)),
-          (lptr_t)(&qst[wave].x[cc][0]), 16, 0, 0);
+    for (int cc = 0; cc < 8; ++cc) qn[cc] = *reinterpret_cast<const u32x4 *>(qp + cc * 16 + 8 * h);
   };
   auto read_q = [&](int32_t qr, bf16x8 (&dst)[8]) {
     const bool a = qr >= 0 && qr < n_q;
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
-      u32x4 x = *reinterpret_cast<const u32x4 *>(&qst[wave].x[cc][8 * lane]);
+      u32x4 x = qn[cc];
       if (!a) x = u32x4{0u, 0u, 0u, 0u};
       dst[cc] = as_bf16x8(x);
     }
@@ -591,12 +590,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   int4 inf = info[w % T];
   int32_t qraw = tq[(w % T) * TPT + tl];
   int64_t nkeys = kv_keys(inf.x);
-  int64_t n_chunks = (nkeys + kKC - 1) / kKC;
+  int64_t n_chunks = (nkeys + kKA - 1) / kKA;
   int64_t ci = 0;
   stage_q(g, qraw);
   async_chunk<NW>(sm0, k + ((int64_t)g * kv_stride) * kD,
                   v + ((int64_t)g * kv_stride) * kD, (int64_t)inf.x * B,
-                  (int)(nkeys < kKC ? nkeys : kKC));
+                  (int)(nkeys < kKA ? nkeys : kKA));
   // Metadata of the next item.  The one after it is fetched at the start of
   // each item's last chunk, so the load completes under that chunk's
   // compute and is only moved into place after the chunk's barrier.
@@ -643,7 +642,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
   float mref = -INFINITY, lsum = 0.f;
 
-  // One 64-key chunk of the current item on buffer P, with the next chunk
+  // One chunk of the current item on buffer P, with the next chunk
   // (or the next item's first chunk and queries) streaming into the other.
   // Returns false once this workgroup's range is done.
   auto step = [&](auto tag) -> bool {
@@ -651,7 +650,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     AsyncSmem &cur = P ? sm1 : sm0;
     AsyncSmem &nxt = P ? sm0 : sm1;
     const int64_t b = inf.x;
-    const int64_t kc = ci * kKC;
+    const int64_t kc = ci * kKA;
     const bool last = ci + 1 >= n_chunks;
     int gnn = 0;
     int4 infnn = make_int4(0, 0, 0, 0);
@@ -661,18 +660,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
       fetch(wn + per, gnn, infnn, qrawnn);
     }
     if (!last) {
-      const int64_t nxt_row = kc + kKC;
+      const int64_t nxt_row = kc + kKA;
       async_chunk<NW>(nxt, k + ((int64_t)g * kv_stride) * kD,
                       v + ((int64_t)g * kv_stride) * kD, b * B + nxt_row,
-                      (int)(nkeys - nxt_row < kKC ? nkeys - nxt_row : kKC));
+                      (int)(nkeys - nxt_row < kKA ? nkeys - nxt_row : kKA));
     } else if (has_next) {
       const int64_t nk = kv_keys(infn.x);
       async_chunk<NW>(nxt, k + ((int64_t)gn * kv_stride) * kD,
                       v + ((int64_t)gn * kv_stride) * kD, (int64_t)infn.x * B,
-                      (int)(nk < kKC ? nk : kKC));
+                      (int)(nk < kKA ? nk : kKA));
     }
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < kKA / 32; ++sub) {
       const int koff0 = (int)kc + sub * 32;
       if (koff0 >= nkeys) break;
       f32x16 sacc;
@@ -760,7 +759,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     infn = infnn;
     qrawn = qrawnn;
     nkeys = kv_keys(inf.x);
-    n_chunks = (nkeys + kKC - 1) / kKC;
+    n_chunks = (nkeys + kKA - 1) / kKA;
     ci = 0;
     read_q(qraw, qf);
 #pragma unroll
@@ -813,10 +812,13 @@ hipError_t launch_mfma_g(const uint16_t *q, const uint16_t *k, const uint16_t *v
                        0, st, q, k, v, kv_stride, q_pos0, n_q, hq, hkv, B, tile_ptr,
                        nb, info, tq, sl2, part_o, part_le, n_part);
   }
+  // own-block pass: 4-wave workgroups (see prefill_mfma_kernel)
+  constexpr int NWB = 4;
+  constexpr int TPTB = NWB * NB * (32 / G);
   const int64_t b_first = q_pos0 / B, b_last = (q_pos0 + n_q - 1) / B;
-  const int64_t tiles = (b_last - b_first + 1) * ((B + TPT - 1) / TPT);
-  hipLaunchKernelGGL((prefill_mfma_kernel<G, NB, NW, true>),
-                     dim3((unsigned)tiles, hkv), dim3(64 * NW), 0, st, q, k, v,
+  const int64_t tiles = (b_last - b_first + 1) * ((B + TPTB - 1) / TPTB);
+  hipLaunchKernelGGL((prefill_mfma_kernel<G, NB, NWB, true>),
+                     dim3((unsigned)tiles, hkv), dim3(64 * NWB), 0, st, q, k, v,
                      kv_stride, q_pos0, n_q, hq, B, row_ptr, q_list, tile_ptr, nb,
                      sel, topk, slot, sl2, part_o, part_le, n_part, o, lse);
   return hipGetLastError();
