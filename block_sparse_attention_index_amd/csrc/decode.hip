@@ -230,16 +230,19 @@ __global__ __launch_bounds__(256) void decode_attn(
 //
 // Work unit u = ((s * Hkv + g) * topk + kk) * nseg + seg: keys
 // [b*B + seg*seg_len, +seg_len) of block b = sel[s][kk], clipped to the block
-// and to the query position; its partial is record u of the workspace.  One
+// and to the query position.  One
 // workgroup per CU walks a contiguous range of units as one stream of 128-key
 // chunks: each chunk's K and V rows arrive by LDS DMA (16 bytes per lane,
 // XOR-swizzled 256-byte rows) into one of two buffers while the previous
 // chunk is computed, and the next unit's queries are staged with its first
 // chunk.  Wave w owns keys 32w .. 32w+31 of a chunk: S^T = K Q^T with the G
 // heads as MFMA columns, an online softmax per head, O^T += V^T P^T with V^T
-// read by ds_read_b64_tr_b16.  At a unit's last chunk the four waves'
-// (max, sum, O) are combined through LDS (reusing the chunk buffer just
-// consumed) into the unit's normalised partial and base-2 log-sum-exp.  The
+// read by ds_read_b64_tr_b16.  The softmax state carries on across the
+// consecutive units of one (sequence, KV head) -- a run; at a run's last
+// chunk the four waves' (max, sum, O) are combined through LDS (reusing the
+// chunk buffer just consumed) into the run's normalised partial and base-2
+// log-sum-exp, record `first unit of the run in this range` of the workspace
+// (decode_merge_runs finds them from the static unit partition).  The
 // two buffers are distinct LDS objects named statically by each chunk step,
 // so the compiler can tell the DMA into one from the reads of the other.
 // ---------------------------------------------------------------------------
@@ -358,11 +361,25 @@ __global__ __launch_bounds__(256) void decode_stream(
     for (; u < u_end; ++u) {
       d = unit(u);
       if (d.nk > 0) break;
-      for (int x = tid; x < G * D; x += 256) part_o[(size_t)u * G * D + x] = 0.f;
-      if (tid < G) part_lse[(size_t)u * G + tid] = -INFINITY;
     }
     return u;
   };
+  // Runs: the units of one (sequence, KV head) in this workgroup's range
+  // share the query rows, so the online softmax simply continues across them
+  // and one partial per run is written, in the slot of the run's first unit
+  // in the range (unique per workgroup and run, below n_units).  A run whose
+  // units are all empty gets the neutral partial (o = 0, lse = -inf).
+  const uint32_t ups_g = (uint32_t)(topk * nseg);   // units per (sequence, KV head)
+  auto run_slot = [&](uint32_t sg) __attribute__((always_inline)) {
+    const uint32_t u0 = sg * ups_g;
+    return u0 > u_begin ? u0 : u_begin;
+  };
+  auto put_neutral = [&](uint32_t sg) __attribute__((always_inline)) {
+    const size_t sl = run_slot(sg);
+    for (int x = tid; x < G * D; x += 256) part_o[sl * G * D + x] = 0.f;
+    if (tid < G) part_lse[sl * G + tid] = -INFINITY;
+  };
+  uint32_t sg_next = u_begin / ups_g;   // runs before this one are written
   auto dma_kv = [&](StreamBuf &buf, const DecUnit &d, int64_t row0, int nrows)
       __attribute__((always_inline)) {
     const uint16_t *kb = kc + (((int64_t)d.s * hkv + d.g) * len_max + row0) * D;
@@ -398,7 +415,10 @@ __global__ __launch_bounds__(256) void decode_stream(
 
   DecUnit cu;
   uint32_t u = next_unit(u_begin, cu);
-  if (u >= u_end) return;
+  if (u >= u_end) {
+    for (uint32_t sg = sg_next; sg <= (u_end - 1) / ups_g; ++sg) put_neutral(sg);
+    return;
+  }
   DecUnit nu = cu;
   uint32_t un = next_unit(u + 1, nu);
   dma_q(cu);
@@ -495,9 +515,10 @@ __global__ __launch_bounds__(256) void decode_stream(
           acc[cb] = mfma32(as_bf16x8(vraw), ks == 0 ? pb0 : pb1, acc[cb]);
         }
     }
-    if (last) {
-      // combine the four waves through LDS (the consumed buffer), then store
-      // the unit's partial before the chunk barrier's wait
+    const uint32_t sg_cur = (uint32_t)cu.s * (uint32_t)hkv + (uint32_t)cu.g;
+    if (last && (un >= u_end || (uint32_t)nu.s * (uint32_t)hkv + (uint32_t)nu.g != sg_cur)) {
+      // the run ends: combine the four waves through LDS (the consumed
+      // buffer), then store the run's partial before the chunk barrier's wait
       __syncthreads();
       float *mo = reinterpret_cast<float *>(&cur);   // [4][G][D]
       float *mm = mo + 4 * G * D;                    // [4][G]
@@ -528,8 +549,9 @@ __global__ __launch_bounds__(256) void decode_stream(
           z = fmaf(sc, ml[w * G + hd], z);
           ov = fmaf(sc, mo[(w * G + hd) * D + c], ov);
         }
-        part_o[((size_t)u * G + hd) * D + c] = ov / z;
-        if (c == 0) part_lse[(size_t)u * G + hd] = mx + __log2f(z);
+        const size_t sl = run_slot(sg_cur);
+        part_o[(sl * G + hd) * D + c] = ov / z;
+        if (c == 0) part_lse[sl * G + hd] = mx + __log2f(z);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -548,12 +570,17 @@ __global__ __launch_bounds__(256) void decode_stream(
     }
     // the staging area is rewritten by the next unit's DMA: finish these reads
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), others untouched
+    const uint32_t sg = (uint32_t)cu.s * (uint32_t)hkv + (uint32_t)cu.g;
+    if (sg >= sg_next) {   // a new run (runs whose units were all empty: neutral)
+      for (; sg_next < sg; ++sg_next) put_neutral(sg_next);
+      sg_next = sg + 1;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
-    m = -INFINITY;
-    l = 0.f;
+        for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
+      m = -INFINITY;
+      l = 0.f;
+    }
     ci = 0;
     int endp;
     for (;;) {
@@ -578,6 +605,7 @@ __global__ __launch_bounds__(256) void decode_stream(
     if (nx < 0) break;
     par = nx;
   }
+  for (; sg_next <= (u_end - 1) / ups_g; ++sg_next) put_neutral(sg_next);
 }
 
 // ---------------------------------------------------------------------------
@@ -1243,6 +1271,52 @@ __global__ __launch_bounds__(D) void decode_merge(
   if (lse && c == 0) lse[(int64_t)s * hq + hh] = (m + __log2f(z)) * kLn2;
 }
 
+// Merge of decode_stream's run partials: the units of (sequence s, KV head
+// g) are [sg * ups_g, (sg + 1) * ups_g) with sg = s * hkv + g; the
+// workgroups whose static unit ranges (u_q each, one more for the first u_r)
+// meet that span each left one partial, in the slot of their first unit in
+// it.  Workgroup = (query head, sequence), one thread per column.
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_runs(
+    int G, int hkv, uint32_t ups_g, uint32_t u_q, uint32_t u_r,
+    const float *__restrict__ part_o, const float *__restrict__ part_lse,
+    float *__restrict__ o, float *__restrict__ lse) {
+  const int hh = blockIdx.x, s = blockIdx.y, c = threadIdx.x;
+  const int hq = gridDim.x, g = hh / G, hl = hh % G;
+  const uint32_t sg = (uint32_t)s * (uint32_t)hkv + (uint32_t)g;
+  const uint32_t u0 = sg * ups_g, u1 = u0 + ups_g - 1;
+  const uint32_t split = u_r * (u_q + 1);   // units of the longer ranges
+  auto wg_of = [&](uint32_t u) { return u < split ? u / (u_q + 1) : u_r + (u - split) / u_q; };
+  const uint32_t b0 = wg_of(u0), b1 = wg_of(u1);
+  float m = -3.0e38f, z = 0.f, acc = 0.f;
+  constexpr int kBatch = 16;   // partials whose loads are in flight together
+  for (uint32_t bx0 = b0; bx0 <= b1; bx0 += kBatch) {
+    float li[kBatch], oi[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const uint32_t bx = bx0 + k;
+      li[k] = -INFINITY;
+      oi[k] = 0.f;
+      if (bx <= b1) {
+        const uint32_t ub = bx * u_q + (bx < u_r ? bx : u_r);
+        const size_t sl = ub > u0 ? ub : u0;
+        li[k] = part_lse[sl * G + hl];
+        oi[k] = part_o[(sl * G + hl) * D + c];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float mn = fmaxf(m, li[k]);
+      const float sc = fast_exp2(m - mn), w = fast_exp2(li[k] - mn);
+      z = fmaf(z, sc, w);
+      acc = fmaf(acc, sc, w * oi[k]);
+      m = mn;
+    }
+  }
+  o[((int64_t)s * hq + hh) * D + c] = acc / z;
+  if (lse && c == 0) lse[(int64_t)s * hq + hh] = (m + __log2f(z)) * kLn2;
+}
+
 // ---------------------------------------------------------------------------
 // Fused decode step, stage 1: workgroup = (chunk of kDecChunk blocks,
 // sequence), plus one more workgroup per sequence (x = n_chunks) that appends
@@ -1351,7 +1425,9 @@ hipError_t launch_dec(const T *q, const T *kc, const T *vc, int32_t n_seq,
                        len_max, seq_len, hq, hkv, B, const_cast<int32_t *>(sel), topk, pl.nseg,
                        pl.seg_len, pl.u_q, pl.u_r, scale * kLog2e, part_o, part_lse, nullptr,
                        nullptr, 0, (int64_t)0);
-    np = topk * pl.nseg;
+    hipLaunchKernelGGL((decode_merge_runs<D>), dim3(hq, n_seq), dim3(D), 0, st, G, hkv,
+                       (uint32_t)(topk * pl.nseg), pl.u_q, pl.u_r, part_o, part_lse, o, lse);
+    return hipGetLastError();
   } else {
     const dim3 grid(topk * nsub, hkv, n_seq);
     hipLaunchKernelGGL((decode_attn<T, G, D>), grid, dim3(256), 0, st, q, kc, vc,
@@ -1581,8 +1657,8 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
       return hipErrorInvalidValue;
   }
 #undef MSA_STEP_CASE
-  hipLaunchKernelGGL((decode_merge<128>), dim3(hq, n_seq), dim3(128), 0, st,
-                     topk * pl.nseg, G, hkv, part_o, part_lse, o, lse);
+  hipLaunchKernelGGL((decode_merge_runs<128>), dim3(hq, n_seq), dim3(128), 0, st, G, hkv,
+                     (uint32_t)(topk * pl.nseg), pl.u_q, pl.u_r, part_o, part_lse, o, lse);
   return hipGetLastError();
 }
 
