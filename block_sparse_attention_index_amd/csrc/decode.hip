@@ -613,11 +613,12 @@ __global__ __launch_bounds__(256) void decode_stream(
 // decode_stream over a page pool.  A page holds one MSA block of one KV head
 // ([n_pages][Hkv][B][d]); logical block b of sequence s lives in page
 // block_table[s][b].  FP8 pages carry one scale per (page, KV head) for K and
-// one for V: k = k_scale * e4m3(k_page), likewise v.  The units, the chunk
-// stream and the partial records are those of decode_stream (non-fused); a
-// unit never leaves its block, so its two scales are constants: the scores
-// are scaled once (folded into the softmax scale) and the partial output
-// once at the unit's end.
+// one for V: k = k_scale * e4m3(k_page), likewise v.  The units and the chunk
+// stream are those of decode_stream (non-fused).  bf16 pages also keep its
+// runs (one partial per run); an FP8 unit never leaves its block, so its two
+// scales are constants: the scores are scaled once (folded into the softmax
+// scale) and the partial output once at the unit's end -- one partial per
+// unit.
 //
 // decode_paged is the bf16 kernel (decode_stream's double-buffered chunk
 // stream with page addressing); decode_paged_fp8 below the FP8 one.
@@ -705,11 +706,22 @@ __global__ __launch_bounds__(256) void decode_paged(
     for (; u < u_end; ++u) {
       d = unit(u);
       if (d.nk > 0) break;
-      for (int x = tid; x < G * D; x += 256) part_o[(size_t)u * G * D + x] = 0.f;
-      if (tid < G) part_lse[(size_t)u * G + tid] = -INFINITY;
     }
     return u;
   };
+  // runs of one (sequence, KV head), as in decode_stream (bf16 pages: no V
+  // scale, so a run may cross pages)
+  const uint32_t ups_g = (uint32_t)(topk * nseg);
+  auto run_slot = [&](uint32_t sg) __attribute__((always_inline)) {
+    const uint32_t u0 = sg * ups_g;
+    return u0 > u_begin ? u0 : u_begin;
+  };
+  auto put_neutral = [&](uint32_t sg) __attribute__((always_inline)) {
+    const size_t sl = run_slot(sg);
+    for (int x = tid; x < G * D; x += 256) part_o[sl * G * D + x] = 0.f;
+    if (tid < G) part_lse[sl * G + tid] = -INFINITY;
+  };
+  uint32_t sg_next = u_begin / ups_g;
   // K and V rows with decode_stream's swizzles
   auto dma_kv = [&](PagedBuf<false> &buf, const PagedUnit &d, int64_t row, int nrows)
       __attribute__((always_inline)) {
@@ -746,7 +758,10 @@ __global__ __launch_bounds__(256) void decode_paged(
 
   PagedUnit cu;
   uint32_t u = next_unit(u_begin, cu);
-  if (u >= u_end) return;
+  if (u >= u_end) {
+    for (uint32_t sg = sg_next; sg <= (u_end - 1) / ups_g; ++sg) put_neutral(sg);
+    return;
+  }
   PagedUnit nu = cu;
   uint32_t un = next_unit(u + 1, nu);
   dma_q(cu);
@@ -838,7 +853,8 @@ __global__ __launch_bounds__(256) void decode_paged(
           acc[cb] = mfma32(as_bf16x8(vraw), ks == 0 ? pb0 : pb1, acc[cb]);
         }
     }
-    if (last) {
+    const uint32_t sg_cur = (uint32_t)cu.s * (uint32_t)hkv + (uint32_t)cu.g;
+    if (last && (un >= u_end || (uint32_t)nu.s * (uint32_t)hkv + (uint32_t)nu.g != sg_cur)) {
       __syncthreads();
       // the waves' (o, m, l) through LDS, in the consumed chunk buffer
       static_assert(4 * G * D * 4 + 8 * G * 4 <= (int)sizeof(PagedBuf<false>), "");
@@ -871,8 +887,9 @@ __global__ __launch_bounds__(256) void decode_paged(
           z = fmaf(sc, ml[w * G + hd], z);
           ov = fmaf(sc, mo[(w * G + hd) * D + c], ov);
         }
-        part_o[((size_t)u * G + hd) * D + c] = cu.vs * (ov / z);
-        if (c == 0) part_lse[(size_t)u * G + hd] = mx + __log2f(z);
+        const size_t sl = run_slot(sg_cur);
+        part_o[(sl * G + hd) * D + c] = ov / z;
+        if (c == 0) part_lse[sl * G + hd] = mx + __log2f(z);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -888,12 +905,17 @@ __global__ __launch_bounds__(256) void decode_paged(
       qf[cc] = as_bf16x8(xq);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
+    const uint32_t sg = (uint32_t)cu.s * (uint32_t)hkv + (uint32_t)cu.g;
+    if (sg >= sg_next) {   // a new run (runs whose units were all empty: neutral)
+      for (; sg_next < sg; ++sg_next) put_neutral(sg_next);
+      sg_next = sg + 1;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
-    m = -INFINITY;
-    l = 0.f;
+        for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
+      m = -INFINITY;
+      l = 0.f;
+    }
     ci = 0;
     int endp;
     for (;;) {
@@ -918,6 +940,7 @@ __global__ __launch_bounds__(256) void decode_paged(
     if (nx < 0) break;
     par = nx;
   }
+  for (; sg_next <= (u_end - 1) / ups_g; ++sg_next) put_neutral(sg_next);
 }
 
 // ---------------------------------------------------------------------------
@@ -1589,8 +1612,12 @@ hipError_t launch_decode_paged(const void *q, const void *k_pages, const void *v
     default:
       return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((decode_merge<128>), dim3(hq, n_seq), dim3(128), 0, st,
-                     topk * pl.nseg, G, hkv, part_o, part_lse, o, lse);
+  if (kv_dtype == 2)   // FP8: one partial per unit (each unit carries its page's V scale)
+    hipLaunchKernelGGL((decode_merge<128>), dim3(hq, n_seq), dim3(128), 0, st,
+                       topk * pl.nseg, G, hkv, part_o, part_lse, o, lse);
+  else                 // bf16: one partial per run
+    hipLaunchKernelGGL((decode_merge_runs<128>), dim3(hq, n_seq), dim3(128), 0, st, G, hkv,
+                       (uint32_t)(topk * pl.nseg), pl.u_q, pl.u_r, part_o, part_lse, o, lse);
   return hipGetLastError();
 }
 
