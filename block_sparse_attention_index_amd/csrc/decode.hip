@@ -306,42 +306,25 @@ __global__ __launch_bounds__(256) void decode_stream(
     int64_t len = seq_len[s] + (FUSED ? 1 : 0);
     return len > len_max ? len_max : len;
   };
-  if constexpr (FUSED) {
-    if (u_begin < u_end) {
-      const uint32_t s_last = (u_end - 1) / ups;
-      for (uint32_t s = s_first + wave; s <= s_last && s - s_first < kStepSeqs; s += 4) {
-        const int64_t len = query_len(s);   // in flight with the lists' loads
-        int32_t *row = &selrows[(s - s_first) * 64];
-        // scratch: a quarter of the (still unused) chunk buffers per wave
-        float *st_s = reinterpret_cast<float *>(wave < 2 ? &sb0 : &sb1) +
-                      (wave & 1) * (int)(sizeof(StreamBuf) / 8);
-        int *st_b = reinterpret_cast<int *>(st_s) + (int)(sizeof(StreamBuf) / 16);
-        const size_t c0 = (size_t)s * n_chunks * (topk - 1);
-        decode_merge_lists(
-            cand_s + c0, cand_b + c0, n_chunks, topk, 1,
-            [&] {
-              int64_t own = len >= 1 ? (len - 1) / B : 0;
-              return (int)(own >= nb_max ? nb_max - 1 : own);
-            },
-            row, st_s, st_b, (int)(sizeof(StreamBuf) / 16));
-        if (s * ups >= u_begin) {   // this workgroup holds the sequence's first unit
-          __builtin_amdgcn_s_waitcnt(0xC07F);   // the row's LDS writes have landed
-          if (lane < topk) sel[(size_t)s * topk + lane] = row[lane];
-        }
-      }
-    }
-    __syncthreads();
-  }
 
+  // Unit u of (sequence, KV head) sg = u / (topk * nseg): segment-major, and
+  // within a segment the selection's last entry first -- the own block when
+  // the row is full -- then ranks 0 .. topk-2.  So a range that starts on a
+  // segment boundary starts on an own-block unit, whose block is known
+  // before the selection is.
+  auto unit_pos = [&](uint32_t u, int &s, int &g, int &seg, int &kk) __attribute__((always_inline)) {
+    const uint32_t upg = (uint32_t)(topk * nseg);
+    const uint32_t sg = u / upg, idx = u - sg * upg;
+    seg = (int)(idx / (uint32_t)topk);
+    const int kr = (int)(idx - (uint32_t)seg * (uint32_t)topk);
+    kk = kr == 0 ? topk - 1 : kr - 1;
+    s = (int)(sg / (uint32_t)hkv);
+    g = (int)(sg - (uint32_t)s * (uint32_t)hkv);
+  };
   auto unit = [&](uint32_t u) __attribute__((always_inline)) {
     DecUnit d;
-    const uint32_t r1 = u / (uint32_t)nseg;
-    const int seg = (int)(u - r1 * (uint32_t)nseg);
-    const uint32_t r2 = r1 / (uint32_t)topk;
-    const int kk = (int)(r1 - r2 * (uint32_t)topk);
-    const uint32_t r3 = r2 / (uint32_t)hkv;
-    d.g = (int)(r2 - r3 * (uint32_t)hkv);
-    d.s = (int)r3;
+    int seg, kk;
+    unit_pos(u, d.s, d.g, seg, kk);
     const int64_t len = query_len(d.s);
     int32_t b;
     if constexpr (FUSED)
@@ -413,6 +396,58 @@ __global__ __launch_bounds__(256) void decode_stream(
   };
   auto kv_rows = [&](int n) __attribute__((always_inline)) { return n < kSK ? n : kSK; };
 
+  // FUSED: the first unit's queries and chunk go out before the selection
+  // merge when that unit is an own-block one (the own block is the row's
+  // last entry once the row is full, own >= topk - 1)
+  bool pre = false;
+  if constexpr (FUSED) {
+    if (u_begin < u_end) {
+      DecUnit d0;
+      int seg0, kk0;
+      unit_pos(u_begin, d0.s, d0.g, seg0, kk0);
+      const int64_t len0 = query_len(d0.s);
+      const int64_t own0 = len0 >= 1 ? (len0 - 1) / B : 0;
+      if (kk0 == topk - 1 && len0 >= 1 && own0 >= topk - 1 && own0 < nb_max) {
+        d0.t0 = own0 * B + (int64_t)seg0 * seg_len;
+        int64_t n0 = len0 - d0.t0;
+        if (n0 > seg_len) n0 = seg_len;
+        if (n0 > (int64_t)B - (int64_t)seg0 * seg_len) n0 = (int64_t)B - (int64_t)seg0 * seg_len;
+        if (n0 > 0) {
+          d0.nk = (int)n0;
+          dma_q(d0);
+          dma_kv(sb0, d0, d0.t0, kv_rows(d0.nk));
+          pre = true;
+        }
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    if (u_begin < u_end) {
+      const uint32_t s_last = (u_end - 1) / ups;
+      for (uint32_t s = s_first + wave; s <= s_last && s - s_first < kStepSeqs; s += 4) {
+        const int64_t len = query_len(s);   // in flight with the lists' loads
+        int32_t *row = &selrows[(s - s_first) * 64];
+        // scratch: a quarter of the (still unused) second chunk buffer per
+        // wave -- the first may already be receiving the first unit's chunk
+        float *st_s = reinterpret_cast<float *>(&sb1) + wave * (int)(sizeof(StreamBuf) / 16);
+        int *st_b = reinterpret_cast<int *>(st_s) + (int)(sizeof(StreamBuf) / 32);
+        const size_t c0 = (size_t)s * n_chunks * (topk - 1);
+        decode_merge_lists(
+            cand_s + c0, cand_b + c0, n_chunks, topk, 1,
+            [&] {
+              int64_t own = len >= 1 ? (len - 1) / B : 0;
+              return (int)(own >= nb_max ? nb_max - 1 : own);
+            },
+            row, st_s, st_b, (int)(sizeof(StreamBuf) / 32));
+        if (s * ups >= u_begin) {   // this workgroup holds the sequence's first unit
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // the row's LDS writes have landed
+          if (lane < topk) sel[(size_t)s * topk + lane] = row[lane];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
   DecUnit cu;
   uint32_t u = next_unit(u_begin, cu);
   if (u >= u_end) {
@@ -421,8 +456,10 @@ __global__ __launch_bounds__(256) void decode_stream(
   }
   DecUnit nu = cu;
   uint32_t un = next_unit(u + 1, nu);
-  dma_q(cu);
-  dma_kv(sb0, cu, cu.t0, kv_rows(cu.nk));
+  if (!(pre && u == u_begin)) {   // else the same unit's chunk is already on its way
+    dma_q(cu);
+    dma_kv(sb0, cu, cu.t0, kv_rows(cu.nk));
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -680,13 +717,15 @@ __global__ __launch_bounds__(256) void decode_paged(
 
   auto unit = [&](uint32_t u) __attribute__((always_inline)) {
     PagedUnit d;
-    const uint32_t r1 = u / (uint32_t)nseg;
-    const int seg = (int)(u - r1 * (uint32_t)nseg);
-    const uint32_t r2 = r1 / (uint32_t)topk;
-    const int kk = (int)(r1 - r2 * (uint32_t)topk);
-    const uint32_t r3 = r2 / (uint32_t)hkv;
-    d.g = (int)(r2 - r3 * (uint32_t)hkv);
-    d.s = (int)r3;
+    // decode_stream's unit order (segment-major, the row's last entry first),
+    // so both kernels accumulate a run's units in the same order
+    const uint32_t upg = (uint32_t)(topk * nseg);
+    const uint32_t sgi = u / upg, idx = u - sgi * upg;
+    const int seg = (int)(idx / (uint32_t)topk);
+    const int kr = (int)(idx - (uint32_t)seg * (uint32_t)topk);
+    const int kk = kr == 0 ? topk - 1 : kr - 1;
+    d.s = (int)(sgi / (uint32_t)hkv);
+    d.g = (int)(sgi - (uint32_t)d.s * (uint32_t)hkv);
     int64_t len = seq_len[d.s];
     if (len > len_max) len = len_max;
     const int32_t b = sel[(int64_t)d.s * topk + kk];
