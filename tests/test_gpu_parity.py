@@ -392,6 +392,69 @@ def test_decode_steps_in_a_captured_graph(orc):
 
 
 
+def test_fused_steps_in_a_captured_graph():
+    # A chain of fused steps (each appends its token, so the caches and the
+    # running block maxima change) captured once and replayed after restoring
+    # the state must give the eager results on every replay, bit for bit.
+    hq, hkv, d, di, B, K = 64, 8, 128, 128, 64, 6
+    lens, steps = [300, 1000, 63], 4
+    n, T = len(lens), max(lens) + steps
+    cfg = synth.Config("dec-step-graph", T, "bf16", hq, hkv, d, di, B, K, 3, n_seq=n,
+                       mode="decode")
+    _say("fused decode step graph replay")
+    x = synth.decode_inputs(cfg, "cpu", 5)
+    nb_max = -(-T // B)
+    kc0, vc0, ik0 = x["k_cache"].to(DEV), x["v_cache"].to(DEV), x["idx_k"].to(DEV)
+    seq0 = torch.tensor(lens, dtype=torch.int64, device=DEV)
+    kmax0 = torch.full((n, nb_max, di), float("nan"), device=DEV)
+    for s, L in enumerate(lens):
+        ops.msa_index_pool(ik0[s:s + 1, :L], B, kmax=kmax0[s:s + 1], seq_len=seq0[s:s + 1],
+                           nb_max=nb_max)
+    q_all = synth._normal_rows((steps, n, hq, d), torch.bfloat16, "cpu", 2, "q").to(DEV)
+    iq_all = synth._normal_rows((steps, n, di), torch.float32, "cpu", 2, "idx_q").to(DEV)
+    pos = [[L + t for L in lens] for t in range(steps)]
+    k_new = [torch.stack([kc0[s, :, pos[t][s]] for s in range(n)]).contiguous() for t in range(steps)]
+    v_new = [torch.stack([vc0[s, :, pos[t][s]] for s in range(n)]).contiguous() for t in range(steps)]
+    ik_new = [torch.stack([ik0[s, pos[t][s]] for s in range(n)]).contiguous() for t in range(steps)]
+    seqs = [seq0 + t for t in range(steps)]
+    kc, vc, ik, kmax = kc0.clone(), vc0.clone(), ik0.clone(), kmax0.clone()
+    bufs = pipeline.alloc_decode_step(q_all[0], kmax, B, K)
+    outs = [torch.empty_like(bufs.o) for _ in range(steps)]
+    sels = [torch.empty_like(bufs.sel) for _ in range(steps)]
+
+    def reset():
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        ik.copy_(ik0)
+        kmax.copy_(kmax0)
+
+    def run():
+        for t in range(steps):
+            o, _, sel = pipeline.decode_append_step(
+                q_all[t], k_new[t], v_new[t], iq_all[t], ik_new[t], kc, vc, kmax, seqs[t], B, K,
+                cfg.scale, idx_k_cache=ik, bufs=bufs)
+            outs[t].copy_(o)
+            sels[t].copy_(sel)
+
+    reset()
+    run()
+    torch.cuda.synchronize()
+    eager = [(o_.cpu().clone(), s_.cpu().clone()) for o_, s_ in zip(outs, sels)]
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        reset()                                  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t in range(steps):
+            assert torch.equal(outs[t].cpu(), eager[t][0]), f"replay {rep} step {t}"
+            assert torch.equal(sels[t].cpu(), eager[t][1]), f"replay {rep} step {t}"
+
+
 # --------------------------------------------------------------------------
 # fused decode step (append + running block max + scan + top-K + attention)
 # --------------------------------------------------------------------------
