@@ -51,6 +51,35 @@ def attended_pairs(q_pos0: int, n_q: int, block: int, topk: int) -> int:
     return int(((keff - 1) * block + p % block + 1).sum())
 
 
+def index_work(T: int, cfg, n_calls: int) -> dict:
+    """Algorithmic work of the index stages of one T-token prefill: the pool
+    reads every index key and writes the block summaries; the top-K scores
+    2*d_idx FLOP per (query, earlier block) -- sum over p of own(p); the
+    inversion reads K selections per query and writes the CSR row pointers,
+    one query entry and one slot per selected pair."""
+    B, K, di = cfg.block, cfg.topk, cfg.d_idx
+    nb = -(-T // B)
+    p = np.arange(T, dtype=np.int64)
+    pairs = int(np.minimum(K, p // B + 1).sum())
+    return {"pool_bytes": T * di * 4 + nb * di * 4,
+            "topk_flop": 2 * di * int((p // B).sum()),
+            "invert_bytes": T * K * 4 + pairs * 8 + (nb + 1) * 4 * n_calls}
+
+
+def index_roofline(w: dict, pool_ms: float, topk_ms: float, invert_ms: float) -> dict:
+    """Each index stage against the roofline that bounds it: the pool and the
+    inversion against HBM, the top-K scores against the fp32 peak."""
+    def hbm(b, t):
+        g = b / (t * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(g, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(g / PEAK_HBM_GBS, 4)}
+    tf = w["topk_flop"] / (topk_ms * 1e-3) / 1e12
+    return {"pool": hbm(w["pool_bytes"], pool_ms),
+            "topk": {"bound": "fp32 mfma", "achieved": round(tf, 2), "peak": PEAK_F32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_F32_TFLOPS, 4)},
+            "invert": hbm(w["invert_bytes"], invert_ms)}
+
+
 def decode_bytes(L: int, cfg) -> int:
     """Algorithmic HBM bytes of one decode step for a sequence of length L
     (query at L-1): K and V of the attended keys, the block summaries scanned,
@@ -370,6 +399,10 @@ def main():
         "index_ms": {"pool": round(ms(ev["pool"]) / args.steps, 3),
                      "topk": round(ms(ev["topk"]) / args.steps, 3),
                      "invert": round(ms(ev["invert"]) / args.steps, 3)},
+        "index_roofline": index_roofline(index_work(T, cfg, n_calls),
+                                         ms(ev["pool"]) / args.steps,
+                                         ms(ev["topk"]) / args.steps,
+                                         ms(ev["invert"]) / args.steps),
         "roofline": {"kernel": "msa_sparse_gqa_prefill (KV-outer pass + own-block/merge pass)",
                      "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 5),
