@@ -117,9 +117,11 @@ int msa_index_pool_mean(const float *idx_k, int32_t n_seq, int64_t len_max,
  * 的差异化优化" (prefill scores every block for every query).
  *
  * Query i sits at position p = q_pos0 + i, own = p / B.  Its candidates are
- * the blocks b < own, scored in fp32 by s[b] = sum_c idx_q[i][c]*kmax[b][c];
- * it keeps the best min(K-1, own) by (score desc, block asc), adds own, and
- * writes them ascending to sel[i][0..], padding with -1 up to K.
+ * the blocks b < own, scored in fp32 by s[b] = sum_c idx_q[i][c]*kmax[b][c]
+ * (fp32 products and sums in an unspecified order, so scores within the fp32
+ * dot-product error bound of each other may rank either way); it keeps the
+ * best min(K-1, own) by (score desc, block asc), adds own, and writes them
+ * ascending to sel[i][0..], padding with -1 up to K.
  *
  *   idx_q  [n_q][d_idx] fp32;  kmax [nb][d_idx] fp32 with
  *          nb >= own of the last query + 1
