@@ -159,3 +159,17 @@ def test_full_dec16(orc):
         assert eo <= TOL_BF16 and el <= TOL_BF16, (s, eo, el)
     _say(f"dec16: {n} sequences, near-ties flagged {nf_all}; "
          f"max|do| {worst[0]:.3g} max|dlse| {worst[1]:.3g}")
+    # the fused step as it is timed: the last token appended again in place
+    # (idempotent) gives the same selection and output bit for bit
+    L = cfg.T - 1
+    before = x["seq_len"] - 1
+    kmax_f = ops.msa_index_pool(x["idx_k"], B, seq_len=x["seq_len"], nb_max=cfg.nb)
+    fb = pipeline.alloc_decode_step(x["q"], kmax_f, B, K)
+    o_f, lse_f, sel_f = pipeline.decode_append_step(
+        x["q"], x["k_cache"][:, :, L].contiguous(), x["v_cache"][:, :, L].contiguous(),
+        x["idx_q"], x["idx_k"][:, L].contiguous(), x["k_cache"], x["v_cache"], kmax_f, before,
+        B, K, cfg.scale, idx_k_cache=x["idx_k"], bufs=fb)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(sel_f), sel)
+    assert np.array_equal(_np(o_f), o) and np.array_equal(_np(lse_f), lse)
+    _say("dec16: fused step matches the separate calls bit for bit")

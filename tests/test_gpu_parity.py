@@ -462,12 +462,16 @@ def test_fused_steps_in_a_captured_graph():
     (64, 8, 64, 6, [0, 63, 64, 200, 1000]),      # empty cache, block-opening tokens
     (16, 1, 128, 4, [1, 127, 300]),              # G = 16
     (8, 8, 512, 8, [511, 512, 3000]),            # G = 1, the 1M-token block size
+    # 128 sequences with full rows (own block >= K - 1): the workgroups whose
+    # range starts on an own-block unit fetch its first chunk before the
+    # selection merge (own blocks from 7 to 512 keys)
+    (8, 1, 512, 8, [3590 + 9 * i for i in range(128)]),
 ])
 def test_decode_step_fused(orc, hq, hkv, B, K, lens):
     n, d, di, steps = len(lens), 128, 128, 3
     T = max(lens) + steps
     cfg = synth.Config("dec-step", T, "bf16", hq, hkv, d, di, B, K, 4, n_seq=n, mode="decode")
-    _say(f"fused decode step G={hq // hkv} B={B} K={K} lens={lens}")
+    _say(f"fused decode step G={hq // hkv} B={B} K={K} lens={lens[:8]}{' ...' if n > 8 else ''}")
     x = synth.decode_inputs(cfg, "cpu", 0)
     nb_max = -(-T // B)
     kc = x["k_cache"].to(DEV)
