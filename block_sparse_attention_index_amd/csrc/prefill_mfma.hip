@@ -22,9 +22,10 @@
 // staged row-major in LDS and each V^T operand is read with two
 // ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x 16-column tile
 // transposed, so lane i gets column i of four consecutive keys).  Lazy
-// rescaling: the running reference max moves only when a row's max exceeds
-// it by more than 8 (so every weight is at most 2^8), which removes most O
-// rescales.
+// rescaling keeps every weight at most 2^8 and removes most O rescales: in
+// pass B the running reference max moves only when a row's max exceeds it by
+// more than 8; in pass A the weights are first taken against the reference
+// and the row max is only computed when a lane's 16 weights sum past 2^8.
 #include <type_traits>
 
 #include "msa_internal.h"
@@ -451,16 +452,33 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 // lands in its slot.  Rows are unpadded and XOR-swizzled by segment instead:
 //   K: segment s of row r at slot s ^ (r & 15)  -- the 16 rows read by a
 //      16-lane group for an A operand hit 16 distinct bank groups;
-//   V: segment s of row r at slot s ^ 2(r & 7) -- the 4 rows x 2 segments of
-//      a ds_read_b64_tr_b16 group are 8 distinct slots, and the 8 rows one
-//      instruction reads (aligned to 8) spread over all 16 slots; rows 8
-//      apart share the pattern, so all of a lane's V reads sit at constant
-//      offsets from one address per column block.
+//   V: segment s of row r at slot s ^ 4(r & 3) -- a half-wave of a
+//      ds_read_b64_tr_b16 reads 4 consecutive rows x 4 segments (one aligned
+//      group of four), and the XOR moves each row to its own group of four
+//      slots, so the 32 lanes cover all 64 banks once; rows 4 apart share the
+//      pattern, so all of a lane's V reads sit at constant offsets from one
+//      address per column block.
 // Rows past the chunk repeat its last valid row (masked keys then meet finite
 // values: their weight is exactly 0).  Chunks are kKA = 128 keys (64 KiB of
 // K and V), two in LDS: one computed while the next streams in.
 // ---------------------------------------------------------------------------
 constexpr int kKA = 128;   // keys per staged chunk, persistent pass
+constexpr float kCap = 256.f;   // bound on a lane's weight sum per sub-tile
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of the 16 bf16 weights of a lane (the values the P*V product uses),
+// in fp32 on v_dot2 against ones.
+__device__ __forceinline__ float row_sum16(bf16x8 a, bf16x8 b) {
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a[2 * i], a[2 * i + 1]}, one, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{b[2 * i], b[2 * i + 1]}, one, s1, false);
+  }
+  return s0 + s1;
+}
 
 struct AsyncSmem {
   uint16_t Ks[kKA * kD];
@@ -471,7 +489,7 @@ typedef __attribute__((address_space(1))) void *gptr_t;
 typedef __attribute__((address_space(3))) void *lptr_t;
 
 __device__ __forceinline__ int kswz(int r, int sgm) { return sgm ^ (r & 15); }
-__device__ __forceinline__ int vswz(int r, int sgm) { return sgm ^ (2 * (r & 7)); }
+__device__ __forceinline__ int vswz(int r, int sgm) { return sgm ^ (4 * (r & 3)); }
 
 template <int NW>
 __device__ __forceinline__ void async_chunk(AsyncSmem &sm, const uint16_t *k,
@@ -618,7 +636,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   // its 16-lane group reads 4 keys x 16 columns; lane a16 supplies key
   // (a16 / 4) and the 8-byte piece a16 % 4.  The second piece of a k-step is
   // 8 keys further, the next k-step 16, the next sub-tile 32 (constant
-  // offsets: the swizzle repeats every 8 rows).  Keeping each read one
+  // offsets: the swizzle repeats every 4 rows).  Keeping each read one
   // constant away from the buffer base keeps the compiler's alias
   // information for it.
   int voff[4];
@@ -691,13 +709,31 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
           if (koff >= nkeys) sacc[rr] = -INFINITY;
         }
       }
-      float mloc = sacc[0];
+      // Weights against the current reference max; the row max itself is
+      // only computed when some lane's 16 weights sum past 2^8 (or are not
+      // finite: the item's first sub-tile), which bounds every weight by 2^8
+      // as a per-sub-tile max test would.
+      bf16x8 pb0, pb1;
+      float ps;
+      auto weights = [&]() {
+        f32x8 p0, p1;
+        const float nm = -mref;
 #pragma unroll
-      for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, sacc[rr]);
-      mloc = max_with_partner(mloc);
-      const float mt = mloc * scale_log2;
-      if (__ballot(mt > mref + kLazy)) {
-        const float mnew = fmaxf(mref, mt);
+        for (int rr = 0; rr < 8; ++rr) {
+          p0[rr] = fast_exp2(fmaf(sacc[rr], scale_log2, nm));
+          p1[rr] = fast_exp2(fmaf(sacc[rr + 8], scale_log2, nm));
+        }
+        pb0 = __builtin_convertvector(p0, bf16x8);
+        pb1 = __builtin_convertvector(p1, bf16x8);
+        ps = row_sum16(pb0, pb1);
+      };
+      weights();
+      if (__ballot(!(ps <= kCap))) {
+        float mloc = sacc[0];
+#pragma unroll
+        for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, sacc[rr]);
+        mloc = max_with_partner(mloc);
+        const float mnew = fmaxf(mref, mloc * scale_log2);
         const float alpha = fast_exp2(mref - mnew);
         lsum *= alpha;
 #pragma unroll
@@ -705,18 +741,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
         mref = mnew;
-      }
-      f32x8 p0, p1;
-      float ps = 0.f;
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        p0[rr] = fast_exp2(fmaf(sacc[rr], scale_log2, -mref));
-        p1[rr] = fast_exp2(fmaf(sacc[rr + 8], scale_log2, -mref));
-        ps += p0[rr] + p1[rr];
+        weights();
       }
       lsum += ps;
-      const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
-      const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
       const char *vbase = reinterpret_cast<const char *>(cur.Vs);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
