@@ -211,8 +211,8 @@ def cpu_baseline(x, cfg, budget_s: float = 15.0):
     flops = 4.0 * cfg.d * cfg.Hq * sum(attended_pairs(int(p), 1, B, K) for p in rows)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"{n} random prefill queries of the 1M-token sequence "
-                      f"(select + attend, fp64), {dt:.1f} s; pool of all 1M "
+            "sample": f"{n} random prefill queries of the {T}-token sequence "
+                      f"(select + attend, fp64), {dt:.1f} s; pool of all {T} "
                       f"index keys not included"}
 
 
