@@ -134,7 +134,7 @@ def calibrate_copy(mib: int) -> None:
     print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
-def measure_dec16(dev, seed: int, reps: int = 100):
+def measure_dec16(dev, seed: int, reps: int = 100, with_cpu: bool = False):
     """Batched decode at the 16 x 256K-token cache workload: one fused decode
     step per sequence (append of the 262144th token, its block's running max,
     the index scan over every cached block summary, top-K, split-KV attention
@@ -177,13 +177,44 @@ def measure_dec16(dev, seed: int, reps: int = 100):
     us = min(times)
     nbytes = cfg.n_seq * decode_bytes(cfg.T, cfg)
     gbs = nbytes / (us * 1e-6) / 1e9
-    del x, kmax, bufs, g
+    res = {"workload": "dec16: 16 sequences x 262144-token bf16 cache, Hq 64 / Hkv 8, d 128, "
+                       "block 512, top-K 8; one fused decode step repeated "
+                       f"{reps}x in a graph, best of 3 replays",
+           "us_per_step": round(us, 3), "bytes_per_step": int(nbytes),
+           "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    del kmax, bufs, g
+    if with_cpu:
+        res["cpu_baseline"] = dec16_cpu_baseline(x, cfg)
+    del x
     torch.cuda.empty_cache()
-    return {"workload": "dec16: 16 sequences x 262144-token bf16 cache, Hq 64 / Hkv 8, d 128, "
-                        "block 512, top-K 8; one fused decode step repeated "
-                        f"{reps}x in a graph, best of 3 replays",
-            "us_per_step": round(us, 3), "bytes_per_step": int(nbytes),
-            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return res
+
+
+def dec16_cpu_baseline(x, cfg):
+    """The CPU oracle on the whole batched decode step (every sequence: pool of
+    its index keys, selection for the query at the last position, attention
+    over the selected blocks, fp64); host copies of the caches are not
+    timed."""
+    import oracle
+    oracle.build(force=False)
+    B, K, L = cfg.block, cfg.topk, cfg.T
+    pos = np.array([L - 1], np.int64)
+    dt = 0.0
+    for s in range(cfg.n_seq):
+        idx_k = x["idx_k"][s].cpu().numpy()
+        idx_q = x["idx_q"][s:s + 1].cpu().numpy()
+        q_h = synth.host(x["q"][s:s + 1])
+        k_h, v_h = synth.host(x["k_cache"][s]), synth.host(x["v_cache"][s])
+        t0 = time.perf_counter()
+        kmax = oracle.pool(idx_k, B)
+        sel, *_ = oracle.select(idx_q, pos, kmax, B, K)
+        oracle.attend(q_h, k_h, v_h, np.array([0]), pos, sel, B, cfg.scale, oracle.BF16)
+        dt += time.perf_counter() - t0
+        del k_h, v_h
+    return {"value": round(dt * 1e6, 1), "unit": "us/step", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"the whole step, all {cfg.n_seq} sequences (pool of each "
+                      f"sequence's {L} index keys, selection, attention), {dt:.2f} s"}
 
 
 def cpu_baseline(x, cfg, budget_s: float = 15.0):
@@ -412,7 +443,7 @@ def main():
     if not args.no_dec16:
         print("[bench] batched decode (dec16)", file=sys.stderr, flush=True)
         del bufs, dbufs, dec_graph
-        out["decode16"] = measure_dec16(dev, args.seed)
+        out["decode16"] = measure_dec16(dev, args.seed, with_cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(x, cfg)
