@@ -247,6 +247,7 @@ __global__ __launch_bounds__(256) void decode_attn(
 // so the compiler can tell the DMA into one from the reads of the other.
 // ---------------------------------------------------------------------------
 constexpr int kSK = 128;   // keys per streamed chunk (one per wave quarter)
+constexpr float kDecLazy = 8.f;   // reference-max slack (log2 units)
 
 struct StreamBuf {
   uint16_t Ks[kSK * 128];
@@ -521,22 +522,27 @@ __global__ __launch_bounds__(256) void decode_stream(
       float mloc = x[0];
 #pragma unroll
       for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, x[rr]);
-      const float mnew = fmaxf(m, max_with_partner(mloc));   // finite: key k0 is valid
-      const float alpha = fast_exp2(m - mnew);
+      // lazy rescale: the reference max moves only when the row max passes it
+      // by more than 8, so every weight is at most 2^8
+      const float mt = fmaxf(m, max_with_partner(mloc));   // finite: key k0 is valid
+      if (__ballot(mt > m + kDecLazy)) {
+        const float alpha = fast_exp2(m - mt);
+        l *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+        m = mt;
+      }
       f32x8 p0, p1;
       float ps = 0.f;
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
-        p0[rr] = fast_exp2(x[rr] - mnew);
-        p1[rr] = fast_exp2(x[rr + 8] - mnew);
+        p0[rr] = fast_exp2(x[rr] - m);
+        p1[rr] = fast_exp2(x[rr + 8] - m);
         ps += p0[rr] + p1[rr];
       }
-      l = fmaf(l, alpha, sum_with_partner(ps));
-      m = mnew;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+      l += sum_with_partner(ps);
       const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
       const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
       const char *vbase = reinterpret_cast<const char *>(cur.Vs);
@@ -861,22 +867,27 @@ __global__ __launch_bounds__(256) void decode_paged(
       float mloc = x[0];
 #pragma unroll
       for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, x[rr]);
-      const float mnew = fmaxf(m, max_with_partner(mloc));
-      const float alpha = fast_exp2(m - mnew);
+      // lazy rescale: the reference max moves only when the row max passes it
+      // by more than 8, so every weight is at most 2^8
+      const float mt = fmaxf(m, max_with_partner(mloc));
+      if (__ballot(mt > m + kDecLazy)) {
+        const float alpha = fast_exp2(m - mt);
+        l *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+        m = mt;
+      }
       f32x8 p0, p1;
       float ps = 0.f;
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
-        p0[rr] = fast_exp2(x[rr] - mnew);
-        p1[rr] = fast_exp2(x[rr + 8] - mnew);
+        p0[rr] = fast_exp2(x[rr] - m);
+        p1[rr] = fast_exp2(x[rr + 8] - m);
         ps += p0[rr] + p1[rr];
       }
-      l = fmaf(l, alpha, sum_with_partner(ps));
-      m = mnew;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+      l += sum_with_partner(ps);
       const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
       const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
       const char *vbase = reinterpret_cast<const char *>(cur.Vs);
@@ -1218,22 +1229,27 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
       float mloc = x[0];
 #pragma unroll
       for (int rr = 1; rr < 16; ++rr) mloc = fmaxf(mloc, x[rr]);
-      const float mnew = fmaxf(m, max_with_partner(mloc));
-      const float alpha = fast_exp2(m - mnew);
+      // lazy rescale: the reference max moves only when the row max passes it
+      // by more than 8, so every weight is at most 2^8
+      const float mt = fmaxf(m, max_with_partner(mloc));
+      if (__ballot(mt > m + kDecLazy)) {
+        const float alpha = fast_exp2(m - mt);
+        l *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+        m = mt;
+      }
       f32x8 p0, p1;
       float ps = 0.f;
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
-        p0[rr] = fast_exp2(x[rr] - mnew);
-        p1[rr] = fast_exp2(x[rr + 8] - mnew);
+        p0[rr] = fast_exp2(x[rr] - m);
+        p1[rr] = fast_exp2(x[rr + 8] - m);
         ps += p0[rr] + p1[rr];
       }
-      l = fmaf(l, alpha, sum_with_partner(ps));
-      m = mnew;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[cb][rr] *= alpha;
+      l += sum_with_partner(ps);
       const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
       const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
 #pragma unroll
