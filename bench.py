@@ -217,6 +217,141 @@ def dec16_cpu_baseline(x, cfg):
                       f"sequence's {L} index keys, selection, attention), {dt:.2f} s"}
 
 
+def _graph_us(fn, reps: int = 20) -> float:
+    """Best of three replays of `reps` captured calls, µs per call."""
+    st = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        g.replay()
+        b.record(st)
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e3 / reps)
+    return best
+
+
+def _event_ms(fn, reps: int = 5) -> float:
+    """Mean over `reps` eager calls after one warm-up, ms per call."""
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def measure_next(dev, seed: int) -> dict:
+    """The rows past the default path, each against its own roofline:
+    several sequences per prefill call (chunks of queries against their
+    caches, and many short requests), the paged bf16 / FP8 decode attention
+    at the batched decode shape, and the index variants (mean-pool, forced
+    local window) beside the default max-pool and top-K."""
+    out = {"metric": "next-row measurements (one GPU)", "data": "synthetic, seeded"}
+    # -- several sequences per call: the 32K-token workload's sequence packed
+    cfg = synth.CONFIGS["p32k"]
+    x = synth.sequence_inputs(cfg, dev, seed)
+    B, K, d, hq = cfg.block, cfg.topk, cfg.d, cfg.Hq
+    for name, n_seq, L, nq in (("chunks", 8, cfg.T, 8192), ("short", 64, 2048, 2048)):
+        cu_q = np.arange(n_seq + 1, dtype=np.int64) * nq
+        cu_kv = np.arange(n_seq + 1, dtype=np.int64) * L
+        q = x["q"][L - nq:L].repeat(n_seq, 1, 1).contiguous()
+        iq = x["idx_q"][L - nq:L].repeat(n_seq, 1).contiguous()
+        k = x["k"][:, :L].repeat(1, n_seq, 1).contiguous()
+        v = x["v"][:, :L].repeat(1, n_seq, 1).contiguous()
+        ik = x["idx_k"][:L].repeat(n_seq, 1).contiguous()
+        ms = _event_ms(lambda: ops.msa_prefill_varlen(q, k, v, iq, ik, cu_q, cu_kv, B, K,
+                                                      cfg.scale))
+        flop = 4.0 * d * hq * n_seq * attended_pairs(L - nq, nq, B, K)
+        out[f"varlen_{name}"] = {
+            "workload": f"{n_seq} sequences x {L}-token cache, last {nq} tokens as queries, "
+                        f"Hq {hq} / Hkv {cfg.Hkv}, d {d}, block {B}, top-K {K}",
+            "ms_per_call": round(ms, 3), "attended_tflops": round(flop / ms / 1e9, 1),
+            "frac_bf16_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        del q, iq, k, v, ik
+    del x
+    torch.cuda.empty_cache()
+    # -- paged bf16 / FP8 decode attention at the batched decode shape
+    cfg = synth.CONFIGS["dec16"]
+    n, B, K, hq, hkv, d = cfg.n_seq, cfg.block, cfg.topk, cfg.Hq, cfg.Hkv, cfg.d
+    nb = cfg.T // B
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    q = torch.randn((n, hq, d), device=dev, generator=g).to(torch.bfloat16)
+    seq = torch.full((n,), cfg.T, dtype=torch.int64, device=dev)
+    sel = torch.stack([torch.sort(torch.randperm(nb - 1, device=dev, generator=g)[:K - 1]).values
+                       for _ in range(n)])
+    sel = torch.cat([sel, torch.full((n, 1), nb - 1, device=dev)], 1).to(torch.int32).contiguous()
+    table = torch.randperm(n * nb, device=dev, generator=g).to(torch.int32).view(n, nb).contiguous()
+    ws = torch.empty(ops.load().msa_decode_workspace_bytes(n, hq, d, B, K), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty((n, hq, d), device=dev)
+    lse = torch.empty((n, hq), device=dev)
+    kv_elems = n * hkv * K * B * d
+    kp = torch.randn((n * nb, hkv, B, d), device=dev, generator=g).to(torch.bfloat16)
+    vp = torch.randn((n * nb, hkv, B, d), device=dev, generator=g).to(torch.bfloat16)
+    us = _graph_us(lambda: ops.msa_sparse_gqa_decode_paged(q, kp, vp, table, seq, sel, B,
+                                                           o=o, lse=lse, ws=ws))
+    out["paged_bf16"] = {"workload": f"{n} sequences x {cfg.T} tokens in {B}-key pages, top-K {K}",
+                         "us_per_step": round(us, 2),
+                         "kv_gbs": round(kv_elems * 4 / (us * 1e-6) / 1e9, 1),
+                         "hbm_frac": round(kv_elems * 4 / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del kp, vp
+    torch.cuda.empty_cache()
+    kp = torch.randn((n * nb, hkv, B, d), device=dev, generator=g).to(torch.float8_e4m3fn)
+    vp = torch.randn((n * nb, hkv, B, d), device=dev, generator=g).to(torch.float8_e4m3fn)
+    ks = torch.rand((n * nb, hkv), device=dev, generator=g) + 0.5
+    vs = torch.rand((n * nb, hkv), device=dev, generator=g) + 0.5
+    us = _graph_us(lambda: ops.msa_sparse_gqa_decode_paged(q, kp, vp, table, seq, sel, B,
+                                                           k_scale=ks, v_scale=vs, o=o, lse=lse,
+                                                           ws=ws))
+    out["paged_fp8"] = {"workload": out["paged_bf16"]["workload"] + ", e4m3 K/V",
+                        "us_per_step": round(us, 2),
+                        "kv_gbs": round(kv_elems * 2 / (us * 1e-6) / 1e9, 1),
+                        "hbm_frac": round(kv_elems * 2 / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del kp, vp, ks, vs, q, o, lse, ws
+    torch.cuda.empty_cache()
+    # -- index variants next to the default rule
+    T1, B1, di = 1 << 20, 512, 128
+    ik = torch.randn((T1, di), device=dev, generator=g)
+    nb1 = T1 // B1
+    pool_bytes = T1 * di * 4 + nb1 * di * 4
+    km = torch.empty((nb1, di), device=dev)
+    for name, fn in (("pool_max", lambda: ops.msa_index_pool(ik, B1, kmax=km)),
+                     ("pool_mean", lambda: ops.msa_index_pool_mean(ik, B1, kmean=km))):
+        us = _graph_us(fn)
+        out[name] = {"workload": f"{T1} index keys, d_idx {di}, block {B1}",
+                     "us": round(us, 2), "gbs": round(pool_bytes / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(pool_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del ik, km
+    cfg = synth.CONFIGS["p128k"]
+    T2, B2, K2 = cfg.T, cfg.block, cfg.topk
+    iq = torch.randn((T2, di), device=dev, generator=g)
+    kmax = torch.randn((T2 // B2, di), device=dev, generator=g)
+    p = np.arange(T2, dtype=np.int64)
+    flop = 2 * di * int((p // B2).sum())
+    for name, fn in (("topk", lambda: ops.msa_index_topk(iq, kmax, B2, K2)),
+                     ("topk_window4", lambda: ops.msa_index_topk_window(iq, kmax, B2, K2, 4))):
+        ms = _event_ms(fn)
+        out[name] = {"workload": f"{T2} queries x {T2 // B2} blocks, d_idx {di}, top-K {K2}",
+                     "ms": round(ms, 3), "tflops": round(flop / ms / 1e9, 2),
+                     "frac_fp32_peak": round(flop / ms / 1e9 / PEAK_F32_TFLOPS, 4)}
+    return out
+
+
 def cpu_baseline(x, cfg, budget_s: float = 15.0):
     """Time the CPU oracle on a bounded sample of the same workload: the
     index branch and attention for a random sample of prefill queries."""
@@ -267,6 +402,9 @@ def main():
     ap.add_argument("--no-dec16", action="store_true",
                     help="skip the batched-decode (16 x 256K cache) measurement")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--next", action="store_true",
+                    help="only measure the rows past the default path (several sequences per "
+                         "call, paged / FP8 decode, index variants); prints one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -278,6 +416,12 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.next:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        ops.load()
+        print(json.dumps(measure_next(dev, args.seed)), flush=True)
         return
 
     cfg = synth.CONFIGS[args.config]

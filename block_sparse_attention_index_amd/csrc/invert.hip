@@ -20,17 +20,25 @@
 namespace msa {
 namespace {
 
-constexpr int kTQ = 1024;   // queries per tile
 constexpr int kNR = 4096;   // blocks per LDS range
+
+// Queries per tile: the smallest power of two from 64 to 1024 that keeps the
+// tile count at most 256, so that a short query range still spreads over many
+// workgroups (each tile's scatter walks its queries 64 at a time).
+int tile_q(int64_t n_q) {
+  int tq = 64;
+  while (tq < 1024 && (n_q + tq - 1) / tq > 256) tq *= 2;
+  return tq;
+}
 
 __global__ __launch_bounds__(256) void inv_hist(const int32_t *__restrict__ sel,
                                                 int64_t n_q, int topk,
-                                                int64_t nb,
+                                                int64_t nb, int tq,
                                                 int32_t *__restrict__ hist) {
   __shared__ int cnt[kNR];
   const int64_t t = blockIdx.x;
-  const int64_t i0 = t * kTQ;
-  const int64_t nt = (n_q - i0 < kTQ ? n_q - i0 : kTQ) * topk;
+  const int64_t i0 = t * tq;
+  const int64_t nt = (n_q - i0 < tq ? n_q - i0 : tq) * topk;
   const int32_t *s = sel + i0 * topk;
   for (int64_t r0 = 0; r0 < nb; r0 += kNR) {
     const int nr = (int)(nb - r0 < kNR ? nb - r0 : kNR);
@@ -91,14 +99,14 @@ __global__ __launch_bounds__(1024) void inv_rowptr(const int32_t *__restrict__ t
 }
 
 __global__ __launch_bounds__(64) void inv_scatter(
-    const int32_t *__restrict__ sel, int64_t n_q, int topk, int64_t nb,
+    const int32_t *__restrict__ sel, int64_t n_q, int topk, int64_t nb, int tq,
     const int32_t *__restrict__ base, const int32_t *__restrict__ row_ptr,
     int32_t *__restrict__ q_list, int32_t *__restrict__ slot) {
   __shared__ int32_t cursor[kNR];
   __shared__ unsigned long long bits[kNR];
   const int lane = threadIdx.x;
   const int64_t t = blockIdx.x;
-  const int64_t i0 = t * kTQ;
+  const int64_t i0 = t * tq;
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int64_t r0 = 0; r0 < nb; r0 += kNR) {
     const int nr = (int)(nb - r0 < kNR ? nb - r0 : kNR);
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(64) void inv_scatter(
       bits[j] = 0ull;
     }
     __syncthreads();
-    for (int sub = 0; sub < kTQ / 64; ++sub) {
+    for (int sub = 0; sub < tq / 64; ++sub) {
       const int64_t i = i0 + sub * 64 + lane;
       if (i0 + sub * 64 >= n_q) break;
       const bool act = i < n_q;
@@ -147,7 +155,12 @@ __global__ __launch_bounds__(64) void inv_scatter(
 
 size_t invert_ws_bytes(int64_t n_q, int32_t topk, int64_t n_blocks) {
   (void)topk;
-  const int64_t n_tiles = (n_q + kTQ - 1) / kTQ;
+  // the most tiles any range of at most n_q queries uses (tile_q grows with
+  // the range, so a shorter range can use more tiles than n_q itself)
+  const int64_t n_small = (n_q + 63) / 64;
+  const int64_t n_tiles_small = n_small < 256 ? n_small : 256;
+  const int64_t n_tiles_large = (n_q + 1023) / 1024;
+  const int64_t n_tiles = n_tiles_small > n_tiles_large ? n_tiles_small : n_tiles_large;
   return align256((size_t)(n_tiles > 0 ? n_tiles : 1) * n_blocks * 4) +
          align256((size_t)n_blocks * 4);
 }
@@ -155,14 +168,15 @@ size_t invert_ws_bytes(int64_t n_q, int32_t topk, int64_t n_blocks) {
 hipError_t launch_invert(const int32_t *sel, int64_t n_q, int32_t topk,
                          int64_t n_blocks, int32_t *row_ptr, int32_t *q_list,
                          int32_t *slot, void *ws, hipStream_t st) {
-  const int64_t n_tiles = (n_q + kTQ - 1) / kTQ;
+  const int tq = tile_q(n_q);
+  const int64_t n_tiles = (n_q + tq - 1) / tq;
+  const size_t ws_all = invert_ws_bytes(n_q, topk, n_blocks);
   int32_t *hist = static_cast<int32_t *>(ws);
   int32_t *total = reinterpret_cast<int32_t *>(
-      static_cast<char *>(ws) +
-      align256((size_t)(n_tiles > 0 ? n_tiles : 1) * n_blocks * 4));
+      static_cast<char *>(ws) + ws_all - align256((size_t)n_blocks * 4));
   if (n_tiles > 0) {
     hipLaunchKernelGGL(inv_hist, dim3((unsigned)n_tiles), dim3(256), 0, st, sel,
-                       n_q, topk, n_blocks, hist);
+                       n_q, topk, n_blocks, tq, hist);
   }
   hipLaunchKernelGGL(inv_colscan, dim3((unsigned)((n_blocks + 255) / 256)),
                      dim3(256), 0, st, hist, n_tiles, n_blocks, total);
@@ -170,7 +184,7 @@ hipError_t launch_invert(const int32_t *sel, int64_t n_q, int32_t topk,
                      row_ptr);
   if (n_tiles > 0) {
     hipLaunchKernelGGL(inv_scatter, dim3((unsigned)n_tiles), dim3(64), 0, st,
-                       sel, n_q, topk, n_blocks, hist, row_ptr, q_list, slot);
+                       sel, n_q, topk, n_blocks, tq, hist, row_ptr, q_list, slot);
   }
   return hipGetLastError();
 }
