@@ -19,6 +19,37 @@ constexpr int64_t kMaxGridY = 65535;
 // (sequence, KV head, selected block) work items of one decode call: the
 // streaming kernel numbers their segments in 32 bits
 constexpr int64_t kMaxDecodeItems = int64_t(1) << 28;
+// Shape limits that keep every byte count below 2^60 (they are computed in
+// 64-bit arithmetic): token positions and counts, heads, head size.
+constexpr int64_t kMaxTokens = int64_t(1) << 40;
+constexpr int64_t kMaxHeads = int64_t(1) << 16;
+constexpr int32_t kMaxD = 1024;
+bool bytes_fit(__int128 x) { return x >= 0 && x < ((__int128)1 << 60); }
+// n_q * topk < 2^31 - 1 (query-block pairs are numbered in 32 bits), without
+// forming the product
+bool pairs_ok(int64_t n_q, int32_t topk) {
+  return n_q >= 0 && topk >= 1 && n_q <= (int64_t)(INT32_MAX - 1) / topk;
+}
+// Partial records of a prefill call: at most (q_pos0 + n_q) * (K - 1) pairs,
+// each Hq * (d + 2) floats, plus per-block tables.
+bool prefill_shape_ok(int64_t q_pos0, int64_t n_q, int32_t hq, int32_t d, int32_t block,
+                      int32_t topk) {
+  if (q_pos0 < 0 || n_q < 0 || q_pos0 > kMaxTokens || n_q > kMaxTokens || hq < 1 ||
+      hq > kMaxHeads || d < 1 || d > kMaxD)
+    return false;
+  const __int128 toks = (__int128)q_pos0 + n_q;
+  return bytes_fit(toks * topk * hq * (d + 2) * 4 + (toks / block + 1) * 4096);
+}
+// Decode partials: one record of Hq * (d + 1) floats per (sequence, selected
+// block, 128-key segment), plus the scan's candidate lists.
+bool decode_shape_ok(int32_t n_seq, int64_t nb_max, int32_t hq, int32_t d, int32_t block,
+                     int32_t topk) {
+  if (n_seq < 1 || n_seq > kMaxGridY || nb_max < 1 || nb_max > INT32_MAX || hq < 1 ||
+      hq > kMaxHeads || d < 1 || d > kMaxD)
+    return false;
+  return bytes_fit((__int128)n_seq * hq * topk * ((block + 127) / 128) * (d + 1) * 4 +
+                   (__int128)n_seq * (nb_max / 64 + 1) * topk * 8);
+}
 
 bool block_ok(int32_t b) { return b >= 16 && b <= kMaxBlock && b % 16 == 0; }
 bool topk_ok(int32_t k) { return k >= 1 && k <= kMaxTopk; }
@@ -149,7 +180,8 @@ int msa_index_topk(const float *idx_q, int64_t n_q, int64_t q_pos0,
 
 size_t msa_topk_decode_workspace_bytes(int32_t n_seq, int64_t nb_max,
                                        int32_t topk) {
-  if (n_seq < 1 || nb_max < 1 || !topk_ok(topk)) return 0;
+  if (n_seq < 1 || n_seq > kMaxGridY || nb_max < 1 || nb_max > INT32_MAX || !topk_ok(topk))
+    return 0;
   return msa::topk_decode_ws_bytes(n_seq, nb_max, topk);
 }
 
@@ -180,7 +212,8 @@ int msa_index_topk_decode(const float *idx_q, int32_t n_seq,
 }
 
 size_t msa_invert_workspace_bytes(int64_t n_q, int32_t topk, int64_t n_blocks) {
-  if (n_q < 0 || !topk_ok(topk) || n_blocks < 1) return 0;
+  if (!topk_ok(topk) || !pairs_ok(n_q, topk) || n_blocks < 1 || n_blocks >= INT32_MAX)
+    return 0;
   return msa::invert_ws_bytes(n_q, topk, n_blocks);
 }
 
@@ -188,9 +221,8 @@ int msa_invert_selection(const int32_t *sel, int64_t n_q, int32_t topk,
                          int64_t n_blocks, int32_t *row_ptr, int32_t *q_list,
                          int32_t *slot, void *ws, size_t ws_bytes,
                          void *stream) {
-  if (!sel || !row_ptr || !q_list || !slot || !ws || n_q < 0 ||
-      !topk_ok(topk) || n_blocks < 1 || n_blocks >= INT32_MAX ||
-      n_q * (int64_t)topk >= INT32_MAX)
+  if (!sel || !row_ptr || !q_list || !slot || !ws || !topk_ok(topk) ||
+      !pairs_ok(n_q, topk) || n_blocks < 1 || n_blocks >= INT32_MAX)
     return MSA_ERR_INVALID_ARG;
   if (ws_bytes < msa::invert_ws_bytes(n_q, topk, n_blocks))
     return MSA_ERR_WORKSPACE;
@@ -201,8 +233,8 @@ int msa_invert_selection(const int32_t *sel, int64_t n_q, int32_t topk,
 size_t msa_prefill_workspace_bytes(int32_t dtype, int64_t q_pos0, int64_t n_q,
                                    int32_t hq, int32_t d, int32_t block,
                                    int32_t topk) {
-  if ((dtype != MSA_F32 && dtype != MSA_BF16) || q_pos0 < 0 || n_q < 0 ||
-      hq < 1 || d < 1 || !block_ok(block) || !topk_ok(topk))
+  if ((dtype != MSA_F32 && dtype != MSA_BF16) || !block_ok(block) || !topk_ok(topk) ||
+      !prefill_shape_ok(q_pos0, n_q, hq, d, block, topk))
     return 0;
   return msa::prefill_ws_bytes(dtype, q_pos0, n_q, hq, d, block, topk);
 }
@@ -216,10 +248,10 @@ int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
                            float *lse, void *ws, size_t ws_bytes,
                            void *stream) {
   if (!q || !k || !v || !sel || !row_ptr || !q_list || !slot || !o || !ws ||
-      (dtype != MSA_F32 && dtype != MSA_BF16) || n_q < 0 || q_pos0 < 0 ||
-      hq < 1 || hkv < 1 || hkv > kMaxGridY || hq % hkv != 0 || d < 1 ||
-      !block_ok(block) || !topk_ok(topk) || !std::isfinite(scale) ||
-      q_pos0 + n_q > kv_stride || n_q * (int64_t)topk >= INT32_MAX)
+      (dtype != MSA_F32 && dtype != MSA_BF16) || !block_ok(block) || !topk_ok(topk) ||
+      !prefill_shape_ok(q_pos0, n_q, hq, d, block, topk) || hkv < 1 || hkv > kMaxGridY ||
+      hq % hkv != 0 || !std::isfinite(scale) || q_pos0 + n_q > kv_stride ||
+      !pairs_ok(n_q, topk))
     return MSA_ERR_INVALID_ARG;
   if (!msa::prefill_supported(dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
   if (n_q == 0) return MSA_OK;
@@ -244,8 +276,12 @@ bool varlen_lens_ok(int32_t n_seq, const int64_t *cu_q, const int64_t *cu_kv) {
   if (!cu_q || !cu_kv || n_seq < 1 || n_seq > kMaxGridY || cu_q[0] != 0 || cu_kv[0] != 0)
     return false;
   for (int32_t s = 0; s < n_seq; ++s) {
+    // offsets in [0, 2^40] first, so the differences cannot overflow
+    if (cu_q[s + 1] < 0 || cu_q[s + 1] > kMaxTokens || cu_kv[s + 1] < 0 ||
+        cu_kv[s + 1] > kMaxTokens)
+      return false;
     const int64_t qn = cu_q[s + 1] - cu_q[s], kvn = cu_kv[s + 1] - cu_kv[s];
-    if (qn < 0 || kvn < 0 || qn > kvn || qn * (int64_t)kMaxTopk >= INT32_MAX) return false;
+    if (qn < 0 || kvn < 0 || qn > kvn || !pairs_ok(qn, kMaxTopk)) return false;
   }
   return true;
 }
@@ -282,7 +318,8 @@ size_t msa_prefill_varlen_workspace_bytes(int32_t dtype, int32_t n_seq, const in
                                           const int64_t *cu_kv, int32_t hq, int32_t d,
                                           int32_t d_idx, int32_t block, int32_t topk) {
   if ((dtype != MSA_F32 && dtype != MSA_BF16) || !varlen_lens_ok(n_seq, cu_q, cu_kv) ||
-      hq < 1 || d < 1 || !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk))
+      !prefill_shape_ok(0, cu_kv[n_seq], hq, d, block, kMaxTopk) || !didx_ok(d_idx) ||
+      !block_ok(block) || !topk_ok(topk))
     return 0;
   return varlen_layout(dtype, n_seq, cu_q, cu_kv, hq, d, d_idx, block, topk).total;
 }
@@ -295,7 +332,8 @@ int msa_prefill_varlen(const void *q, const void *k, const void *v, const float 
   if (!q || !k || !v || !idx_q || !idx_k || !sel || !o || !ws ||
       (dtype != MSA_F32 && dtype != MSA_BF16) || !varlen_lens_ok(n_seq, cu_q, cu_kv) ||
       hq < 1 || hkv < 1 || hkv > kMaxGridY || hq % hkv != 0 || d < 1 || !didx_ok(d_idx) ||
-      !block_ok(block) || !topk_ok(topk) || !std::isfinite(scale))
+      !block_ok(block) || !topk_ok(topk) || !std::isfinite(scale) ||
+      !prefill_shape_ok(0, cu_kv[n_seq], hq, d, block, kMaxTopk))
     return MSA_ERR_INVALID_ARG;
   if (!msa::prefill_supported(dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
   const VarlenLayout L = varlen_layout(dtype, n_seq, cu_q, cu_kv, hq, d, d_idx, block, topk);
@@ -336,7 +374,7 @@ int msa_prefill_varlen(const void *q, const void *k, const void *v, const float 
 
 size_t msa_decode_workspace_bytes(int32_t n_seq, int32_t hq, int32_t d,
                                   int32_t block, int32_t topk) {
-  if (n_seq < 1 || hq < 1 || d < 1 || !block_ok(block) || !topk_ok(topk))
+  if (!block_ok(block) || !topk_ok(topk) || !decode_shape_ok(n_seq, 1, hq, d, block, topk))
     return 0;
   return msa::decode_ws_bytes(n_seq, hq, d, block, topk);
 }
@@ -353,7 +391,8 @@ int msa_sparse_gqa_decode(const void *q, const void *k_cache,
       n_seq > kMaxGridY || len_max < 1 || hq < 1 || hkv < 1 ||
       hkv > kMaxGridY || hq % hkv != 0 || d < 1 || !block_ok(block) ||
       !topk_ok(topk) || !std::isfinite(scale) ||
-      (int64_t)n_seq * hkv * topk > kMaxDecodeItems)
+      (int64_t)n_seq * hkv * topk > kMaxDecodeItems ||
+      !decode_shape_ok(n_seq, 1, hq, d, block, topk))
     return MSA_ERR_INVALID_ARG;
   if (!msa::decode_supported(dtype, d, hq / hkv) ||
       !msa::decode_partials_ok(dtype, d, hq / hkv, block, topk))
@@ -380,7 +419,8 @@ int msa_sparse_gqa_decode_paged(const void *q, const void *k_pages, const void *
       max_blocks < 1 || n_seq < 1 || n_seq > kMaxGridY || hq < 1 || hkv < 1 ||
       hq % hkv != 0 || d < 1 || !block_ok(block) || !topk_ok(topk) ||
       !std::isfinite(scale) || (int64_t)n_seq * hkv * topk > kMaxDecodeItems ||
-      (int64_t)n_pages * hkv * block > (int64_t(1) << 40))
+      (int64_t)n_pages * hkv * block > (int64_t(1) << 40) ||
+      !decode_shape_ok(n_seq, max_blocks, hq, d, block, topk))
     return MSA_ERR_INVALID_ARG;
   if (!msa::decode_paged_supported(kv_dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
   if (ws_bytes < msa::decode_ws_bytes(n_seq, hq, d, block, topk)) return MSA_ERR_WORKSPACE;
@@ -392,7 +432,7 @@ int msa_sparse_gqa_decode_paged(const void *q, const void *k_pages, const void *
 
 size_t msa_decode_step_workspace_bytes(int32_t n_seq, int64_t nb_max, int32_t hq,
                                        int32_t d, int32_t block, int32_t topk) {
-  if (n_seq < 1 || nb_max < 1 || hq < 1 || d < 1 || !block_ok(block) || !topk_ok(topk))
+  if (!block_ok(block) || !topk_ok(topk) || !decode_shape_ok(n_seq, nb_max, hq, d, block, topk))
     return 0;
   return msa::decode_step_ws_bytes(n_seq, nb_max, hq, d, block, topk);
 }
@@ -410,7 +450,8 @@ int msa_decode_step(const void *q, const void *k_new, const void *v_new,
       n_seq < 1 || n_seq > kMaxGridY || len_max < 1 || nb_max < 1 ||
       nb_max > INT32_MAX || hq < 1 || hkv < 1 || hq % hkv != 0 || d < 1 ||
       !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk) || !std::isfinite(scale) ||
-      (int64_t)n_seq * hkv * topk > kMaxDecodeItems)
+      (int64_t)n_seq * hkv * topk > kMaxDecodeItems ||
+      !decode_shape_ok(n_seq, nb_max, hq, d, block, topk))
     return MSA_ERR_INVALID_ARG;
   if (!msa::decode_step_supported(dtype, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
   if (ws_bytes < msa::decode_step_ws_bytes(n_seq, nb_max, hq, d, block, topk))
@@ -422,3 +463,4 @@ int msa_decode_step(const void *q, const void *k_new, const void *v_new,
 }
 
 }  // extern "C"
+

@@ -25,15 +25,20 @@
 namespace msa {
 
 int64_t nonown_pairs(int64_t q_pos0, int64_t n_q, int32_t block, int32_t topk) {
-  int64_t total = 0;
+  // A token of block b keeps min(K, b + 1) - 1 non-own blocks: b of them for
+  // the first K - 1 blocks, K - 1 from block K - 1 on.  Sum the first blocks
+  // one by one (at most K - 1 of them), the rest in closed form.
   if (n_q <= 0) return 0;
-  const int64_t b_first = q_pos0 / block, b_last = (q_pos0 + n_q - 1) / block;
-  for (int64_t b = b_first; b <= b_last; ++b) {
-    int64_t lo = b * block > q_pos0 ? b * block : q_pos0;
-    int64_t hi = (b + 1) * block < q_pos0 + n_q ? (b + 1) * block : q_pos0 + n_q;
-    const int64_t keep = (b + 1) < topk ? (b + 1) : topk;   // min(K, own+1)
-    total += (hi - lo) * (keep - 1);
+  const int64_t p0 = q_pos0, p1 = q_pos0 + n_q;       // tokens [p0, p1)
+  const int64_t full_from = (int64_t)(topk - 1) * block;   // first token of block K-1
+  int64_t total = 0;
+  for (int64_t b = p0 / block; b < topk - 1 && b * block < p1; ++b) {
+    const int64_t lo = b * block > p0 ? b * block : p0;
+    const int64_t hi = (b + 1) * block < p1 ? (b + 1) * block : p1;
+    total += (hi - lo) * b;
   }
+  const int64_t lo = p0 > full_from ? p0 : full_from;
+  if (p1 > lo) total += (p1 - lo) * (int64_t)(topk - 1);
   return total;
 }
 

@@ -3,9 +3,9 @@ decode step.  They only order calls and size buffers; all arithmetic runs in
 the library's kernels.
 
 Prefill ([CXT] section 3.3: every query scores every earlier block): pool the
-index keys, select per query, then -- per chunk of queries, so the partial
-outputs of the KV-outer pass fit in HBM -- build the chunk's CSR and run the
-sparse GQA.  Decode (same section: only the new query is scored): re-pool the
+index keys, select per query, then build the CSR and run the sparse GQA --
+over all queries at once when the partial outputs of the KV-outer pass fit in
+free HBM (so each KV block is read by one pass), else per chunk of queries.  Decode (same section: only the new query is scored): re-pool the
 block that holds each sequence's newest token, select for the new query, and
 attend over the selected blocks.
 
@@ -38,9 +38,9 @@ class PrefillBuffers:
 
 
 def default_chunk(dtype: int, T: int, hq: int, d: int, block: int, topk: int,
-                  budget_bytes: int = 48 << 30) -> int:
+                  budget_bytes: int) -> int:
     """Largest power-of-two query chunk (>= one block) whose prefill
-    workspace fits ``budget_bytes``."""
+    workspace fits ``budget_bytes``; the whole sequence when it fits."""
     c = 1 << max(0, (T - 1).bit_length())
     while c > block and ops.prefill_workspace_bytes(dtype, T - c if T > c else 0, min(c, T),
                                                      hq, d, block, topk) > budget_bytes:
@@ -49,12 +49,23 @@ def default_chunk(dtype: int, T: int, hq: int, d: int, block: int, topk: int,
 
 
 def alloc_prefill(q, idx_q, block: int, topk: int, chunk: int | None = None,
-                  budget_bytes: int = 48 << 30) -> PrefillBuffers:
+                  budget_bytes: int | None = None, headroom_bytes: int = 8 << 30) -> PrefillBuffers:
+    """Buffers for :func:`prefill`.  With no ``chunk`` and no
+    ``budget_bytes``, the partial-record workspace may take the device memory
+    that is free once the outputs are allocated, less ``headroom_bytes``: one
+    chunk covers the whole sequence whenever it fits (each KV block is then
+    streamed by a single pass over all queries), and long sequences fall back
+    to query chunks, which re-stream the blocks before each chunk."""
     T, hq, d = q.shape
     dev = q.device
     nb = -(-T // block)
     code = ops._dtype_code(q)
-    chunk = chunk or default_chunk(code, T, hq, d, block, topk, budget_bytes)
+    if chunk is None:
+        if budget_bytes is None:
+            free, _ = torch.cuda.mem_get_info(dev)
+            outputs = T * hq * (d + 1) * 4 + T * topk * 4 * 3 + nb * idx_q.shape[1] * 4
+            budget_bytes = max(1 << 30, free - outputs - headroom_bytes)
+        chunk = default_chunk(code, T, hq, d, block, topk, budget_bytes)
     lib = ops.load()
     # the largest workspace is the last chunk's (most non-own pairs)
     ws_attn = max(lib.msa_prefill_workspace_bytes(code, c0, min(chunk, T - c0), hq, d, block,

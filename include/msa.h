@@ -35,7 +35,9 @@
  *     calls from several host threads are safe.
  *   - Block size B: a multiple of 16, at most 4096.  Top-K: 1 <= K <= 64.
  *     Index dimension d_idx: 1..1024 (multiples of 4 up to 1024, any value up
- *     to 256).
+ *     to 256).  Token positions and counts are at most 2^40, Hq at most
+ *     65536 and d at most 1024; a shape whose workspace would reach 2^60
+ *     bytes is refused (MSA_ERR_INVALID_ARG, and its size query returns 0).
  *   - Positions count from 0.  own(p) = p / B is a token's own block.
  */
 #ifndef MSA_H

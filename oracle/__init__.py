@@ -32,11 +32,11 @@ F32, BF16 = 0, 1
 
 
 def build(force: bool = True) -> str:
-    """Compile ``msa_oracle.c`` into ``liboracle.so`` with gcc (-O2, OpenMP)."""
+    """Compile ``msa_oracle.c`` into ``liboracle.so`` with gcc (-O3 without fast-math, OpenMP)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call([
-            "gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC",
+            "gcc", "-O3", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC",
             "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
@@ -61,6 +61,7 @@ def _load():
         lib.oracle_attend.argtypes = [P, P, P, i32, i64, P, P, P, i32, i32, i32,
                                       i32, i32, i64, f64, P, P, P]
         lib.oracle_counts.argtypes = [P, i64, i32, P, i32, P, P]
+        lib.oracle_dequant_e4m3.argtypes = [P, i64, i32, i64, P, P]
         _lib = lib
     return _lib
 
@@ -196,3 +197,20 @@ def counts(sel: np.ndarray, q_pos: np.ndarray, block: int):
     if rc:
         raise ValueError("oracle_counts: invalid arguments")
     return nnz.value, att.value
+
+
+def dequant_e4m3(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 KV pages to fp32 [CXT §3.3: KV kept in blocks, in reduced
+    precision].  ``codes`` [n_pages, Hkv, ...] uint8 (OCP e4m3 bit patterns,
+    no infinities), ``scale`` [n_pages, Hkv] fp32 -> fp32 of the shape of
+    ``codes``: scale times the code's value, rounded once to fp32."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    n_pages, hkv = codes.shape[0], codes.shape[1]
+    assert scale.shape == (n_pages, hkv)
+    row = int(np.prod(codes.shape[2:])) if codes.ndim > 2 else 1
+    out = np.empty(codes.shape, np.float32)
+    rc = _load().oracle_dequant_e4m3(_ptr(codes), n_pages, hkv, row, _ptr(scale), _ptr(out))
+    if rc:
+        raise ValueError("oracle_dequant_e4m3: invalid arguments")
+    return out

@@ -46,13 +46,21 @@
 #define ORC_OK 0
 #define ORC_EINVAL -1
 
-/* bf16 -> fp32 is exact: the 16 bits are the top half of the fp32 pattern. */
-static double elem(const void *p, int dtype, int64_t i) {
-  if (dtype == 0) return (double)((const float *)p)[i];
-  uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
-  float f;
-  memcpy(&f, &u, sizeof f);
-  return (double)f;
+/* n consecutive elements starting at index i, upcast exactly to double
+ * (bf16 -> fp32 is exact: the 16 bits are the top half of the fp32 pattern). */
+static void elems(const void *p, int dtype, int64_t i, int32_t n, double *dst) {
+  if (dtype == 0) {
+    const float *f = (const float *)p + i;
+    for (int32_t c = 0; c < n; ++c) dst[c] = (double)f[c];
+  } else {
+    const uint16_t *h = (const uint16_t *)p + i;
+    for (int32_t c = 0; c < n; ++c) {
+      uint32_t u = (uint32_t)h[c] << 16;
+      float f;
+      memcpy(&f, &u, sizeof f);
+      dst[c] = (double)f;
+    }
+  }
 }
 
 /* Strict "a is larger than b" in the total order used for the max-pool:
@@ -169,28 +177,41 @@ int oracle_select_window(const float *idx_q, int64_t n_q, const int64_t *q_pos,
     if (q_pos[i] < 0 || q_pos[i] / block >= nb_avail) return ORC_EINVAL;
   const double u = ldexp(1.0, -24);
   const double gamma = d_idx * u / (1.0 - d_idx * u);
+  /* kmax transposed and upcast once, kt[c][b]: the scores below are then
+   * accumulated over c in ascending order for every block, exactly as the
+   * plain loop "for b: for c: s += q[c] * kmax[b][c]" would (the same
+   * products and the same order of sums), with the loop over blocks inside */
+  double *kt = (double *)malloc(sizeof(double) * (size_t)nb_avail * (size_t)d_idx);
+  if (!kt) return ORC_EINVAL;
+  for (int64_t b = 0; b < nb_avail; ++b)
+    for (int32_t cc = 0; cc < d_idx; ++cc)
+      kt[(int64_t)cc * nb_avail + b] = (double)kmax[b * d_idx + cc];
   int bad = 0;
 #pragma omp parallel
   {
     cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)(nb_avail + 1));
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(nb_avail + 1));
     int32_t *keep = (int32_t *)malloc(sizeof(int32_t) * (size_t)(topk + 1));
-    if (!c || !keep) {
+    if (!c || !sc || !keep) {
 #pragma omp atomic write
       bad = 1;
     }
 #pragma omp for schedule(dynamic, 64)
     for (int64_t i = 0; i < n_q; ++i) {
-      if (!c || !keep) continue;
+      if (!c || !sc || !keep) continue;
       const float *q = idx_q + i * d_idx;
       int64_t own = q_pos[i] / block;
       int64_t first = own - window + 1 > 0 ? own - window + 1 : 0;  /* forced: first..own */
       int64_t n_cand = first;                                        /* blocks below them */
       int64_t picks = topk - window;
+      for (int64_t b = 0; b < n_cand; ++b) sc[b] = 0.0;
+      for (int32_t cc = 0; cc < d_idx; ++cc) {
+        const double qc = (double)q[cc];
+        const double *kr = kt + (int64_t)cc * nb_avail;
+        for (int64_t b = 0; b < n_cand; ++b) sc[b] += qc * kr[b];
+      }
       for (int64_t b = 0; b < n_cand; ++b) {
-        double s = 0.0;
-        for (int32_t cc = 0; cc < d_idx; ++cc)
-          s += (double)q[cc] * (double)kmax[b * d_idx + cc];
-        c[b].s = s;
+        c[b].s = sc[b];
         c[b].b = (int32_t)b;
       }
       qsort(c, (size_t)n_cand, sizeof(cand_t), cand_cmp);
@@ -220,8 +241,10 @@ int oracle_select_window(const float *idx_q, int64_t n_q, const int64_t *q_pos,
       if (err_bnd) err_bnd[i] = eb;
     }
     free(c);
+    free(sc);
     free(keep);
   }
+  free(kt);
   return bad ? ORC_EINVAL : ORC_OK;
 }
 
@@ -312,20 +335,27 @@ int oracle_attend(const void *q, const void *k, const void *v, int32_t dtype,
     }
   }
   const int32_t grp = hq / hkv;
+  const int64_t cap = (int64_t)topk * block;   /* at most this many keys per query */
+  enum { TILE = 256 };
   int bad = 0;
 #pragma omp parallel
   {
     int32_t *blk = (int32_t *)malloc(sizeof(int32_t) * (size_t)topk);
-    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)topk * block);
-    double *s = (double *)malloc(sizeof(double) * (size_t)topk * block);
-    double *acc = (double *)malloc(sizeof(double) * (size_t)d);
-    if (!blk || !keys || !s || !acc) {
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+    double *s = (double *)malloc(sizeof(double) * (size_t)cap * grp);
+    double *kt = (double *)malloc(sizeof(double) * (size_t)TILE * d);
+    double *vrow = (double *)malloc(sizeof(double) * (size_t)d);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)d * grp);
+    double *mx = (double *)malloc(sizeof(double) * (size_t)grp);
+    double *z = (double *)malloc(sizeof(double) * (size_t)grp);
+    const int ok = blk && keys && s && kt && vrow && acc && mx && z;
+    if (!ok) {
 #pragma omp atomic write
       bad = 1;
     }
 #pragma omp for schedule(dynamic, 4)
     for (int64_t e = 0; e < n_eval; ++e) {
-      if (!blk || !keys || !s || !acc) continue;
+      if (!ok) continue;
       const int64_t pos = q_pos[e];
       /* the union of the selected blocks: sort, drop repeats and padding */
       int32_t nblk = 0;
@@ -340,37 +370,104 @@ int oracle_attend(const void *q, const void *k, const void *v, int32_t dtype,
         for (int64_t t = t0; t <= t1; ++t) keys[nk++] = t;
       }
       if (n_keys) n_keys[e] = nk;
-      for (int32_t h = 0; h < hq; ++h) {
-        const int64_t g = h / grp;
-        const int64_t qb = (q_row[e] * hq + h) * (int64_t)d;
-        double m = -INFINITY;
-        for (int64_t j = 0; j < nk; ++j) {
-          const int64_t kb = (g * kv_stride + keys[j]) * (int64_t)d;
-          double dot = 0.0;
-          for (int32_t c = 0; c < d; ++c)
-            dot += elem(q, dtype, qb + c) * elem(k, dtype, kb + c);
-          s[j] = scale * dot;
-          if (s[j] > m) m = s[j];
+      /* One KV head at a time, for the grp query heads that read it.  The
+       * loops are ordered so that the innermost runs over keys (or columns):
+       * every sum below still adds the same products in the same order as
+       * the plain per-head form -- s_t over c ascending, Z and o over keys
+       * ascending -- so the results are identical to it. */
+      for (int32_t g = 0; g < hkv; ++g) {
+        /* s[hl][j] = q[row][g*grp+hl] . k[g][keys[j]] */
+        for (int64_t j0 = 0; j0 < nk; j0 += TILE) {
+          const int64_t nt = nk - j0 < TILE ? nk - j0 : TILE;
+          for (int64_t jj = 0; jj < nt; ++jj) {
+            const int64_t kb = ((int64_t)g * kv_stride + keys[j0 + jj]) * (int64_t)d;
+            elems(k, dtype, kb, d, vrow);
+            for (int32_t c = 0; c < d; ++c) kt[(int64_t)c * TILE + jj] = vrow[c];
+          }
+          for (int32_t hl = 0; hl < grp; ++hl) {
+            const int64_t qb = (q_row[e] * hq + (int64_t)g * grp + hl) * (int64_t)d;
+            double *sr = s + (int64_t)hl * cap + j0;
+            for (int64_t jj = 0; jj < nt; ++jj) sr[jj] = 0.0;
+            elems(q, dtype, qb, d, vrow);
+            for (int32_t c = 0; c < d; ++c) {
+              const double qc = vrow[c];
+              const double *kr = kt + (int64_t)c * TILE;
+              for (int64_t jj = 0; jj < nt; ++jj) sr[jj] += qc * kr[jj];
+            }
+          }
         }
-        double z = 0.0;
-        for (int32_t c = 0; c < d; ++c) acc[c] = 0.0;
-        for (int64_t j = 0; j < nk; ++j) {
-          const double w = exp(s[j] - m);
-          const int64_t vb = (g * kv_stride + keys[j]) * (int64_t)d;
-          z += w;
-          for (int32_t c = 0; c < d; ++c) acc[c] += w * elem(v, dtype, vb + c);
+        /* scale, row max, then the softmax-weighted sum of the values */
+        for (int32_t hl = 0; hl < grp; ++hl) {
+          double *sr = s + (int64_t)hl * cap;
+          double m = -INFINITY;
+          for (int64_t j = 0; j < nk; ++j) {
+            sr[j] = scale * sr[j];
+            if (sr[j] > m) m = sr[j];
+          }
+          mx[hl] = m;
+          z[hl] = 0.0;
+          for (int32_t c = 0; c < d; ++c) acc[(int64_t)hl * d + c] = 0.0;
         }
-        float *out = o + (e * hq + h) * (int64_t)d;
-        for (int32_t c = 0; c < d; ++c) out[c] = (float)(acc[c] / z);
-        if (lse) lse[e * hq + h] = (float)(m + log(z));
+        for (int64_t j = 0; j < nk; ++j) {
+          const int64_t vb = ((int64_t)g * kv_stride + keys[j]) * (int64_t)d;
+          elems(v, dtype, vb, d, vrow);
+          for (int32_t hl = 0; hl < grp; ++hl) {
+            const double w = exp(s[(int64_t)hl * cap + j] - mx[hl]);
+            double *ar = acc + (int64_t)hl * d;
+            z[hl] += w;
+            for (int32_t c = 0; c < d; ++c) ar[c] += w * vrow[c];
+          }
+        }
+        for (int32_t hl = 0; hl < grp; ++hl) {
+          const int64_t h = (int64_t)g * grp + hl;
+          float *out = o + (e * hq + h) * (int64_t)d;
+          for (int32_t c = 0; c < d; ++c) out[c] = (float)(acc[(int64_t)hl * d + c] / z[hl]);
+          if (lse) lse[e * hq + h] = (float)(mx[hl] + log(z[hl]));
+        }
       }
     }
     free(blk);
     free(keys);
     free(s);
+    free(kt);
+    free(vrow);
     free(acc);
+    free(mx);
+    free(z);
   }
   return bad ? ORC_EINVAL : ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * FP8 KV pages, dequantised.  [CXT §3.3 "Prefilling 与 Decoding 的差异化优化"]
+ * keeps the KV cache in blocks and in reduced precision; the reading taken
+ * here is OCP FP8 E4M3 (the variant without infinities) with one fp32 scale
+ * per (page, KV head) for K and one for V.
+ *
+ * A code is 1 sign bit s, 4 exponent bits e (bias 7) and 3 mantissa bits m:
+ *   e >= 1:             (-1)^s * 2^(e-7) * (1 + m/8)      (e = 15, m = 7: NaN)
+ *   e == 0:             (-1)^s * 2^-6 * (m/8)             (subnormals, signed 0)
+ * out[p][g][i] = scale[p][g] * value(x[p][g][i]), the product rounded once to
+ * fp32 (it is exact in double: 24 + 4 significant bits).
+ * x: [n_pages][hkv][row_len] codes; scale: [n_pages][hkv]; out likewise fp32.
+ * ---------------------------------------------------------------------- */
+static double e4m3_value(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+int oracle_dequant_e4m3(const uint8_t *x, int64_t n_pages, int32_t hkv, int64_t row_len,
+                        const float *scale, float *out) {
+  if (!x || !scale || !out || n_pages < 0 || hkv < 1 || row_len < 0) return ORC_EINVAL;
+  for (int64_t p = 0; p < n_pages; ++p)
+    for (int32_t g = 0; g < hkv; ++g) {
+      const double sc = (double)scale[p * hkv + g];
+      const int64_t base = (p * hkv + g) * row_len;
+      for (int64_t i = 0; i < row_len; ++i) out[base + i] = (float)(sc * e4m3_value(x[base + i]));
+    }
+  return ORC_OK;
 }
 
 /* ------------------------------------------------------------------------

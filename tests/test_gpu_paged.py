@@ -6,8 +6,10 @@ KV).
 The oracle attends over the contiguous cache the pages stand for: for bf16
 pages the cache itself (and the paged result must equal the contiguous
 kernel's bit for bit: same units, same arithmetic); for FP8 pages the
-dequantised values scale * e4m3 in fp32, against which the tolerance is the
-bf16 one (e4m3 values are exact in bf16; only the scaled products round).
+oracle's dequantised values (scale * e4m3 value in fp32), against which the
+tolerance is the bf16 one (e4m3 values are exact in bf16; only the scaled
+products round).  The FP8 codes and scales are inputs: they are made here by
+torch's fp32 -> e4m3 cast of amax-scaled pages.
 """
 import numpy as np
 import pytest
@@ -56,9 +58,10 @@ def _paged_case(orc, hq, hkv, B, K, lens, fp8, seed):
         ks, vs = amax_k / 448.0, amax_v / 448.0
         kp8 = (kp.float() / ks[:, :, None, None]).to(torch.float8_e4m3fn)
         vp8 = (vp.float() / vs[:, :, None, None]).to(torch.float8_e4m3fn)
-        # the cache the pages stand for: dequantised, contiguous
-        kd = (kp8.float() * ks[:, :, None, None])
-        vd = (vp8.float() * vs[:, :, None, None])
+        # the cache the pages stand for: the oracle's dequantisation of the
+        # codes (scale * e4m3 value, rounded once), laid out contiguously
+        kd = torch.from_numpy(orc.dequant_e4m3(kp8.view(torch.uint8).numpy(), ks.numpy()))
+        vd = torch.from_numpy(orc.dequant_e4m3(vp8.view(torch.uint8).numpy(), vs.numpy()))
         kc = torch.zeros(n, hkv, L, d)
         vc = torch.zeros(n, hkv, L, d)
         for s, Ls in enumerate(lens):

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from block_sparse_attention_index_amd import ops, pipeline, synth
-from helpers import TOL_BF16, TOL_F32, check_selection, max_abs
+from helpers import TOL_BF16, TOL_F32, check_selection, max_abs, selection_report
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -337,13 +337,16 @@ def test_pipeline_end_to_end_tiny(orc):
     pos = np.arange(cfg.T, dtype=np.int64)
     so, gr, ga, eb = orc.select(x["idx_q"].numpy(), pos, kmax, cfg.block, cfg.topk)
     sel = _np(sel)
-    nf, nm = check_selection(sel, so, gr, ga, eb, x["idx_q"].numpy(), kmax, pos, cfg.block)
-    same = np.all(sel == so, axis=1)
+    rep = selection_report(sel, so, gr, ga, eb, x["idx_q"].numpy(), kmax, pos, cfg.block)
+    # every row's output against the oracle evaluated on the device's own
+    # selection (a valid top-K wherever it differs from the oracle's)
     oo, lo, _ = orc.attend(synth.host(x["q"]), synth.host(x["k"]), synth.host(x["v"]),
-                           pos, pos, so, cfg.block, cfg.scale, 0)
-    eo = max_abs(_np(o)[same], oo[same])
-    el = max_abs(_np(lse)[same], lo[same])
-    _say(f"  flagged {nf}, differing {nm}; max|do| {eo:.3g} max|dlse| {el:.3g}")
+                           pos, pos, sel, cfg.block, cfg.scale, 0)
+    eo = max_abs(_np(o), oo)
+    el = max_abs(_np(lse), lo)
+    _say(f"  near-ties flagged {rep['flag_rel']} (relative) + {rep['flag_bound_only']} "
+         f"(error bound only), differing {rep['differing']}; max|do| {eo:.3g} "
+         f"max|dlse| {el:.3g}")
     assert eo <= TOL_F32 and el <= TOL_F32
 
 
@@ -462,6 +465,9 @@ def test_fused_steps_in_a_captured_graph():
     (64, 8, 64, 6, [0, 63, 64, 200, 1000]),      # empty cache, block-opening tokens
     (16, 1, 128, 4, [1, 127, 300]),              # G = 16
     (8, 8, 512, 8, [511, 512, 3000]),            # G = 1, the 1M-token block size
+    # the 1M-token decode shape (Hq 64 / Hkv 8, B 512, K 8): caches of 4..9
+    # blocks, one sequence opening a block, one just short of full rows
+    (64, 8, 512, 8, [4096, 4607, 3583, 1535]),
     # 128 sequences with full rows (own block >= K - 1): the workgroups whose
     # range starts on an own-block unit fetch its first chunk before the
     # selection merge (own blocks from 7 to 512 keys)
