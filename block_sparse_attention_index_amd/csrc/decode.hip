@@ -12,6 +12,7 @@
 // arriving by LDS DMA while the previous chunk computes); other shapes use a
 // VALU kernel with one work item per (sequence, KV head, selected block,
 // 128-key chunk).  HBM-bound: K and V are read once.
+#include <mutex>
 #include <type_traits>
 
 #include "msa_internal.h"
@@ -1744,4 +1745,39 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of msa_decode_step_noalloc: a file-scope device array (each device
+// the library runs on holds its own copy until the process ends).  Its device
+// address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and kept; kernels get that address, never the array's name
+// (which in host code is only a stand-in).  The decode step writes every
+// scratch word it reads before reading it, so nothing needs clearing; calls
+// that overlap on one device share the array and race.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {nullptr};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace msa
+

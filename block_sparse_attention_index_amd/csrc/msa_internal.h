@@ -84,6 +84,11 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
                               int32_t *sel, float *o, float *lse, void *ws,
                               hipStream_t st);
 
+// The static scratch of msa_decode_step_noalloc: its size, and its device
+// address on the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void **ptr);
+
 // Round a byte count up to the 256-byte alignment used for workspace
 // sub-buffers.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -32,7 +32,7 @@ ENTRY_POINTS = (
     "msa_decode_step_workspace_bytes", "msa_decode_step",
     "msa_index_pool_mean", "msa_index_topk_window", "msa_index_topk_decode_window",
     "msa_sparse_gqa_decode_paged", "msa_prefill_varlen_workspace_bytes",
-    "msa_prefill_varlen",
+    "msa_prefill_varlen", "msa_decode_step_noalloc_max_bytes", "msa_decode_step_noalloc",
 )
 
 
@@ -86,6 +86,9 @@ def load():
         "msa_decode_step_workspace_bytes": ([i32, i64, i32, i32, i32, i32], sz),
         "msa_decode_step": ([P, P, P, P, P, P, P, P, P, i32, i32, i64, i64, P, i32, i32,
                              i32, i32, i32, i32, f32, P, P, P, P, sz, P], ctypes.c_int),
+        "msa_decode_step_noalloc_max_bytes": ([], sz),
+        "msa_decode_step_noalloc": ([P, P, P, P, P, P, P, P, P, i32, i32, i64, i64, P, i32,
+                                     i32, i32, i32, i32, i32, f32, P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -491,3 +494,40 @@ def msa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         _ptr(ws), ws.numel(), _stream(q))
     _check("msa_decode_step", st)
     return o, lse, sel
+
+
+def msa_decode_step_noalloc(q, k_new, v_new, idx_q, idx_k_new, k_cache, v_cache, kmax,
+                            seq_len, block: int, topk: int, scale: float | None = None,
+                            idx_k_cache=None, sel=None, o=None, lse=None,
+                            want_lse: bool = True):
+    """:func:`msa_decode_step` on the library's static scratch (no workspace
+    argument; the C call allocates nothing).  Outputs not passed in are
+    allocated here by torch; pass them to keep the whole call allocation-free."""
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache")):
+        _dev(t, nm)
+    if not (q.dtype == k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, the new rows and the caches must share a dtype")
+    for t, nm in ((idx_q, "idx_q"), (idx_k_new, "idx_k_new"), (kmax, "kmax")):
+        _dev(t, nm, torch.float32)
+    if idx_k_cache is not None:
+        _dev(idx_k_cache, "idx_k_cache", torch.float32)
+    _dev(seq_len, "seq_len", torch.int64)
+    n_seq, hq, d = q.shape
+    _, hkv, len_max, _ = k_cache.shape
+    nb_max, d_idx = kmax.shape[1], kmax.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if sel is None:
+        sel = torch.empty((n_seq, topk), dtype=torch.int32, device=q.device)
+    if o is None:
+        o = torch.empty((n_seq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((n_seq, hq), dtype=torch.float32, device=q.device)
+    st = load().msa_decode_step_noalloc(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(idx_q), _ptr(idx_k_new), _ptr(k_cache),
+        _ptr(v_cache), _ptr(idx_k_cache), _ptr(kmax), _dtype_code(q), n_seq, len_max, nb_max,
+        _ptr(seq_len), hq, hkv, d, d_idx, block, topk, scale, _ptr(sel), _ptr(o), _ptr(lse),
+        _stream(q))
+    _check("msa_decode_step_noalloc", st)
+    return o, lse, sel
+

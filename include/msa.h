@@ -359,6 +359,31 @@ int msa_decode_step(const void *q, const void *k_new, const void *v_new,
                     int32_t *sel, float *o, float *lse, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* ------------------------------------------------------------------------
+ * msa_decode_step_noalloc -- msa_decode_step for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Arguments and
+ * results are those of msa_decode_step without ws / ws_bytes; the scratch it
+ * needs (msa_decode_step_workspace_bytes() of the same shape) comes from a
+ * static device array of msa_decode_step_noalloc_max_bytes() bytes (32 MiB)
+ * that the library holds on each device it runs on until the process ends.
+ * Nothing is allocated.  A shape whose scratch exceeds the maximum returns
+ * MSA_ERR_WORKSPACE (for example dec16's 16 sequences x 8 KV heads need
+ * about 17 MiB; about 500 such sequences at block 512, top-K 8 would not
+ * fit).  Every call on one device shares that device's array: calls that
+ * overlap on one device (different streams, different host threads without
+ * ordering) race and give undefined results; calls ordered on one stream are
+ * safe.  The first call on a device looks up the array's address (once).
+ * ------------------------------------------------------------------------ */
+size_t msa_decode_step_noalloc_max_bytes(void);
+int msa_decode_step_noalloc(const void *q, const void *k_new, const void *v_new,
+                            const float *idx_q, const float *idx_k_new, void *k_cache,
+                            void *v_cache, float *idx_k_cache, float *kmax, int32_t dtype,
+                            int32_t n_seq, int64_t len_max, int64_t nb_max,
+                            const int64_t *seq_len, int32_t hq, int32_t hkv, int32_t d,
+                            int32_t d_idx, int32_t block, int32_t topk, float scale,
+                            int32_t *sel, float *o, float *lse, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
