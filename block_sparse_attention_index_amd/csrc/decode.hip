@@ -278,6 +278,99 @@ struct DecUnit {
 // `sel`.  Otherwise the query sits at seq_len[s] - 1 and `sel` is read.
 constexpr int kStepSeqs = 8;
 
+// Device-coherent accesses to the decode partial records of the fused step.
+// A record is written with vector buffer stores carrying the SC1 cache-policy
+// bit (device scope: written through to the point where every XCD's L2 sees
+// it) and read back by another workgroup, on any XCD, with SC1 buffer loads,
+// which do not hit a stale L2 line.  Ordering: the writer waits for its
+// stores to complete before its workgroup's arrival is counted; the reader
+// loads only after the count says every writer has arrived.  No L2
+// write-back or invalidate is needed (both cost far more per workgroup).
+constexpr int kSc1 = 16;   // cache-policy operand: SC1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+typedef unsigned u32v4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      u32v4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)},
+      r, off, 0, kSc1);
+}
+__device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ float4 load4_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32v4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
+  return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                     __uint_as_float(x.w));
+}
+__device__ __forceinline__ float load_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSc1));
+}
+
+// Workgroup of the static unit partition (u_q units each, one more for the
+// first u_r) that holds unit u.
+__device__ __forceinline__ uint32_t unit_wg(uint32_t u, uint32_t u_q, uint32_t u_r) {
+  const uint32_t split = u_r * (u_q + 1);   // units of the longer ranges
+  return u < split ? u / (u_q + 1) : u_r + (u - split) / u_q;
+}
+
+// Combine of run sg's partials inside the streaming kernel, by the last
+// workgroup to finish its part of the run: the workgroups b0..b1 whose unit
+// ranges meet the run each left one normalised partial and base-2
+// log-sum-exp (device-coherent records), in the slot of their first unit in
+// the run.  Thread t owns
+// four consecutive columns of one query head; the partials' loads go out in
+// batches of kBatch so their round trips overlap.
+template <int G>
+__device__ __forceinline__ void combine_run(uint32_t sg, uint32_t ups_g, uint32_t u_q,
+                                            uint32_t u_r, int hq, int hkv,
+                                            const float *__restrict__ part_o,
+                                            const float *__restrict__ part_lse,
+                                            float *__restrict__ o, float *__restrict__ lse) {
+  constexpr int D = 128;
+  constexpr int kBatch = 16;
+  const uint32_t u0 = sg * ups_g, u1 = u0 + ups_g - 1;
+  const uint32_t b0 = unit_wg(u0, u_q, u_r), b1 = unit_wg(u1, u_q, u_r);
+  const int s = (int)(sg / (uint32_t)hkv), g = (int)(sg - (uint32_t)s * (uint32_t)hkv);
+  for (int x = threadIdx.x; x < G * D / 4; x += 256) {
+    const int hd = x / (D / 4), c4 = (x % (D / 4)) * 4;
+    float m = -3.0e38f, z = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (uint32_t bx0 = b0; bx0 <= b1; bx0 += kBatch) {
+      float li[kBatch];
+      float4 oi[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const uint32_t bx = bx0 + k;
+        li[k] = -INFINITY;
+        oi[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (bx <= b1) {
+          const uint32_t ub = bx * u_q + (bx < u_r ? bx : u_r);
+          const size_t sl = ub > u0 ? ub : u0;
+          li[k] = load_sc1(record_rsrc(part_lse + sl * G, G * 4), hd * 4);
+          oi[k] = load4_sc1(record_rsrc(part_o + sl * G * D, G * D * 4), (hd * D + c4) * 4);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float mn = fmaxf(m, li[k]);
+        const float sc = fast_exp2(m - mn), w = fast_exp2(li[k] - mn);
+        z = fmaf(z, sc, w);
+        acc.x = fmaf(acc.x, sc, w * oi[k].x);
+        acc.y = fmaf(acc.y, sc, w * oi[k].y);
+        acc.z = fmaf(acc.z, sc, w * oi[k].z);
+        acc.w = fmaf(acc.w, sc, w * oi[k].w);
+        m = mn;
+      }
+    }
+    const int64_t hh = (int64_t)s * hq + (int64_t)g * G + hd;
+    *reinterpret_cast<float4 *>(&o[hh * D + c4]) =
+        make_float4(acc.x / z, acc.y / z, acc.z / z, acc.w / z);
+    if (lse && c4 == 0) lse[hh] = (m + __log2f(z)) * kLn2;
+  }
+}
+
 template <int G, bool FUSED>
 __global__ __launch_bounds__(256) void decode_stream(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
@@ -286,7 +379,8 @@ __global__ __launch_bounds__(256) void decode_stream(
     int32_t *__restrict__ sel, int topk, int nseg, int seg_len,
     uint32_t u_q, uint32_t u_r, float scale_log2, float *__restrict__ part_o,
     float *__restrict__ part_lse, const float *__restrict__ cand_s,
-    const int *__restrict__ cand_b, int n_chunks, int64_t nb_max) {
+    const int *__restrict__ cand_b, int n_chunks, int64_t nb_max,
+    int *__restrict__ run_cnt, float *__restrict__ o, float *__restrict__ lse) {
   constexpr int D = 128;
   constexpr int QE = G * D < 512 ? 512 : G * D;   // staged query elements
   __shared__ StreamBuf sb0;
@@ -359,10 +453,39 @@ __global__ __launch_bounds__(256) void decode_stream(
     const uint32_t u0 = sg * ups_g;
     return u0 > u_begin ? u0 : u_begin;
   };
+  // FUSED: the run's workgroups meet here once each has stored its partial
+  // (device-coherent stores, completed by each wave before the barrier); the
+  // last to arrive combines them into o and lse (the counters were zeroed by
+  // the scan kernel).
+  __shared__ int last_arrival;
+  auto arrive = [&](uint32_t sg) __attribute__((always_inline)) {
+    if constexpr (FUSED) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t n_wg = unit_wg(sg * ups_g + ups_g - 1, u_q, u_r) -
+                              unit_wg(sg * ups_g, u_q, u_r) + 1;
+        const int before = __hip_atomic_fetch_add(&run_cnt[sg], 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        last_arrival = before == (int)n_wg - 1;
+      }
+      __syncthreads();
+      if (last_arrival) combine_run<G>(sg, ups_g, u_q, u_r, hq, hkv, part_o, part_lse, o, lse);
+    }
+  };
   auto put_neutral = [&](uint32_t sg) __attribute__((always_inline)) {
     const size_t sl = run_slot(sg);
-    for (int x = tid; x < G * D; x += 256) part_o[sl * G * D + x] = 0.f;
-    if (tid < G) part_lse[sl * G + tid] = -INFINITY;
+    if constexpr (FUSED) {
+      const __amdgpu_buffer_rsrc_t ro = record_rsrc(part_o + sl * G * D, G * D * 4);
+      const __amdgpu_buffer_rsrc_t rl = record_rsrc(part_lse + sl * G, G * 4);
+      for (int x4 = tid; x4 < G * D / 4; x4 += 256)
+        store_sc1(ro, x4 * 16, make_float4(0.f, 0.f, 0.f, 0.f));
+      if (tid < G) store_sc1(rl, tid * 4, -INFINITY);
+    } else {
+      for (int x = tid; x < G * D; x += 256) part_o[sl * G * D + x] = 0.f;
+      if (tid < G) part_lse[sl * G + tid] = -INFINITY;
+    }
+    arrive(sg);
   };
   uint32_t sg_next = u_begin / ups_g;   // runs before this one are written
   auto dma_kv = [&](StreamBuf &buf, const DecUnit &d, int64_t row0, int nrows)
@@ -581,22 +704,49 @@ __global__ __launch_bounds__(256) void decode_stream(
         }
       }
       __syncthreads();
-      for (int x = tid; x < G * D; x += 256) {
-        const int hd = x / D, c = x % D;
-        float mx = -INFINITY;
+      const size_t sl = run_slot(sg_cur);
+      if constexpr (FUSED) {
+        // four consecutive columns per thread, stored device-coherent
+        const __amdgpu_buffer_rsrc_t ro = record_rsrc(part_o + sl * G * D, G * D * 4);
+        const __amdgpu_buffer_rsrc_t rl = record_rsrc(part_lse + sl * G, G * 4);
+        for (int x4 = tid; x4 < G * D / 4; x4 += 256) {
+          const int hd = x4 / (D / 4), c4 = (x4 % (D / 4)) * 4;
+          float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mm[w * G + hd]);
-        float z = 0.f, ov = 0.f;
+          for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mm[w * G + hd]);
+          float z = 0.f;
+          float ov[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float sc = fast_exp2(mm[w * G + hd] - mx);   // 0 for a wave without keys
-          z = fmaf(sc, ml[w * G + hd], z);
-          ov = fmaf(sc, mo[(w * G + hd) * D + c], ov);
+          for (int w = 0; w < 4; ++w) {
+            const float sc = fast_exp2(mm[w * G + hd] - mx);   // 0 for a wave without keys
+            z = fmaf(sc, ml[w * G + hd], z);
+            const float4 m4 = *reinterpret_cast<const float4 *>(&mo[(w * G + hd) * D + c4]);
+            ov[0] = fmaf(sc, m4.x, ov[0]);
+            ov[1] = fmaf(sc, m4.y, ov[1]);
+            ov[2] = fmaf(sc, m4.z, ov[2]);
+            ov[3] = fmaf(sc, m4.w, ov[3]);
+          }
+          store_sc1(ro, (hd * D + c4) * 4, make_float4(ov[0] / z, ov[1] / z, ov[2] / z, ov[3] / z));
+          if (c4 == 0) store_sc1(rl, hd * 4, mx + __log2f(z));
         }
-        const size_t sl = run_slot(sg_cur);
-        part_o[(sl * G + hd) * D + c] = ov / z;
-        if (c == 0) part_lse[sl * G + hd] = mx + __log2f(z);
+      } else {
+        for (int x = tid; x < G * D; x += 256) {
+          const int hd = x / D, c = x % D;
+          float mx = -INFINITY;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mm[w * G + hd]);
+          float z = 0.f, ov = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float sc = fast_exp2(mm[w * G + hd] - mx);   // 0 for a wave without keys
+            z = fmaf(sc, ml[w * G + hd], z);
+            ov = fmaf(sc, mo[(w * G + hd) * D + c], ov);
+          }
+          part_o[(sl * G + hd) * D + c] = ov / z;
+          if (c == 0) part_lse[sl * G + hd] = mx + __log2f(z);
+        }
       }
+      arrive(sg_cur);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1413,12 +1563,14 @@ __global__ __launch_bounds__(256) void dstep_scan(
     float *__restrict__ kmax, const float *__restrict__ idx_q,
     const int64_t *__restrict__ seq_len, int64_t len_max, int64_t nb_max,
     int hkv, int d, int d_idx, int B, int topk, float *__restrict__ cand_s,
-    int *__restrict__ cand_b, int n_chunks) {
+    int *__restrict__ cand_b, int n_chunks, int *__restrict__ run_cnt) {
   const int s = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
   const int64_t L = seq_len[s];
   const bool room = L >= 0 && L < len_max && L / B < nb_max;   // else: nothing is written
   const int64_t own = room ? L / B : nb_max - 1;
   if (ch == n_chunks) {
+    // the attention kernel's arrival counters of this sequence start at zero
+    for (int g = tid; g < hkv; g += 256) run_cnt[(int64_t)s * hkv + g] = 0;
     if (!room) return;
     // 16-byte pieces of the K and V rows (d * sizeof(T) is a multiple of 16)
     constexpr int kV = 16 / (int)sizeof(T);
@@ -1503,7 +1655,7 @@ hipError_t launch_dec(const T *q, const T *kc, const T *vc, int32_t n_seq,
     hipLaunchKernelGGL((decode_stream<G, false>), dim3(pl.grid), dim3(256), 0, st, q, kc, vc,
                        len_max, seq_len, hq, hkv, B, const_cast<int32_t *>(sel), topk, pl.nseg,
                        pl.seg_len, pl.u_q, pl.u_r, scale * kLog2e, part_o, part_lse, nullptr,
-                       nullptr, 0, (int64_t)0);
+                       nullptr, 0, (int64_t)0, nullptr, nullptr, nullptr);
     hipLaunchKernelGGL((decode_merge_runs<D>), dim3(hq, n_seq), dim3(D), 0, st, G, hkv,
                        (uint32_t)(topk * pl.nseg), pl.u_q, pl.u_r, part_o, part_lse, o, lse);
     return hipGetLastError();
@@ -1679,14 +1831,18 @@ hipError_t launch_decode_paged(const void *q, const void *k_pages, const void *v
 
 // ---------------------------------------------------------------------------
 // Fused decode step (append, running block max, index scan, top-K, sparse
-// GQA, merge) for bf16 with d = 128.
-// Layout: [candidate scores][candidate ids][partial o][partial lse].
+// GQA, merge) for bf16 with d = 128: two kernels, the scan (with the append)
+// and the streaming attention, whose last workgroup per run merges it.
+// Layout: [candidate scores][candidate ids][arrival counters][partial o]
+// [partial lse].
 // ---------------------------------------------------------------------------
 size_t decode_step_ws_bytes(int32_t n_seq, int64_t nb_max, int32_t hq, int32_t d,
                             int32_t block, int32_t topk) {
   const int64_t n_chunks = (nb_max + kDecChunk - 1) / kDecChunk;
   const size_t nc = (size_t)n_seq * n_chunks * (topk > 1 ? topk - 1 : 1);
-  return align256(nc * 4) + align256(nc * 4) + decode_ws_bytes(n_seq, hq, d, block, topk);
+  // + one arrival counter per (sequence, KV head); Hq bounds Hkv
+  return align256(nc * 4) + align256(nc * 4) + align256((size_t)n_seq * hq * 4) +
+         decode_ws_bytes(n_seq, hq, d, block, topk);
 }
 
 bool decode_step_supported(int32_t dtype, int32_t d, int32_t group) {
@@ -1710,6 +1866,8 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
   w += align256(nc * 4);
   int *cand_b = reinterpret_cast<int *>(w);
   w += align256(nc * 4);
+  int *run_cnt = reinterpret_cast<int *>(w);
+  w += align256((size_t)n_seq * hq * 4);
   const int64_t np_max = dec_partials(n_seq, hq, block, topk);
   float *part_o = reinterpret_cast<float *>(w);
   w += align256((size_t)np_max * d * 4);
@@ -1721,14 +1879,14 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
   hipLaunchKernelGGL((dstep_scan<uint16_t>), dim3(n_chunks + 1, n_seq), dim3(256), 0, st,
                      static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
                      idx_k_new, kc, vc, idx_k_cache, kmax, idx_q, seq_len, len_max, nb_max,
-                     hkv, d, d_idx, block, topk, cand_s, cand_b, n_chunks);
+                     hkv, d, d_idx, block, topk, cand_s, cand_b, n_chunks, run_cnt);
   const StreamPlan pl = stream_plan(n_seq, hkv, block, topk);
 #define MSA_STEP_CASE(GG)                                                               \
   case GG:                                                                              \
     hipLaunchKernelGGL((decode_stream<GG, true>), dim3(pl.grid), dim3(256), 0, st, qq, kc, \
                        vc, len_max, seq_len, hq, hkv, block, sel, topk, pl.nseg,         \
                        pl.seg_len, pl.u_q, pl.u_r, scale * kLog2e, part_o, part_lse, cand_s, \
-                       cand_b, n_chunks, nb_max);                                        \
+                       cand_b, n_chunks, nb_max, run_cnt, o, lse);                       \
     break;
   switch (G) {
     MSA_STEP_CASE(1)
@@ -1740,8 +1898,6 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
       return hipErrorInvalidValue;
   }
 #undef MSA_STEP_CASE
-  hipLaunchKernelGGL((decode_merge_runs<128>), dim3(hq, n_seq), dim3(128), 0, st, G, hkv,
-                     (uint32_t)(topk * pl.nseg), pl.u_q, pl.u_r, part_o, part_lse, o, lse);
   return hipGetLastError();
 }
 
