@@ -15,7 +15,10 @@ step (4*d*Hq FLOP per attended (query, key) pair, prefill and decode);
 steps run as one captured HIP graph, replayed each step); ``roofline`` is
 for the sparse-GQA prefill (its two kernels per call, timed with HIP events on
 the launch stream) against the dense bf16 MFMA peak; ``cpu_baseline`` times
-the CPU oracle on a bounded sample of the same workload.
+the CPU oracle on the same step (index branch and decode steps in full, the
+prefill attention on a stratified sample extrapolated by attended pairs);
+``selection_vs_oracle`` counts the near-ties and differing rows of the
+device's selection of all queries against the oracle's.
 """
 from __future__ import annotations
 
@@ -212,7 +215,7 @@ def dec16_cpu_baseline(x, cfg):
         dt += time.perf_counter() - t0
         del k_h, v_h
     return {"value": round(dt * 1e6, 1), "unit": "us/step", "cores": oracle.threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"the whole step, all {cfg.n_seq} sequences (pool of each "
                       f"sequence's {L} index keys, selection, attention), {dt:.2f} s"}
 
@@ -352,43 +355,94 @@ def measure_next(dev, seed: int) -> dict:
     return out
 
 
-def cpu_baseline(x, cfg, budget_s: float = 15.0):
-    """Time the CPU oracle on a bounded sample of the same workload: the
-    index branch and attention for a random sample of prefill queries."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or 'unknown'."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, cfg, dev_sel, n_dec: int, attn_budget_s: float = 10.0):
+    """The CPU oracle (fp64, every host core) on the same 1M-token step as the
+    GPU: the index branch in full (pool of all index keys, selection of every
+    query), the prefill attention on a stratified sample of queries (blocks 0
+    and 1 and the last block in full, plus random queries, about
+    `attn_budget_s` of work) extrapolated to all queries by attended pairs,
+    and every decode step in full (each: re-pool of the newest token's block,
+    selection and attention for its query).  The device's selection is also
+    compared with the oracle's here: near-ties flagged per rule, and rows
+    where the two differ."""
     import oracle
     oracle.build(force=False)
     T, B, K = cfg.T, cfg.block, cfg.topk
+    L_all = x["idx_k"].shape[0]
+    idx_k = x["idx_k"].cpu().numpy()
+    idx_q = x["idx_q"].cpu().numpy()
+    k_h, v_h = synth.host(x["k"]), synth.host(x["v"])
+    # index branch, whole
+    t0 = time.perf_counter()
+    kmax = oracle.pool(idx_k[:T], B)
+    t_pool = time.perf_counter() - t0
+    pos = np.arange(T, dtype=np.int64)
+    t0 = time.perf_counter()
+    so, gr, ga, eb = oracle.select(idx_q[:T], pos, kmax, B, K)
+    t_sel = time.perf_counter() - t0
+    rel = np.nan_to_num(gr, nan=np.inf) < 1e-3
+    bnd = np.nan_to_num(ga, nan=np.inf) <= np.nan_to_num(eb, nan=0.0)
+    diff = np.any(np.asarray(dev_sel) != so, axis=1)
+    ties = {"rows": T, "flag_rel": int(rel.sum()), "flag_bound_only": int((bnd & ~rel).sum()),
+            "differing": int(diff.sum()), "differing_unflagged": int((diff & ~(rel | bnd)).sum())}
+    # prefill attention on a stratified sample, extrapolated by attended pairs
     rng = np.random.default_rng(0)
-    idx_k = x["idx_k"][:T].cpu().numpy()
-    kmax = oracle.pool(idx_k, B)
-    k_h = synth.host(x["k"])
-    v_h = synth.host(x["v"])
-    # calibrate on a few queries, then size the sample to the budget
-    n_cal = 8 * max(1, oracle.threads())
-    rows = np.sort(rng.choice(T, size=n_cal, replace=False))
-    t0 = time.perf_counter()
-    _run_oracle_rows(oracle, x, cfg, kmax, k_h, v_h, rows)
-    dt = time.perf_counter() - t0
-    n = int(min(T, max(n_cal, n_cal * budget_s / max(dt, 1e-3))))
-    rows = np.sort(rng.choice(T, size=n, replace=False))
-    t0 = time.perf_counter()
-    _run_oracle_rows(oracle, x, cfg, kmax, k_h, v_h, rows)
-    dt = time.perf_counter() - t0
-    flops = 4.0 * cfg.d * cfg.Hq * sum(attended_pairs(int(p), 1, B, K) for p in rows)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"{n} random prefill queries of the {T}-token sequence "
-                      f"(select + attend, fp64), {dt:.1f} s; pool of all {T} "
-                      f"index keys not included"}
+    fixed = np.unique(np.concatenate([np.arange(min(T, 2 * B)), np.arange(max(0, T - B), T)]))
 
+    def attend(rows):
+        t1 = time.perf_counter()
+        q_h = synth.host(x["q"][torch.from_numpy(rows).to(x["q"].device)])
+        _, _, nk = oracle.attend(q_h, k_h, v_h, np.arange(len(rows)), rows, so[rows], B,
+                                 cfg.scale, oracle.BF16)
+        return time.perf_counter() - t1, int(nk.sum())
 
-def _run_oracle_rows(oracle, x, cfg, kmax, k_h, v_h, rows):
-    pos = rows.astype(np.int64)
-    idx_q = x["idx_q"][torch.from_numpy(rows)].cpu().numpy()
-    sel, *_ = oracle.select(idx_q, pos, kmax, cfg.block, cfg.topk)
-    q_h = synth.host(x["q"][torch.from_numpy(rows)])
-    oracle.attend(q_h, k_h, v_h, np.arange(len(rows)), pos, sel, cfg.block,
-                  cfg.scale, oracle.BF16)
+    t_fix, keys_fix = attend(fixed)
+    per_key = t_fix / max(1, keys_fix)
+    mean_keys = attended_pairs(0, T, B, K) / T
+    n_rand = int(max(64, min(T, attn_budget_s / max(per_key * mean_keys, 1e-9))))
+    rand = np.sort(rng.choice(np.setdiff1d(np.arange(T), fixed), size=n_rand, replace=False))
+    t_rand, keys_rand = attend(rand)
+    t_attn = (t_fix + t_rand) / (keys_fix + keys_rand) * attended_pairs(0, T, B, K)
+    # every decode step
+    t0 = time.perf_counter()
+    km = np.concatenate([kmax, np.zeros((1, cfg.d_idx), np.float32)]) if n_dec else kmax
+    for s in range(n_dec):
+        L = T + s + 1
+        own = (L - 1) // B
+        km[own:own + 1] = oracle.pool(idx_k[own * B:L], B)
+        p = np.array([L - 1], np.int64)
+        sel1, *_ = oracle.select(idx_q[L - 1:L], p, km[:own + 1], B, K)
+        oracle.attend(synth.host(x["q"][L - 1:L]), k_h, v_h, np.array([0]), p, sel1, B,
+                      cfg.scale, oracle.BF16)
+    t_dec = time.perf_counter() - t0
+    assert L_all >= T + n_dec
+    step_s = t_pool + t_sel + t_attn + t_dec
+    flops = 4.0 * cfg.d * cfg.Hq * (attended_pairs(0, T, B, K) +
+                                    sum(attended_pairs(T + s, 1, B, K) for s in range(n_dec)))
+    n_att = len(fixed) + n_rand
+    return {"value": flops / step_s / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": (f"index branch in full (pool {t_pool:.2f} s, selection of all {T} "
+                       f"queries {t_sel:.1f} s); prefill attention measured on {n_att} queries "
+                       f"(blocks 0-1 and the last block in full + {n_rand} random) in "
+                       f"{t_fix + t_rand:.1f} s and extrapolated by attended pairs to "
+                       f"{t_attn:.0f} s (extrapolated); all {n_dec} decode steps in full "
+                       f"{t_dec:.1f} s ({t_dec / max(1, n_dec) * 1e3:.1f} ms/step); step "
+                       f"{step_s:.0f} s"),
+            "step_s": round(step_s, 2), "extrapolated_s": round(t_attn, 2),
+            "decode_ms_per_step": round(t_dec / max(1, n_dec) * 1e3, 2),
+            "selection_vs_oracle": ties}
 
 
 def main():
@@ -584,13 +638,15 @@ def main():
                      "traffic": stored_traffic(cfg.name),
                      "launch_ms": round(attn_ms, 3), "launches_per_step": n_calls},
     }
+    sel_final = bufs.sel.cpu().numpy()
     if not args.no_dec16:
         print("[bench] batched decode (dec16)", file=sys.stderr, flush=True)
         del bufs, dbufs, dec_graph
         out["decode16"] = measure_dec16(dev, args.seed, with_cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(x, cfg)
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(x, cfg, sel_final, n_dec)
+        out["selection_vs_oracle"] = out["cpu_baseline"].pop("selection_vs_oracle")
     print(json.dumps(out), flush=True)
 
 

@@ -319,9 +319,8 @@ __device__ __forceinline__ uint32_t unit_wg(uint32_t u, uint32_t u_q, uint32_t u
 // workgroup to finish its part of the run: the workgroups b0..b1 whose unit
 // ranges meet the run each left one normalised partial and base-2
 // log-sum-exp (device-coherent records), in the slot of their first unit in
-// the run.  Thread t owns
-// four consecutive columns of one query head; the partials' loads go out in
-// batches of kBatch so their round trips overlap.
+// the run.  Thread t owns four consecutive columns of one query head; the
+// partials' loads go out in batches of kBatch so their round trips overlap.
 template <int G>
 __device__ __forceinline__ void combine_run(uint32_t sg, uint32_t ups_g, uint32_t u_q,
                                             uint32_t u_r, int hq, int hkv,

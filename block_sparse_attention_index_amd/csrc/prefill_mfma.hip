@@ -491,24 +491,53 @@ typedef __attribute__((address_space(3))) void *lptr_t;
 __device__ __forceinline__ int kswz(int r, int sgm) { return sgm ^ (r & 15); }
 __device__ __forceinline__ int vswz(int r, int sgm) { return sgm ^ (4 * (r & 3)); }
 
+// Each 16-byte piece of a chunk goes by a buffer load straight into LDS: the
+// chunk's first row is the buffer base (scalar registers), so a lane's
+// source offset is a constant of its slot for every full chunk (no address
+// arithmetic per chunk); only a short chunk recomputes them, clamping rows.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const uint16_t *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lptr_t dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
+template <int NW>
+struct ChunkOffsets {
+  static constexpr int IPW = (kKA * kD / 8) / (64 * NW);   // instructions per wave
+  uint32_t k[IPW], v[IPW];
+  __device__ __forceinline__ void init(int nrows) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = ((wave * IPW + i) * 64 + lane) >> 4, sp = lane & 15;
+      const int rr = r < nrows ? r : nrows - 1;
+      k[i] = (uint32_t)(rr * kD + kswz(r, sp) * 8) * 2;
+      v[i] = (uint32_t)(rr * kD + vswz(r, sp) * 8) * 2;
+    }
+  }
+};
+
 template <int NW>
 __device__ __forceinline__ void async_chunk(AsyncSmem &sm, const uint16_t *k,
                                             const uint16_t *v, int64_t row0,
-                                            int nrows) {
-  constexpr int IPW = (kKA * kD / 8) / (64 * NW);   // instructions per wave
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                                            int nrows, const ChunkOffsets<NW> &full) {
+  constexpr int IPW = ChunkOffsets<NW>::IPW;
+  const int wave = threadIdx.x >> 6;
+  ChunkOffsets<NW> part;
+  const ChunkOffsets<NW> *off = &full;
+  if (nrows < kKA) {
+    part.init(nrows);
+    off = &part;
+  }
+  const uint32_t bytes = (uint32_t)nrows * kD * 2;
+  const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(k + row0 * kD, bytes);
+  const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(v + row0 * kD, bytes);
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int inst = wave * IPW + i;
-    const int pslot = inst * 64 + lane;              // 16-byte slot in the tile
-    const int r = pslot >> 4, sp = pslot & 15;
-    const int64_t rr = row0 + (r < nrows ? r : nrows - 1);
-    __builtin_amdgcn_global_load_lds(
-        (gptr_t)(const_cast<uint16_t *>(k + rr * kD + kswz(r, sp) * 8)),
-        (lptr_t)(&sm.Ks[inst * 64 * 8]), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(
-        (gptr_t)(const_cast<uint16_t *>(v + rr * kD + vswz(r, sp) * 8)),
-        (lptr_t)(&sm.Vs[inst * 64 * 8]), 16, 0, 0);
+    lds_dma16(rk, (lptr_t)(&sm.Ks[inst * 64 * 8]), off->k[i]);
+    lds_dma16(rv, (lptr_t)(&sm.Vs[inst * 64 * 8]), off->v[i]);
   }
 }
 
@@ -611,9 +640,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   int64_t n_chunks = (nkeys + kKA - 1) / kKA;
   int64_t ci = 0;
   stage_q(g, qraw);
+  ChunkOffsets<NW> coff;
+  coff.init(kKA);
   async_chunk<NW>(sm0, k + ((int64_t)g * kv_stride) * kD,
                   v + ((int64_t)g * kv_stride) * kD, (int64_t)inf.x * B,
-                  (int)(nkeys < kKA ? nkeys : kKA));
+                  (int)(nkeys < kKA ? nkeys : kKA), coff);
   // Metadata of the next item.  The one after it is fetched at the start of
   // each item's last chunk, so the load completes under that chunk's
   // compute and is only moved into place after the chunk's barrier.
@@ -681,12 +712,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
       const int64_t nxt_row = kc + kKA;
       async_chunk<NW>(nxt, k + ((int64_t)g * kv_stride) * kD,
                       v + ((int64_t)g * kv_stride) * kD, b * B + nxt_row,
-                      (int)(nkeys - nxt_row < kKA ? nkeys - nxt_row : kKA));
+                      (int)(nkeys - nxt_row < kKA ? nkeys - nxt_row : kKA), coff);
     } else if (has_next) {
       const int64_t nk = kv_keys(infn.x);
       async_chunk<NW>(nxt, k + ((int64_t)gn * kv_stride) * kD,
                       v + ((int64_t)gn * kv_stride) * kD, (int64_t)infn.x * B,
-                      (int)(nk < kKA ? nk : kKA));
+                      (int)(nk < kKA ? nk : kKA), coff);
     }
 #pragma unroll
     for (int sub = 0; sub < kKA / 32; ++sub) {
