@@ -38,6 +38,8 @@ bool prefill_shape_ok(int64_t q_pos0, int64_t n_q, int32_t hq, int32_t d, int32_
       hq > kMaxHeads || d < 1 || d > kMaxD)
     return false;
   const __int128 toks = (__int128)q_pos0 + n_q;
+  // blocks, tiles and CSR offsets are numbered in 32 bits
+  if (toks / block >= INT32_MAX / 2) return false;
   return bytes_fit(toks * topk * hq * (d + 2) * 4 + (toks / block + 1) * 4096);
 }
 // Decode partials: one record of Hq * (d + 1) floats per (sequence, selected
@@ -264,13 +266,17 @@ int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
 }
 
 // ---------------------------------------------------------------------------
-// Several sequences in one call: the prefill path per sequence, in order, on
-// one stream, sharing one workspace (stream order makes the reuse safe).
+// Several sequences in one call.  bf16 with d = 128 (the matrix-core path):
+// the sequences go in chains of at most 64 (and at most kChainBytes of
+// workspace, a single larger sequence making a chain of its own), each chain
+// one launch sequence over all its sequences -- pool, top-K, CSR inversion and
+// sparse attention with merge -- with every sequence's blocks numbered in
+// one global CSR.  Other types and head sizes: the single-sequence path per
+// sequence, in order, sharing one workspace (stream order makes the reuse
+// safe).
 // ---------------------------------------------------------------------------
 namespace {
-struct VarlenLayout {
-  size_t kmax, row_ptr, q_list, slot, inv, attn, total;
-};
+constexpr size_t kChainBytes = size_t(16) << 30;
 
 bool varlen_lens_ok(int32_t n_seq, const int64_t *cu_q, const int64_t *cu_kv) {
   if (!cu_q || !cu_kv || n_seq < 1 || n_seq > kMaxGridY || cu_q[0] != 0 || cu_kv[0] != 0)
@@ -286,9 +292,104 @@ bool varlen_lens_ok(int32_t n_seq, const int64_t *cu_q, const int64_t *cu_kv) {
   return true;
 }
 
+bool chain_path(int32_t dtype, int32_t d) { return dtype == MSA_BF16 && d == 128; }
+
+// Sub-buffers of one chain (or, on the per-sequence path, of one sequence).
+struct VarlenLayout {
+  size_t kmax, row_ptr, q_list, slot, sel_g, inv, attn, total;
+};
+
+VarlenLayout make_layout(int64_t nb, int64_t nq, int32_t d_idx, int32_t topk, size_t inv,
+                         size_t attn) {
+  VarlenLayout L;
+  size_t off = 0;
+  L.kmax = off;    off += msa::align256((size_t)nb * d_idx * 4);
+  L.row_ptr = off; off += msa::align256((size_t)(nb + 1) * 4);
+  L.q_list = off;  off += msa::align256((size_t)nq * topk * 4);
+  L.slot = off;    off += msa::align256((size_t)nq * topk * 4);
+  L.sel_g = off;   off += msa::align256((size_t)nq * topk * 4);
+  L.inv = off;     off += msa::align256(std::max<size_t>(inv, 1));
+  L.attn = off;    off += msa::align256(std::max<size_t>(attn, 1));
+  L.total = off;
+  return L;
+}
+
+// The table of the sequences [a, e) with queries (empty ones skipped): query
+// rows from cu_q[a], K/V rows absolute.
+msa::SeqTab chain_tab(const int64_t *cu_q, const int64_t *cu_kv, int32_t a, int32_t e,
+                      int32_t block) {
+  msa::SeqTab t{};
+  t.B = block;
+  int n = 0;
+  for (int32_t s = a; s < e; ++s) {
+    const int64_t qn = cu_q[s + 1] - cu_q[s], kvn = cu_kv[s + 1] - cu_kv[s];
+    if (qn == 0) continue;
+    t.q_row0[n] = cu_q[s] - cu_q[a];
+    t.q_pos0[n] = kvn - qn;
+    t.kv_row0[n] = cu_kv[s];
+    t.blk0[n + 1] = t.blk0[n] + (int32_t)cdiv(kvn, block);
+    t.qt0[n + 1] = t.qt0[n] + (int32_t)cdiv(qn, 64);
+    t.ob0[n + 1] = t.ob0[n] + (int32_t)((kvn - 1) / block - (kvn - qn) / block + 1);
+    ++n;
+    t.q_row0[n] = cu_q[s + 1] - cu_q[a];
+    t.kv_row0[n] = cu_kv[s + 1];
+  }
+  t.n = n;
+  return t;
+}
+
+VarlenLayout chain_layout(const msa::SeqTab &t, int32_t hq, int32_t d, int32_t d_idx,
+                          int32_t topk) {
+  const int64_t nb = t.blk0[t.n], nq = t.q_row0[t.n];
+  return make_layout(nb, nq, d_idx, topk, msa::invert_ws_bytes(nq, topk, nb),
+                     msa::prefill_chain_ws_bytes(t, hq, d, topk));
+}
+
+// Calls fn(a, e, table, layout) for each chain, in order.
+extern "C++" template <typename F>
+void for_each_chain(int32_t n_seq, const int64_t *cu_q, const int64_t *cu_kv, int32_t hq,
+                    int32_t d, int32_t d_idx, int32_t block, int32_t topk, F &&fn) {
+  int32_t a = 0;
+  while (a < n_seq) {
+    int32_t e = a, n = 0;
+    while (e < n_seq) {
+      if (cu_q[e + 1] == cu_q[e]) {
+        ++e;
+        continue;
+      }
+      if (n > 0) {
+        if (n == msa::kMaxSeqs) break;
+        const msa::SeqTab t = chain_tab(cu_q, cu_kv, a, e + 1, block);
+        if (!pairs_ok(t.q_row0[t.n], topk) || t.blk0[t.n] >= INT32_MAX / 2 ||
+            chain_layout(t, hq, d, d_idx, topk).total > kChainBytes)
+          break;
+      }
+      ++e;
+      ++n;
+    }
+    const msa::SeqTab t = chain_tab(cu_q, cu_kv, a, e, block);
+    if (t.n > 0) fn(a, e, t, chain_layout(t, hq, d, d_idx, topk));
+    a = e;
+  }
+}
+
 VarlenLayout varlen_layout(int32_t dtype, int32_t n_seq, const int64_t *cu_q,
                            const int64_t *cu_kv, int32_t hq, int32_t d, int32_t d_idx,
                            int32_t block, int32_t topk) {
+  if (chain_path(dtype, d)) {
+    // one layout for every chain: each field sized for the largest chain
+    int64_t nb_max = 1, q_max = 1;
+    size_t inv = 0, attn = 0;
+    for_each_chain(n_seq, cu_q, cu_kv, hq, d, d_idx, block, topk,
+                   [&](int32_t, int32_t, const msa::SeqTab &t, const VarlenLayout &) {
+                     const int64_t nb = t.blk0[t.n], nq = t.q_row0[t.n];
+                     nb_max = std::max(nb_max, nb);
+                     q_max = std::max(q_max, nq);
+                     inv = std::max(inv, msa::invert_ws_bytes(nq, topk, nb));
+                     attn = std::max(attn, msa::prefill_chain_ws_bytes(t, hq, d, topk));
+                   });
+    return make_layout(nb_max, q_max, d_idx, topk, inv, attn);
+  }
   int64_t nb_max = 1, q_max = 1;
   size_t inv = 0, attn = 0;
   for (int32_t s = 0; s < n_seq; ++s) {
@@ -300,17 +401,7 @@ VarlenLayout varlen_layout(int32_t dtype, int32_t n_seq, const int64_t *cu_q,
     inv = std::max(inv, msa::invert_ws_bytes(qn, topk, nb));
     attn = std::max(attn, msa::prefill_ws_bytes(dtype, kvn - qn, qn, hq, d, block, topk));
   }
-  auto a256 = [](size_t x) { return (x + 255) / 256 * 256; };
-  VarlenLayout L;
-  size_t off = 0;
-  L.kmax = off;    off += a256((size_t)nb_max * d_idx * 4);
-  L.row_ptr = off; off += a256((size_t)(nb_max + 1) * 4);
-  L.q_list = off;  off += a256((size_t)q_max * topk * 4);
-  L.slot = off;    off += a256((size_t)q_max * topk * 4);
-  L.inv = off;     off += a256(std::max<size_t>(inv, 1));
-  L.attn = off;    off += a256(std::max<size_t>(attn, 1));
-  L.total = off;
-  return L;
+  return make_layout(nb_max, q_max, d_idx, topk, inv, attn);
 }
 }  // namespace
 
@@ -343,11 +434,34 @@ int msa_prefill_varlen(const void *q, const void *k, const void *v, const float 
   int32_t *row_ptr = reinterpret_cast<int32_t *>(w + L.row_ptr);
   int32_t *q_list = reinterpret_cast<int32_t *>(w + L.q_list);
   int32_t *slot = reinterpret_cast<int32_t *>(w + L.slot);
+  int32_t *sel_g = reinterpret_cast<int32_t *>(w + L.sel_g);
   void *inv_ws = w + L.inv;
   void *attn_ws = w + L.attn;
   const hipStream_t st = as_stream(stream);
   const int64_t es = dtype == MSA_BF16 ? 2 : 4;   // bytes per q/k/v element
   const int64_t total_kv = cu_kv[n_seq];
+  if (chain_path(dtype, d)) {
+    hipError_t e = hipSuccess;
+    for_each_chain(n_seq, cu_q, cu_kv, hq, d, d_idx, block, topk,
+                   [&](int32_t a, int32_t, const msa::SeqTab &t, const VarlenLayout &) {
+                     if (e != hipSuccess) return;
+                     const int64_t r0 = cu_q[a], nq = t.q_row0[t.n], nb = t.blk0[t.n];
+                     int32_t *sel_c = sel + r0 * topk;
+                     e = msa::launch_pool_tab(idx_k, t, d_idx, kmax, st);
+                     if (e == hipSuccess)
+                       e = msa::launch_topk_tab(idx_q + r0 * d_idx, t, kmax, d_idx, topk, 1,
+                                                sel_c, sel_g, st);
+                     if (e == hipSuccess)
+                       e = msa::launch_invert(sel_g, nq, topk, nb, row_ptr, q_list, slot,
+                                              inv_ws, st);
+                     if (e == hipSuccess)
+                       e = msa::launch_prefill_chain(
+                           static_cast<const char *>(q) + r0 * hq * d * es, k, v, total_kv, t,
+                           hq, hkv, d, sel_c, topk, row_ptr, q_list, slot, scale,
+                           o + r0 * hq * d, lse ? lse + r0 * hq : nullptr, attn_ws, st);
+                   });
+    return e == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+  }
   for (int32_t s = 0; s < n_seq; ++s) {
     const int64_t qn = cu_q[s + 1] - cu_q[s], kvn = cu_kv[s + 1] - cu_kv[s];
     if (qn == 0) continue;

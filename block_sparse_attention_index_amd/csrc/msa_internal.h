@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "seqtab.h"
+
 namespace msa {
 
 // Launch helpers: each enqueues its kernels on `st` and returns the HIP
@@ -24,6 +26,15 @@ hipError_t launch_topk_prefill(const float *idx_q, int64_t n_q, int64_t q_pos0,
                                const float *kmax, int64_t nb, int32_t d_idx,
                                int32_t block, int32_t topk, int32_t win, int32_t *sel,
                                hipStream_t st);
+
+// Chain-table forms (sequences packed one after another, see seqtab.h):
+// the max-pool of every global block, and the per-query top-K of every
+// sequence (sel: local block ids; sel_g, if not null: global ids).
+hipError_t launch_pool_tab(const float *idx_k, const SeqTab &tab, int32_t d_idx, float *kmax,
+                           hipStream_t st);
+hipError_t launch_topk_tab(const float *idx_q, const SeqTab &tab, const float *kmax,
+                           int32_t d_idx, int32_t topk, int32_t win, int32_t *sel,
+                           int32_t *sel_g, hipStream_t st);
 
 size_t topk_decode_ws_bytes(int32_t n_seq, int64_t nb_max, int32_t topk);
 hipError_t launch_topk_decode(const float *idx_q, int32_t n_seq,
@@ -52,6 +63,18 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v,
                           const int32_t *row_ptr, const int32_t *q_list,
                           const int32_t *slot, float scale, float *o,
                           float *lse, void *ws, hipStream_t st);
+
+// The matrix-core sparse prefill (bf16, d = 128) over the sequences of one
+// chain table (queries packed by sequence, K/V rows at tab.kv_row0[s]): the
+// workspace it needs and its launch.  The CSR is global over the table's
+// blocks.
+size_t prefill_chain_ws_bytes(const SeqTab &tab, int32_t hq, int32_t d, int32_t topk);
+hipError_t launch_prefill_chain(const void *q, const void *k, const void *v,
+                                int64_t kv_stride, const SeqTab &tab, int32_t hq,
+                                int32_t hkv, int32_t d, const int32_t *sel, int32_t topk,
+                                const int32_t *row_ptr, const int32_t *q_list,
+                                const int32_t *slot, float scale, float *o, float *lse,
+                                void *ws, hipStream_t st);
 
 size_t decode_ws_bytes(int32_t n_seq, int32_t hq, int32_t d, int32_t block,
                        int32_t topk);

@@ -286,9 +286,9 @@ hipError_t launch_generic(const T *q, const T *k, const T *v, int64_t kv_stride,
   const int64_t nb = (q_pos0 + n_q + B - 1) / B;
   const float sl2 = scale * kLog2e;
   if (n_part > 0) {
-    hipLaunchKernelGGL(prefill_tiles, dim3(1), dim3(1024), 0, st, row_ptr, nb,
-                       q_pos0, n_q, B, kQTA, tile_ptr);
     const int64_t grid = n_part / kQTA + nb;
+    hipLaunchKernelGGL(prefill_tiles, dim3(1), dim3(1024), 0, st, row_ptr,
+                       seqtab_one(q_pos0, n_q, B), kQTA, grid, tile_ptr);
     hipLaunchKernelGGL((prefill_nonown_generic<T, G, DU>),
                        dim3((unsigned)grid, hkv), dim3(256), 0, st, q, k, v,
                        kv_stride, q_pos0, n_q, hq, B, row_ptr, q_list, tile_ptr,
@@ -342,12 +342,8 @@ size_t prefill_ws_bytes(int32_t dtype, int64_t q_pos0, int64_t n_q, int32_t hq,
                         int32_t d, int32_t block, int32_t topk) {
   const int64_t nb = (q_pos0 + n_q + block - 1) / block;
   const int64_t np = nonown_pairs(q_pos0, n_q, block, topk);
-  if (dtype == 1 && d == 128) {
-    // matrix-core path: fp16 partial outputs and (lse, exponent) float2s
-    return align256((size_t)(nb + 1) * 4) + align256((size_t)np * hq * d * 2) +
-           align256((size_t)np * hq * 8) + align256((size_t)(np / 16 + nb) * 16) +
-           align256((size_t)(np + 256 * nb) * 4);
-  }
+  if (dtype == 1 && d == 128)   // matrix-core path
+    return prefill_chain_ws_bytes(seqtab_one(q_pos0, n_q, block), hq, d, topk);
   // + per-tile metadata of the MFMA pass A, bounded for any head group:
   //   tiles <= pairs / 16 + nb (16 = smallest tile), rows <= pairs + 256 nb.
   return align256((size_t)(nb + 1) * 4) + align256((size_t)np * hq * d * 4) +

@@ -3,6 +3,7 @@
 // per-row tile table of the KV-outer pass.
 #pragma once
 #include "msa_internal.h"
+#include "seqtab.h"
 
 namespace msa {
 
@@ -18,13 +19,16 @@ __device__ __host__ __forceinline__ int64_t own_through(int64_t b,
 
 namespace {
 
-// tile_ptr[b] = sum over rows b' < b of ceil(non-own entries of b' / tq).
+// tile_ptr[b] = sum over global rows b' < b of ceil(non-own entries of b' /
+// tq), capped at max_tiles (the workspace's tile capacity; a valid CSR never
+// reaches it, an invalid one is cut short rather than overrunning it).
 __global__ __launch_bounds__(1024) void prefill_tiles(
-    const int32_t *__restrict__ row_ptr, int64_t nb, int64_t q_pos0,
-    int64_t n_q, int B, int tq, int32_t *__restrict__ tile_ptr) {
+    const int32_t *__restrict__ row_ptr, SeqTab tab, int tq, int64_t max_tiles,
+    int32_t *__restrict__ tile_ptr) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nb = tab.blk0[tab.n];
   if (tid == 0) {
     carry_s = 0;
     tile_ptr[0] = 0;
@@ -34,8 +38,9 @@ __global__ __launch_bounds__(1024) void prefill_tiles(
     const int64_t b = base + tid;
     int32_t x = 0;
     if (b < nb) {
-      const int64_t own = own_through(b, q_pos0, n_q, B) -
-                          own_through(b - 1, q_pos0, n_q, B);
+      const int sq = prefix_find(tab.blk0, tab.n, b);
+      const int64_t lb = b - tab.blk0[sq];
+      const int64_t own = own_through_g(tab, sq, lb) - own_through_g(tab, sq, lb - 1);
       int64_t non = (int64_t)(row_ptr[b + 1] - row_ptr[b]) - own;
       if (non < 0) non = 0;
       x = (int32_t)((non + tq - 1) / tq);
@@ -49,7 +54,7 @@ __global__ __launch_bounds__(1024) void prefill_tiles(
     __syncthreads();
     int32_t off = carry_s;
     for (int w = 0; w < wave; ++w) off += wsum[w];
-    if (b < nb) tile_ptr[b + 1] = off + x;
+    if (b < nb) tile_ptr[b + 1] = off + x < max_tiles ? off + x : (int32_t)max_tiles;
     __syncthreads();
     if (tid == 1023) carry_s = off + x;
     __syncthreads();

@@ -31,6 +31,7 @@
 #include "msa_internal.h"
 #include "prefill_common.h"
 #include "mfma_common.h"
+#include "seqtab.h"
 
 namespace msa {
 namespace {
@@ -131,19 +132,20 @@ __device__ __forceinline__ void put_partial(uint16_t *part_o, float2 *part_le,
   if (hf == 0) part_le[n * hq + (int64_t)g * G + hl] = make_float2(mref + __log2f(ltot), (float)e);
 }
 
-// NB = 32-row N-blocks per wave, NW = waves per workgroup.  At most 256
-// registers per lane (two waves per SIMD): with NW = 4, two workgroups share
-// a CU, so one's merge loads overlap the other's matrix-core work.
-template <int G, int NB, int NW, bool OWN>
+// Own-block pass: workgroup = (tile of TPT own tokens of one query-holding
+// block of one sequence, KV head g).  NB = 32-row N-blocks per wave, NW =
+// waves per workgroup.  At most 256 registers per lane (two waves per SIMD):
+// with NW = 4, two workgroups share a CU, so one's merge loads overlap the
+// other's matrix-core work.  Query rows, selections, slots, outputs and CSR
+// positions are those of the whole chain (global); blocks in sel are local
+// to the query's sequence.
+template <int G, int NB, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, int64_t kv_stride, int64_t q_pos0,
-    int64_t n_q, int hq, int B, const int32_t *__restrict__ row_ptr,
-    const int32_t *__restrict__ q_list, const int32_t *__restrict__ tile_ptr,
-    int64_t nb, const int32_t *__restrict__ sel, int topk,
-    const int32_t *__restrict__ slot, float scale_log2,
-    uint16_t *__restrict__ part_o, float2 *__restrict__ part_le, int64_t n_part,
-    float *__restrict__ o, float *__restrict__ lse) {
+    const uint16_t *__restrict__ v, int64_t kv_stride, SeqTab tab, int hq,
+    const int32_t *__restrict__ sel, int topk, const int32_t *__restrict__ slot,
+    float scale_log2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_le,
+    int64_t n_part, float *__restrict__ o, float *__restrict__ lse) {
   constexpr int NT = 64 * NW;    // threads
   constexpr int TPN = 32 / G;    // tokens per 32-row N-block
   constexpr int TPW = NB * TPN;  // tokens per wave
@@ -154,30 +156,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, j = lane & 31;
 
-  // ---- the tile: block b, its key count, and each N-block row's query ----
-  int64_t b, nkeys, e0 = 0, e_end = 0, tok0 = 0, min_pos;
-  if constexpr (!OWN) {
-    const int64_t w = blockIdx.x;
-    if (w >= tile_ptr[nb]) return;
-    b = find_row(tile_ptr, nb, w);
-    const int64_t own_b =
-        own_through(b, q_pos0, n_q, B) - own_through(b - 1, q_pos0, n_q, B);
-    e0 = row_ptr[b] + own_b + (w - tile_ptr[b]) * TPT;
-    e_end = row_ptr[b + 1];
-    nkeys = B;
-    if (b * B + nkeys > kv_stride) nkeys = kv_stride - b * B;  // invalid input only
-    min_pos = INT64_MAX;
-  } else {
-    const int tpb = (B + TPT - 1) / TPT;
-    b = q_pos0 / B + blockIdx.x / tpb;
-    tok0 = b * B + (int64_t)(blockIdx.x % tpb) * TPT;
-    int64_t hi = tok0 + TPT - 1;
-    if (hi > b * B + B - 1) hi = b * B + B - 1;
-    if (hi > q_pos0 + n_q - 1) hi = q_pos0 + n_q - 1;
-    if (hi < tok0 || hi < q_pos0) return;
-    nkeys = hi - b * B + 1;
-    min_pos = tok0;
-  }
+  // ---- the tile: sequence s, its block b, the key count, each row's query ----
+  const int B = tab.B;
+  const int tpb = (B + TPT - 1) / TPT;
+  const int64_t bt = blockIdx.x / tpb;   // query-holding block of the chain
+  const int sq = prefix_find(tab.ob0, tab.n, bt);
+  const int64_t q_pos0 = tab.q_pos0[sq], n_q = seq_nq(tab, sq), row0 = tab.q_row0[sq];
+  const int64_t b = q_pos0 / B + (bt - tab.ob0[sq]);
+  const int64_t tok0 = b * B + (int64_t)(blockIdx.x % tpb) * TPT;
+  int64_t hi = tok0 + TPT - 1;
+  if (hi > b * B + B - 1) hi = b * B + B - 1;
+  if (hi > q_pos0 + n_q - 1) hi = q_pos0 + n_q - 1;
+  if (hi < tok0 || hi < q_pos0) return;
+  const int64_t nkeys = hi - b * B + 1;
+  const int64_t min_pos = tok0;
 
   int64_t qi[NB], pos[NB];
   bool act[NB];
@@ -187,18 +179,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   for (int nbk = 0; nbk < NB; ++nbk) {
     const int tl = wave * TPW + nbk * TPN + j / G;
     head[nbk] = j % G;
-    if constexpr (!OWN) {
-      const int64_t e = e0 + tl;
-      int64_t x = e < e_end ? q_list[e] : -1;
-      act[nbk] = x >= 0 && x < n_q;
-      qi[nbk] = act[nbk] ? x : 0;
-      pos[nbk] = q_pos0 + qi[nbk];
-    } else {
-      const int64_t p = tok0 + tl;
-      act[nbk] = p >= q_pos0 && p < q_pos0 + n_q && p < b * B + B;
-      pos[nbk] = p < b * B + B ? p : b * B + B - 1;
-      qi[nbk] = act[nbk] ? p - q_pos0 : 0;
-    }
+    const int64_t p = tok0 + tl;
+    act[nbk] = p >= q_pos0 && p < q_pos0 + n_q && p < b * B + B;
+    pos[nbk] = p < b * B + B ? p : b * B + B - 1;
+    qi[nbk] = act[nbk] ? row0 + (p - q_pos0) : 0;   // query row of the chain
     const uint16_t *qp = q + ((qi[nbk] * hq + (int64_t)g * G + head[nbk]) * kD);
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
@@ -222,8 +206,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     lsum[nbk] = 0.f;
   }
 
-  const uint16_t *kb = k + ((int64_t)g * kv_stride) * kD;
-  const uint16_t *vb = v + ((int64_t)g * kv_stride) * kD;
+  const uint16_t *kb = k + ((int64_t)g * kv_stride + tab.kv_row0[sq]) * kD;
+  const uint16_t *vb = v + ((int64_t)g * kv_stride + tab.kv_row0[sq]) * kD;
   const int64_t n_chunks = (nkeys + kKC - 1) / kKC;
   ChunkRegs<NT> cr;
   load_chunk(cr, kb, vb, b * B, (int)(nkeys < kKC ? nkeys : kKC));
@@ -254,13 +238,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int nbk = 0; nbk < NB; ++nbk) s[nbk] = mfma32(kf, qf[nbk][cc], s[nbk]);
       }
-      const bool need_mask =
-          koff0 + 31 >= nkeys || (OWN && b * B + koff0 + 31 > min_pos);
+      const bool need_mask = koff0 + 31 >= nkeys || b * B + koff0 + 31 > min_pos;
       bf16x8 pb[NB][2];
 #pragma unroll
       for (int nbk = 0; nbk < NB; ++nbk) {
         if (need_mask) {
-          const int64_t lim = OWN ? pos[nbk] - b * B : nkeys - 1;
+          const int64_t lim = pos[nbk] - b * B;
           const int64_t lim2 = lim < nkeys - 1 ? lim : nkeys - 1;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -325,13 +308,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   for (int nbk = 0; nbk < NB; ++nbk) {
     const float ltot = sum_with_partner(lsum[nbk]);
     const int hh = g * G + head[nbk];
-    if constexpr (!OWN) {
-      if (!act[nbk]) continue;
-      const int64_t e = e0 + wave * TPW + nbk * TPN + j / G;
-      const int64_t n_idx = e - own_through(b, q_pos0, n_q, B);
-      if (n_idx < 0 || n_idx >= n_part) continue;
-      put_partial(part_o, part_le, n_idx, g, hq, G, head[nbk], h, acc[nbk], mref[nbk], ltot);
-    } else {
+    {
       if (!act[nbk]) continue;
       const int64_t i = qi[nbk];
       const int32_t *srow = sel + i * topk;
@@ -350,7 +327,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
           if (kk < topk) {
             const int32_t bk = srow[kk], x = xrow[kk];
             if (bk >= 0 && bk < b) {
-              const int64_t n = x - own_through(bk, q_pos0, n_q, B);
+              const int64_t n = x - own_through_g(tab, sq, bk);
               if (n >= 0 && n < n_part) nid[kk] = n;
             }
           }
@@ -399,7 +376,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int kk = 0; kk < topk; ++kk) {
           const int32_t bk = srow[kk];
           if (bk < 0 || bk >= b) continue;
-          const int64_t n_idx = xrow[kk] - own_through(bk, q_pos0, n_q, B);
+          const int64_t n_idx = xrow[kk] - own_through_g(tab, sq, bk);
           if (n_idx < 0 || n_idx >= n_part) continue;
           mx = fmaxf(mx, part_le[n_idx * hq + hh].x);
         }
@@ -412,7 +389,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int kk = 0; kk < topk; ++kk) {
           const int32_t bk = srow[kk];
           if (bk < 0 || bk >= b) continue;
-          const int64_t n_idx = xrow[kk] - own_through(bk, q_pos0, n_q, B);
+          const int64_t n_idx = xrow[kk] - own_through_g(tab, sq, bk);
           if (n_idx < 0 || n_idx >= n_part) continue;
           const float2 le = part_le[n_idx * hq + hh];
           z += fast_exp2(le.x - mx);
@@ -556,35 +533,36 @@ __device__ __forceinline__ void async_wait_barrier() {
 // next item's metadata, query fragments and first K/V chunk are fetched while
 // the current item computes.
 //
-// Per-tile metadata (built by prefill_tile_info): info[t] = (block, first CSR
-// position, row end) and tq[t][i] = query index of the tile's i-th row token
-// (-1 past the row end).
+// Per-tile metadata (built by prefill_tile_info): info[t] = (global block,
+// first CSR position, row end, sequence) and tq[t][i] = query row of the
+// tile's i-th row token (-1 past the row end).
 // ---------------------------------------------------------------------------
 template <int TPT>
 __global__ __launch_bounds__(256) void prefill_tile_info(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ tile_ptr,
-    const int32_t *__restrict__ q_list, int64_t q_pos0, int64_t n_q, int B,
-    int4 *__restrict__ info, int32_t *__restrict__ tq) {
-  const int64_t b = blockIdx.x;
-  const int32_t t0 = tile_ptr[b], t1 = tile_ptr[b + 1];
+    const int32_t *__restrict__ q_list, SeqTab tab, int4 *__restrict__ info,
+    int32_t *__restrict__ tq) {
+  const int64_t gb = blockIdx.x;
+  const int32_t t0 = tile_ptr[gb], t1 = tile_ptr[gb + 1];
   if (t0 == t1) return;
-  const int64_t own_b =
-      own_through(b, q_pos0, n_q, B) - own_through(b - 1, q_pos0, n_q, B);
-  const int32_t base = (int32_t)(row_ptr[b] + own_b), end = row_ptr[b + 1];
+  const int sq = prefix_find(tab.blk0, tab.n, gb);
+  const int64_t b = gb - tab.blk0[sq];
+  const int64_t own_b = own_through_g(tab, sq, b) - own_through_g(tab, sq, b - 1);
+  const int32_t base = (int32_t)(row_ptr[gb] + own_b), end = row_ptr[gb + 1];
   for (int x = threadIdx.x; x < (t1 - t0) * TPT; x += 256) {
     const int tt = x / TPT, i = x % TPT;
     const int32_t e = base + tt * TPT + i;
     tq[(int64_t)(t0 + tt) * TPT + i] = e < end ? q_list[e] : -1;
-    if (i == 0) info[t0 + tt] = make_int4((int)b, base + tt * TPT, end, 0);
+    if (i == 0) info[t0 + tt] = make_int4((int)gb, base + tt * TPT, end, sq);
   }
 }
 
 template <int G, int NW>
 __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, int64_t kv_stride, int64_t q_pos0,
-    int64_t n_q, int hq, int hkv, int B, const int32_t *__restrict__ tile_ptr,
-    int64_t nb, const int4 *__restrict__ info, const int32_t *__restrict__ tq,
+    const uint16_t *__restrict__ v, int64_t kv_stride, SeqTab tab, int hq, int hkv,
+    const int32_t *__restrict__ tile_ptr, const int4 *__restrict__ info,
+    const int32_t *__restrict__ tq,
     float scale_log2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_le,
     int64_t n_part) {
   constexpr int TPN = 32 / G;
@@ -599,7 +577,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   const int tl = wave * TPN + j / G;  // token slot of this lane's row
   const int hl = j % G;                // head of this lane's row in the group
 
-  const int64_t T = tile_ptr[nb];
+  const int B = tab.B;
+  const int64_t n_q = tab.q_row0[tab.n];   // query rows of the chain
+  const int64_t T = tile_ptr[tab.blk0[tab.n]];
   const int64_t W = T * hkv;
   const int xcd = blockIdx.x & 7;
   const int64_t per = gridDim.x >> 3, r = blockIdx.x >> 3;
@@ -626,9 +606,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
       dst[cc] = as_bf16x8(x);
     }
   };
-  auto kv_keys = [&](int64_t bb) {
+  // first K/V row of an item's block (info: global block, ..., sequence) and
+  // its key count (B: a non-own block is always full)
+  auto kv_row = [&](const int4 &f) {
+    return tab.kv_row0[f.w] + (int64_t)(f.x - tab.blk0[f.w]) * B;
+  };
+  auto kv_keys = [&](const int4 &f) {
     int64_t n = B;
-    if (bb * B + n > kv_stride) n = kv_stride - bb * B;   // invalid input only
+    const int64_t r0 = kv_row(f);
+    if (r0 + n > kv_stride) n = kv_stride - r0;   // invalid input only
     return n;
   };
 
@@ -636,14 +622,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   int g = (int)(w / T);
   int4 inf = info[w % T];
   int32_t qraw = tq[(w % T) * TPT + tl];
-  int64_t nkeys = kv_keys(inf.x);
+  int64_t nkeys = kv_keys(inf);
   int64_t n_chunks = (nkeys + kKA - 1) / kKA;
   int64_t ci = 0;
   stage_q(g, qraw);
   ChunkOffsets<NW> coff;
   coff.init(kKA);
   async_chunk<NW>(sm0, k + ((int64_t)g * kv_stride) * kD,
-                  v + ((int64_t)g * kv_stride) * kD, (int64_t)inf.x * B,
+                  v + ((int64_t)g * kv_stride) * kD, kv_row(inf),
                   (int)(nkeys < kKA ? nkeys : kKA), coff);
   // Metadata of the next item.  The one after it is fetched at the start of
   // each item's last chunk, so the load completes under that chunk's
@@ -698,7 +684,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     constexpr int P = decltype(tag)::value;
     AsyncSmem &cur = P ? sm1 : sm0;
     AsyncSmem &nxt = P ? sm0 : sm1;
-    const int64_t b = inf.x;
+    const int64_t row0 = kv_row(inf);
     const int64_t kc = ci * kKA;
     const bool last = ci + 1 >= n_chunks;
     int gnn = 0;
@@ -711,12 +697,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     if (!last) {
       const int64_t nxt_row = kc + kKA;
       async_chunk<NW>(nxt, k + ((int64_t)g * kv_stride) * kD,
-                      v + ((int64_t)g * kv_stride) * kD, b * B + nxt_row,
+                      v + ((int64_t)g * kv_stride) * kD, row0 + nxt_row,
                       (int)(nkeys - nxt_row < kKA ? nkeys - nxt_row : kKA), coff);
     } else if (has_next) {
-      const int64_t nk = kv_keys(infn.x);
+      const int64_t nk = kv_keys(infn);
       async_chunk<NW>(nxt, k + ((int64_t)gn * kv_stride) * kD,
-                      v + ((int64_t)gn * kv_stride) * kD, (int64_t)infn.x * B,
+                      v + ((int64_t)gn * kv_stride) * kD, kv_row(infn),
                       (int)(nk < kKA ? nk : kKA), coff);
     }
 #pragma unroll
@@ -796,7 +782,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
       const float ltot = sum_with_partner(lsum);
       if (act) {
         const int64_t e = (int64_t)inf.y + tl;
-        const int64_t n_idx = e - own_through(b, q_pos0, n_q, B);
+        const int64_t n_idx = e - own_through_g(tab, inf.w, inf.x - tab.blk0[inf.w]);
         if (n_idx >= 0 && n_idx < n_part)
           put_partial(part_o, part_le, n_idx, g, hq, G, hl, h, acc, mref, ltot);
       }
@@ -816,7 +802,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     gn = gnn;
     infn = infnn;
     qrawn = qrawnn;
-    nkeys = kv_keys(inf.x);
+    nkeys = kv_keys(inf);
     n_chunks = (nkeys + kKA - 1) / kKA;
     ci = 0;
     read_q(qraw, qf);
@@ -850,36 +836,65 @@ int num_cus() {
 
 template <int G, int NB, int NW>
 hipError_t launch_mfma_g(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         int64_t kv_stride, int64_t q_pos0, int64_t n_q, int hq,
-                         int hkv, int B, const int32_t *sel, int topk,
-                         const int32_t *row_ptr, const int32_t *q_list,
-                         const int32_t *slot, float scale, float *o, float *lse,
-                         int32_t *tile_ptr, int4 *info, int32_t *tq,
+                         int64_t kv_stride, const SeqTab &tab, int hq, int hkv,
+                         const int32_t *sel, int topk, const int32_t *row_ptr,
+                         const int32_t *q_list, const int32_t *slot, float scale, float *o,
+                         float *lse, int32_t *tile_ptr, int4 *info, int32_t *tq,
                          uint16_t *part_o, float2 *part_le, int64_t n_part,
-                         hipStream_t st) {
+                         int64_t max_tiles, hipStream_t st) {
   constexpr int TPT = NW * NB * (32 / G);
-  const int64_t nb = (q_pos0 + n_q + B - 1) / B;
+  const int64_t nb = tab.blk0[tab.n];
   const float sl2 = scale * kLog2e;
   if (n_part > 0) {
-    hipLaunchKernelGGL(prefill_tiles, dim3(1), dim3(1024), 0, st, row_ptr, nb,
-                       q_pos0, n_q, B, TPT, tile_ptr);
-    hipLaunchKernelGGL((prefill_tile_info<TPT>), dim3((unsigned)nb), dim3(256), 0,
-                       st, row_ptr, tile_ptr, q_list, q_pos0, n_q, B, info, tq);
+    hipLaunchKernelGGL(prefill_tiles, dim3(1), dim3(1024), 0, st, row_ptr, tab, TPT,
+                       max_tiles, tile_ptr);
+    hipLaunchKernelGGL((prefill_tile_info<TPT>), dim3((unsigned)nb), dim3(256), 0, st,
+                       row_ptr, tile_ptr, q_list, tab, info, tq);
     const int grid = 8 * ((num_cus() + 7) / 8);
     hipLaunchKernelGGL((prefill_nonown_persistent<G, NW>), dim3(grid), dim3(64 * NW),
-                       0, st, q, k, v, kv_stride, q_pos0, n_q, hq, hkv, B, tile_ptr,
-                       nb, info, tq, sl2, part_o, part_le, n_part);
+                       0, st, q, k, v, kv_stride, tab, hq, hkv, tile_ptr, info, tq, sl2,
+                       part_o, part_le, n_part);
   }
-  // own-block pass: 4-wave workgroups (see prefill_mfma_kernel)
+  // own-block pass: 4-wave workgroups (see prefill_mfma_kernel), one per
+  // tile of TPTB own tokens of every query-holding block of every sequence
   constexpr int NWB = 4;
   constexpr int TPTB = NWB * NB * (32 / G);
-  const int64_t b_first = q_pos0 / B, b_last = (q_pos0 + n_q - 1) / B;
-  const int64_t tiles = (b_last - b_first + 1) * ((B + TPTB - 1) / TPTB);
-  hipLaunchKernelGGL((prefill_mfma_kernel<G, NB, NWB, true>),
-                     dim3((unsigned)tiles, hkv), dim3(64 * NWB), 0, st, q, k, v,
-                     kv_stride, q_pos0, n_q, hq, B, row_ptr, q_list, tile_ptr, nb,
-                     sel, topk, slot, sl2, part_o, part_le, n_part, o, lse);
+  const int64_t tiles = (int64_t)tab.ob0[tab.n] * ((tab.B + TPTB - 1) / TPTB);
+  if (tiles > 0)
+    hipLaunchKernelGGL((prefill_mfma_kernel<G, NB, NWB>), dim3((unsigned)tiles, hkv),
+                       dim3(64 * NWB), 0, st, q, k, v, kv_stride, tab, hq, sel, topk, slot,
+                       sl2, part_o, part_le, n_part, o, lse);
   return hipGetLastError();
+}
+
+// Workspace of one chain on the matrix-core path: the tile table, one fp16
+// partial record (+ (lse, exponent)) per (non-own pair, query head), and the
+// per-tile metadata, bounded for any head group (tiles <= pairs / 16 + blocks,
+// tile rows <= pairs + 256 blocks).
+int64_t chain_nonown_pairs(const SeqTab &tab, int32_t topk) {
+  int64_t np = 0;
+  for (int s = 0; s < tab.n; ++s) np += nonown_pairs(tab.q_pos0[s], seq_nq(tab, s), tab.B, topk);
+  return np;
+}
+
+struct MfmaLayout {
+  size_t tile_ptr, part_o, part_le, info, tq, total;
+  int64_t np, nb, max_tiles;
+};
+MfmaLayout mfma_layout(const SeqTab &tab, int32_t hq, int32_t d, int32_t topk, int tpt) {
+  MfmaLayout L;
+  L.nb = tab.blk0[tab.n];
+  L.np = chain_nonown_pairs(tab, topk);
+  size_t off = 0;
+  L.tile_ptr = off; off += align256((size_t)(L.nb + 1) * 4);
+  L.part_o = off;   off += align256((size_t)L.np * hq * d * 2);
+  L.part_le = off;  off += align256((size_t)L.np * hq * 8);
+  L.info = off;     off += align256((size_t)(L.np / 16 + L.nb) * 16);
+  L.tq = off;       off += align256((size_t)(L.np + 256 * L.nb) * 4);
+  L.total = off;
+  const int64_t by_info = L.np / 16 + L.nb, by_tq = (L.np + 256 * L.nb) / tpt;
+  L.max_tiles = by_info < by_tq ? by_info : by_tq;
+  return L;
 }
 
 }  // namespace
@@ -889,36 +904,32 @@ bool mfma_prefill_supported(int32_t dtype, int32_t d, int32_t group) {
          (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
 }
 
-hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v,
-                               int64_t kv_stride, int64_t q_pos0, int64_t n_q,
-                               int32_t hq, int32_t hkv, int32_t d,
-                               int32_t block, const int32_t *sel, int32_t topk,
-                               const int32_t *row_ptr, const int32_t *q_list,
-                               const int32_t *slot, float scale, float *o,
-                               float *lse, void *ws, hipStream_t st) {
-  (void)d;
+size_t prefill_chain_ws_bytes(const SeqTab &tab, int32_t hq, int32_t d, int32_t topk) {
+  return mfma_layout(tab, hq, d, topk, 16).total;
+}
+
+hipError_t launch_prefill_chain(const void *q, const void *k, const void *v,
+                                int64_t kv_stride, const SeqTab &tab, int32_t hq,
+                                int32_t hkv, int32_t d, const int32_t *sel, int32_t topk,
+                                const int32_t *row_ptr, const int32_t *q_list,
+                                const int32_t *slot, float scale, float *o, float *lse,
+                                void *ws, hipStream_t st) {
   const int G = hq / hkv;
-  const int64_t nb = (q_pos0 + n_q + block - 1) / block;
-  const int64_t np = nonown_pairs(q_pos0, n_q, block, topk);
+  const MfmaLayout L = mfma_layout(tab, hq, d, topk, 32 / G * 8);
   char *w = static_cast<char *>(ws);
-  int32_t *tile_ptr = reinterpret_cast<int32_t *>(w);
-  w += align256((size_t)(nb + 1) * 4);
-  uint16_t *part_o = reinterpret_cast<uint16_t *>(w);
-  w += align256((size_t)np * hq * d * 2);
-  float2 *part_le = reinterpret_cast<float2 *>(w);
-  w += align256((size_t)np * hq * 8);
-  int4 *info = reinterpret_cast<int4 *>(w);
-  w += align256((size_t)(np / 16 + nb) * 16);   // same bound as the size query
-  int32_t *tq = reinterpret_cast<int32_t *>(w);
+  int32_t *tile_ptr = reinterpret_cast<int32_t *>(w + L.tile_ptr);
+  uint16_t *part_o = reinterpret_cast<uint16_t *>(w + L.part_o);
+  float2 *part_le = reinterpret_cast<float2 *>(w + L.part_le);
+  int4 *info = reinterpret_cast<int4 *>(w + L.info);
+  int32_t *tq = reinterpret_cast<int32_t *>(w + L.tq);
   const uint16_t *qq = static_cast<const uint16_t *>(q);
   const uint16_t *kk = static_cast<const uint16_t *>(k);
   const uint16_t *vv = static_cast<const uint16_t *>(v);
-#define MSA_MF(GG)                                                              \
-  case GG:                                                                      \
-    return launch_mfma_g<GG, 1, 8>(qq, kk, vv, kv_stride, q_pos0, n_q, hq, hkv,  \
-                                   block, sel, topk, row_ptr, q_list, slot,      \
-                                   scale, o, lse, tile_ptr, info, tq, part_o,    \
-                                   part_le, np, st);
+#define MSA_MF(GG)                                                                \
+  case GG:                                                                        \
+    return launch_mfma_g<GG, 1, 8>(qq, kk, vv, kv_stride, tab, hq, hkv, sel, topk,  \
+                                   row_ptr, q_list, slot, scale, o, lse, tile_ptr,  \
+                                   info, tq, part_o, part_le, L.np, L.max_tiles, st);
   switch (G) {
     MSA_MF(1)
     MSA_MF(2)
@@ -930,6 +941,17 @@ hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v,
   }
 #undef MSA_MF
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v,
+                               int64_t kv_stride, int64_t q_pos0, int64_t n_q,
+                               int32_t hq, int32_t hkv, int32_t d,
+                               int32_t block, const int32_t *sel, int32_t topk,
+                               const int32_t *row_ptr, const int32_t *q_list,
+                               const int32_t *slot, float scale, float *o,
+                               float *lse, void *ws, hipStream_t st) {
+  return launch_prefill_chain(q, k, v, kv_stride, seqtab_one(q_pos0, n_q, block), hq, hkv, d,
+                              sel, topk, row_ptr, q_list, slot, scale, o, lse, ws, st);
 }
 
 }  // namespace msa

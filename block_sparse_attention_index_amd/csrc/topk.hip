@@ -45,11 +45,17 @@ typedef float f32x16s __attribute__((ext_vector_type(16)));
 // 32 lanes of a half-wave reading one column of 32 rows hit 32 banks.
 // KMAX bounds the list length (K - window).
 // ---------------------------------------------------------------------------
+//
+// A launch covers the sequences of a chain table: tile t belongs to the
+// sequence s with qt0[s] <= t < qt0[s+1]; its queries are rows q_row0[s] ..
+// of idx_q / sel, its summaries rows blk0[s] .. of kmax.  sel receives block
+// ids local to the sequence; sel_g (if not null) the same rows with global
+// block ids (local + blk0[s], -1 kept).
 template <int KMAX, bool FULL>
 __global__ __launch_bounds__(256) void topk_prefill_kernel(
-    const float *__restrict__ idx_q, int64_t n_q, int64_t q_pos0,
-    const float *__restrict__ kmax, int d_idx, int B, int topk, int win,
-    int32_t *__restrict__ sel) {
+    const float *__restrict__ idx_q_all, SeqTab tab, const float *__restrict__ kmax_all,
+    int d_idx, int topk, int win, int32_t *__restrict__ sel_all,
+    int32_t *__restrict__ sel_g) {
   constexpr int kW = FULL ? kDFull : kDC;   // staged columns
   constexpr int kPad = kW + 1;
   __shared__ float qs[kQT][kPad];
@@ -64,8 +70,14 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Heavier (later) tiles first.
-  const int64_t n_tiles = (n_q + kQT - 1) / kQT;
-  const int64_t tile = n_tiles - 1 - blockIdx.x;
+  const int64_t tile_g = (int64_t)tab.qt0[tab.n] - 1 - blockIdx.x;
+  const int sq = prefix_find(tab.qt0, tab.n, tile_g);
+  const int64_t tile = tile_g - tab.qt0[sq];
+  const int64_t n_q = seq_nq(tab, sq), q_pos0 = tab.q_pos0[sq];
+  const int B = tab.B;
+  const float *idx_q = idx_q_all + tab.q_row0[sq] * d_idx;
+  const float *kmax = kmax_all + (int64_t)tab.blk0[sq] * d_idx;
+  int32_t *sel = sel_all + tab.q_row0[sq] * topk;
   const int64_t q0 = tile * kQT;
   const int nq = (int)(n_q - q0 < kQT ? n_q - q0 : kQT);
   const int km = topk - win;   // picks by score; the window win is forced
@@ -178,6 +190,10 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
     const int cnt = km > 0 ? lst_n[qi] : 0;
     const int lb = (lane < cnt) ? lst_b[qi][lane] : INT32_MAX;
     write_row(sel + (q0 + qi) * topk, topk, cnt, lb, own, window_first(own, win));
+    if (sel_g)
+      write_row(sel_g + (tab.q_row0[sq] + q0 + qi) * topk, topk, cnt,
+                lane < cnt ? lb + tab.blk0[sq] : INT32_MAX, own + tab.blk0[sq],
+                window_first(own, win) + tab.blk0[sq]);
   }
 }
 
@@ -219,30 +235,38 @@ __global__ __launch_bounds__(64) void topk_decode_merge(
 
 }  // namespace
 
+hipError_t launch_topk_tab(const float *idx_q, const SeqTab &tab, const float *kmax,
+                           int32_t d_idx, int32_t topk, int32_t win, int32_t *sel,
+                           int32_t *sel_g, hipStream_t st) {
+  const int64_t n_tiles = tab.qt0[tab.n];
+  if (n_tiles <= 0) return hipSuccess;
+  const dim3 grid((unsigned)n_tiles), wg(256);
+  const bool full = d_idx <= kDFull;
+#define MSA_TK(KM, FU)                                                                     \
+  hipLaunchKernelGGL((topk_prefill_kernel<KM, FU>), grid, wg, 0, st, idx_q, tab, kmax, d_idx, \
+                     topk, win, sel, sel_g)
+  if (topk - win <= 16) {
+    if (full)
+      MSA_TK(16, true);
+    else
+      MSA_TK(16, false);
+  } else {
+    if (full)
+      MSA_TK(64, true);
+    else
+      MSA_TK(64, false);
+  }
+#undef MSA_TK
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_prefill(const float *idx_q, int64_t n_q, int64_t q_pos0,
                                const float *kmax, int64_t nb, int32_t d_idx,
                                int32_t block, int32_t topk, int32_t win, int32_t *sel,
                                hipStream_t st) {
   (void)nb;
-  const int64_t n_tiles = (n_q + kQT - 1) / kQT;
-  const dim3 grid((unsigned)n_tiles), wg(256);
-  const bool full = d_idx <= kDFull;
-  if (topk - win <= 16) {
-    if (full)
-      hipLaunchKernelGGL((topk_prefill_kernel<16, true>), grid, wg, 0, st, idx_q, n_q,
-                         q_pos0, kmax, d_idx, block, topk, win, sel);
-    else
-      hipLaunchKernelGGL((topk_prefill_kernel<16, false>), grid, wg, 0, st, idx_q, n_q,
-                         q_pos0, kmax, d_idx, block, topk, win, sel);
-  } else {
-    if (full)
-      hipLaunchKernelGGL((topk_prefill_kernel<64, true>), grid, wg, 0, st, idx_q, n_q,
-                         q_pos0, kmax, d_idx, block, topk, win, sel);
-    else
-      hipLaunchKernelGGL((topk_prefill_kernel<64, false>), grid, wg, 0, st, idx_q, n_q,
-                         q_pos0, kmax, d_idx, block, topk, win, sel);
-  }
-  return hipGetLastError();
+  return launch_topk_tab(idx_q, seqtab_one(q_pos0, n_q, block), kmax, d_idx, topk, win, sel,
+                         nullptr, st);
 }
 
 // Layout: [chunk scores][chunk block ids].

@@ -172,3 +172,27 @@ def test_varlen_validation(lib):
     bad = list(args)
     bad[11] = 96                                   # d = 96: no kernel
     assert f(*bad, need, None) == EUNSUP
+
+
+def test_varlen_chain_grouping(lib):
+    """bf16 / d = 128 runs the sequences in chains of at most 64, each chain's
+    workspace covering all its sequences at once: one more sequence grows the
+    workspace until the 65th, which opens a second (smaller) chain; empty
+    sequences add nothing."""
+    c = lambda xs: (ctypes.c_int64 * len(xs))(*xs)
+    wsb = lib.msa_prefill_varlen_workspace_bytes
+
+    def ws(n, qn=300, kvn=1000, dtype=1, d=128):
+        cq = c([i * qn for i in range(n + 1)])
+        ckv = c([i * kvn for i in range(n + 1)])
+        return wsb(dtype, n, cq, ckv, 64, d, 128, 64, 8)
+
+    one, two, w64, w65 = ws(1), ws(2), ws(64), ws(65)
+    assert 0 < one < two < w64
+    assert w65 == w64
+    # an empty sequence between two others changes nothing
+    cq, ckv = c([0, 300, 300, 600]), c([0, 1000, 1500, 2500])
+    assert wsb(1, 3, cq, ckv, 64, 128, 128, 64, 8) == two
+    # the per-sequence path (fp32, or another head size) sizes for one sequence
+    assert ws(1, dtype=0) == ws(8, dtype=0)
+    assert ws(1, d=64) == ws(8, d=64)

@@ -23,9 +23,24 @@ def _say(msg):
     print(msg, flush=True)
 
 
+def _many_short(n, seed):
+    """n requests of a serving batch: mostly short prompts (some only a few
+    tokens), a few longer ones, a few continuing a cached prefix."""
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        kvn = int(r.choice([r.integers(1, 64), r.integers(64, 400), r.integers(400, 1200)],
+                           p=[0.3, 0.55, 0.15]))
+        qn = kvn if r.random() < 0.8 else int(r.integers(0, kvn + 1))
+        out.append((qn, kvn))
+    return out
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,d,B,K,seqs", [
     # (queries, cached tokens) per sequence; queries are each cache's last tokens
     ("bf16", 64, 8, 128, 64, 8, [(1000, 1000), (300, 2000), (0, 500), (1, 1), (700, 700)]),
+    # more sequences than one chain holds (64): two chains
+    ("bf16", 16, 2, 128, 64, 8, _many_short(70, 5)),
     ("bf16", 16, 2, 128, 128, 6, [(129, 4000), (2500, 2500)]),
     ("f32", 8, 2, 64, 64, 4, [(640, 640), (64, 900), (33, 33)]),
 ])
