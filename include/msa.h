@@ -249,10 +249,16 @@ int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
  *   sel          [cu_q[n]][K] int32 out (each sequence's own block indices)
  *   o, lse       [cu_q[n]][Hq][d], [cu_q[n]][Hq] fp32 out (lse may be NULL)
  *   ws           device scratch of msa_prefill_varlen_workspace_bytes()
- * The sequences run one after another on `stream` with the single-sequence
- * kernels (enqueued by the library; nothing is synchronised).  The workspace
- * holds one sequence's summaries, CSR and partial records at a time, so a
- * long sequence is best split by the caller into query chunks.
+ * bf16 with d = 128: the sequences run in chains of up to 64 consecutive
+ * sequences (fewer when the chain's workspace would pass 16 GiB; a single
+ * larger sequence is a chain of its own), each chain one launch sequence
+ * over all of its sequences (the blocks of all of them numbered in one CSR),
+ * so many short requests fill the GPU together.  Other types and head sizes:
+ * one sequence after another with the single-sequence kernels.  Everything is
+ * enqueued on `stream`; nothing is synchronised.  The workspace holds the
+ * largest chain's (or sequence's) summaries, CSR and partial records, so a
+ * long sequence is best split by the caller into query chunks.  Results are
+ * bit-identical to the single-sequence entry points on each sequence.
  * Supported as msa_sparse_gqa_prefill.
  * ------------------------------------------------------------------------ */
 size_t msa_prefill_varlen_workspace_bytes(int32_t dtype, int32_t n_seq, const int64_t *cu_q,
