@@ -479,42 +479,27 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lptr_t dst, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
-template <int NW>
-struct ChunkOffsets {
-  static constexpr int IPW = (kKA * kD / 8) / (64 * NW);   // instructions per wave
-  uint32_t k[IPW], v[IPW];
-  __device__ __forceinline__ void init(int nrows) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int r = ((wave * IPW + i) * 64 + lane) >> 4, sp = lane & 15;
-      const int rr = r < nrows ? r : nrows - 1;
-      k[i] = (uint32_t)(rr * kD + kswz(r, sp) * 8) * 2;
-      v[i] = (uint32_t)(rr * kD + vswz(r, sp) * 8) * 2;
-    }
-  }
-};
-
+// One chunk (nrows <= kKA keys of K and of V) into LDS: every lane copies
+// 16-byte pieces, (kKA * kD / 8) / (64 * NW) of K and as many of V.  Piece
+// (row r, segment sp) lands at the row's swizzled slot; rows past nrows
+// re-read the last row (never used: those keys are masked).  The offsets are
+// recomputed per copy (a few integer operations) rather than kept in
+// registers across the chunk loop.
 template <int NW>
 __device__ __forceinline__ void async_chunk(AsyncSmem &sm, const uint16_t *k,
-                                            const uint16_t *v, int64_t row0,
-                                            int nrows, const ChunkOffsets<NW> &full) {
-  constexpr int IPW = ChunkOffsets<NW>::IPW;
-  const int wave = threadIdx.x >> 6;
-  ChunkOffsets<NW> part;
-  const ChunkOffsets<NW> *off = &full;
-  if (nrows < kKA) {
-    part.init(nrows);
-    off = &part;
-  }
+                                            const uint16_t *v, int64_t row0, int nrows) {
+  constexpr int IPW = (kKA * kD / 8) / (64 * NW);   // copies per lane, per operand
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint32_t bytes = (uint32_t)nrows * kD * 2;
   const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(k + row0 * kD, bytes);
   const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(v + row0 * kD, bytes);
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int inst = wave * IPW + i;
-    lds_dma16(rk, (lptr_t)(&sm.Ks[inst * 64 * 8]), off->k[i]);
-    lds_dma16(rv, (lptr_t)(&sm.Vs[inst * 64 * 8]), off->v[i]);
+    const int r = (inst * 64 + lane) >> 4, sp = lane & 15;
+    const int rr = r < nrows ? r : nrows - 1;
+    lds_dma16(rk, (lptr_t)(&sm.Ks[inst * 64 * 8]), (uint32_t)(rr * kD + kswz(r, sp) * 8) * 2);
+    lds_dma16(rv, (lptr_t)(&sm.Vs[inst * 64 * 8]), (uint32_t)(rr * kD + vswz(r, sp) * 8) * 2);
   }
 }
 
@@ -626,11 +611,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   int64_t n_chunks = (nkeys + kKA - 1) / kKA;
   int64_t ci = 0;
   stage_q(g, qraw);
-  ChunkOffsets<NW> coff;
-  coff.init(kKA);
   async_chunk<NW>(sm0, k + ((int64_t)g * kv_stride) * kD,
                   v + ((int64_t)g * kv_stride) * kD, kv_row(inf),
-                  (int)(nkeys < kKA ? nkeys : kKA), coff);
+                  (int)(nkeys < kKA ? nkeys : kKA));
   // Metadata of the next item.  The one after it is fetched at the start of
   // each item's last chunk, so the load completes under that chunk's
   // compute and is only moved into place after the chunk's barrier.
@@ -698,12 +681,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
       const int64_t nxt_row = kc + kKA;
       async_chunk<NW>(nxt, k + ((int64_t)g * kv_stride) * kD,
                       v + ((int64_t)g * kv_stride) * kD, row0 + nxt_row,
-                      (int)(nkeys - nxt_row < kKA ? nkeys - nxt_row : kKA), coff);
+                      (int)(nkeys - nxt_row < kKA ? nkeys - nxt_row : kKA));
     } else if (has_next) {
       const int64_t nk = kv_keys(infn);
       async_chunk<NW>(nxt, k + ((int64_t)gn * kv_stride) * kD,
                       v + ((int64_t)gn * kv_stride) * kD, kv_row(infn),
-                      (int)(nk < kKA ? nk : kKA), coff);
+                      (int)(nk < kKA ? nk : kKA));
     }
 #pragma unroll
     for (int sub = 0; sub < kKA / 32; ++sub) {
