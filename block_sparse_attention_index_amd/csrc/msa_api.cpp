@@ -265,6 +265,29 @@ int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
                                        as_stream(stream)));
 }
 
+int msa_sparse_gqa_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
+                                 int64_t n_pages, const int32_t *block_table,
+                                 int32_t max_blocks, int64_t q_pos0, int64_t n_q, int32_t hq,
+                                 int32_t hkv, int32_t d, int32_t block, const int32_t *sel,
+                                 int32_t topk, const int32_t *row_ptr, const int32_t *q_list,
+                                 const int32_t *slot, float scale, float *o, float *lse,
+                                 void *ws, size_t ws_bytes, void *stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !sel || !row_ptr || !q_list || !slot ||
+      !o || !ws || n_pages < 1 || max_blocks < 1 || !block_ok(block) || !topk_ok(topk) ||
+      !prefill_shape_ok(q_pos0, n_q, hq, d, block, topk) || hkv < 1 || hkv > kMaxGridY ||
+      hq % hkv != 0 || !std::isfinite(scale) || !pairs_ok(n_q, topk) ||
+      cdiv(q_pos0 + n_q, block) > max_blocks || n_pages > kMaxTokens / block ||
+      !bytes_fit((__int128)n_pages * hkv * block * d * 2))
+    return MSA_ERR_INVALID_ARG;
+  if (!msa::mfma_prefill_supported(MSA_BF16, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
+  if (n_q == 0) return MSA_OK;
+  if (ws_bytes < msa::prefill_ws_bytes(MSA_BF16, q_pos0, n_q, hq, d, block, topk))
+    return MSA_ERR_WORKSPACE;
+  return status_of(msa::launch_prefill_paged(q, k_pages, v_pages, n_pages, block_table, q_pos0,
+                                             n_q, hq, hkv, d, block, sel, topk, row_ptr, q_list,
+                                             slot, scale, o, lse, ws, as_stream(stream)));
+}
+
 // ---------------------------------------------------------------------------
 // Several sequences in one call.  bf16 with d = 128 (the matrix-core path):
 // the sequences go in chains of at most 64 (and at most kChainBytes of
@@ -456,7 +479,8 @@ int msa_prefill_varlen(const void *q, const void *k, const void *v, const float 
                                               inv_ws, st);
                      if (e == hipSuccess)
                        e = msa::launch_prefill_chain(
-                           static_cast<const char *>(q) + r0 * hq * d * es, k, v, total_kv, t,
+                           static_cast<const char *>(q) + r0 * hq * d * es, k, v,
+                           msa::KvMap{nullptr, 0, total_kv, 0, hkv}, t,
                            hq, hkv, d, sel_c, topk, row_ptr, q_list, slot, scale,
                            o + r0 * hq * d, lse ? lse + r0 * hq : nullptr, attn_ws, st);
                    });

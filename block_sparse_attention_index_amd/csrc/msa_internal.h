@@ -70,11 +70,20 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v,
 // blocks.
 size_t prefill_chain_ws_bytes(const SeqTab &tab, int32_t hq, int32_t d, int32_t topk);
 hipError_t launch_prefill_chain(const void *q, const void *k, const void *v,
-                                int64_t kv_stride, const SeqTab &tab, int32_t hq,
+                                const KvMap &kvm, const SeqTab &tab, int32_t hq,
                                 int32_t hkv, int32_t d, const int32_t *sel, int32_t topk,
                                 const int32_t *row_ptr, const int32_t *q_list,
                                 const int32_t *slot, float scale, float *o, float *lse,
                                 void *ws, hipStream_t st);
+
+// The matrix-core sparse prefill of one sequence over a paged bf16 cache
+// (block b in page block_table[b]; pages [n_pages][Hkv][B][d]).
+hipError_t launch_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
+                                int64_t n_pages, const int32_t *block_table, int64_t q_pos0,
+                                int64_t n_q, int32_t hq, int32_t hkv, int32_t d, int32_t block,
+                                const int32_t *sel, int32_t topk, const int32_t *row_ptr,
+                                const int32_t *q_list, const int32_t *slot, float scale,
+                                float *o, float *lse, void *ws, hipStream_t st);
 
 size_t decode_ws_bytes(int32_t n_seq, int32_t hq, int32_t d, int32_t block,
                        int32_t topk);

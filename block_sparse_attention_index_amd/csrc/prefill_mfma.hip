@@ -142,7 +142,7 @@ __device__ __forceinline__ void put_partial(uint16_t *part_o, float2 *part_le,
 template <int G, int NB, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, int64_t kv_stride, SeqTab tab, int hq,
+    const uint16_t *__restrict__ v, KvMap kvm, SeqTab tab, int hq,
     const int32_t *__restrict__ sel, int topk, const int32_t *__restrict__ slot,
     float scale_log2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_le,
     int64_t n_part, float *__restrict__ o, float *__restrict__ lse) {
@@ -206,18 +206,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     lsum[nbk] = 0.f;
   }
 
-  const uint16_t *kb = k + ((int64_t)g * kv_stride + tab.kv_row0[sq]) * kD;
-  const uint16_t *vb = v + ((int64_t)g * kv_stride + tab.kv_row0[sq]) * kD;
+  // the own block's keys and values (rows 0 .. nkeys-1 from these)
+  const int64_t kvo = kv_block_off<kD>(kvm, tab, sq, b, g);
+  const uint16_t *kb = k + kvo;
+  const uint16_t *vb = v + kvo;
   const int64_t n_chunks = (nkeys + kKC - 1) / kKC;
   ChunkRegs<NT> cr;
-  load_chunk(cr, kb, vb, b * B, (int)(nkeys < kKC ? nkeys : kKC));
+  load_chunk(cr, kb, vb, 0, (int)(nkeys < kKC ? nkeys : kKC));
   store_chunk(smb[0], cr);
   __syncthreads();
   for (int64_t ci = 0; ci < n_chunks; ++ci) {
     const int64_t kc = ci * kKC;
     if (ci + 1 < n_chunks) {
       const int64_t nxt = kc + kKC;
-      load_chunk(cr, kb, vb, b * B + nxt,
+      load_chunk(cr, kb, vb, nxt,
                  (int)(nkeys - nxt < kKC ? nkeys - nxt : kKC));
     }
     MfmaSmem &sm = smb[ci & 1];
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(256) void prefill_tile_info(
 template <int G, int NW>
 __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, int64_t kv_stride, SeqTab tab, int hq, int hkv,
+    const uint16_t *__restrict__ v, KvMap kvm, SeqTab tab, int hq, int hkv,
     const int32_t *__restrict__ tile_ptr, const int4 *__restrict__ info,
     const int32_t *__restrict__ tq,
     float scale_log2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_le,
@@ -591,15 +593,17 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
       dst[cc] = as_bf16x8(x);
     }
   };
-  // first K/V row of an item's block (info: global block, ..., sequence) and
-  // its key count (B: a non-own block is always full)
-  auto kv_row = [&](const int4 &f) {
-    return tab.kv_row0[f.w] + (int64_t)(f.x - tab.blk0[f.w]) * B;
+  // element offset of an item's block (info: global block, ..., sequence) in
+  // KV head gg, and its key count (B: a non-own block is always full)
+  auto kv_off = [&](const int4 &f, int gg) {
+    return kv_block_off<kD>(kvm, tab, f.w, f.x - tab.blk0[f.w], gg);
   };
   auto kv_keys = [&](const int4 &f) {
     int64_t n = B;
-    const int64_t r0 = kv_row(f);
-    if (r0 + n > kv_stride) n = kv_stride - r0;   // invalid input only
+    if (!kvm.pages) {   // contiguous rows: never past the cache (invalid input only)
+      const int64_t r0 = tab.kv_row0[f.w] + (int64_t)(f.x - tab.blk0[f.w]) * B;
+      if (r0 + n > kvm.kv_stride) n = kvm.kv_stride - r0;
+    }
     return n;
   };
 
@@ -611,9 +615,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   int64_t n_chunks = (nkeys + kKA - 1) / kKA;
   int64_t ci = 0;
   stage_q(g, qraw);
-  async_chunk<NW>(sm0, k + ((int64_t)g * kv_stride) * kD,
-                  v + ((int64_t)g * kv_stride) * kD, kv_row(inf),
-                  (int)(nkeys < kKA ? nkeys : kKA));
+  int64_t kvo = kv_off(inf, g);
+  async_chunk<NW>(sm0, k + kvo, v + kvo, 0, (int)(nkeys < kKA ? nkeys : kKA));
   // Metadata of the next item.  The one after it is fetched at the start of
   // each item's last chunk, so the load completes under that chunk's
   // compute and is only moved into place after the chunk's barrier.
@@ -667,7 +670,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     constexpr int P = decltype(tag)::value;
     AsyncSmem &cur = P ? sm1 : sm0;
     AsyncSmem &nxt = P ? sm0 : sm1;
-    const int64_t row0 = kv_row(inf);
     const int64_t kc = ci * kKA;
     const bool last = ci + 1 >= n_chunks;
     int gnn = 0;
@@ -679,14 +681,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     }
     if (!last) {
       const int64_t nxt_row = kc + kKA;
-      async_chunk<NW>(nxt, k + ((int64_t)g * kv_stride) * kD,
-                      v + ((int64_t)g * kv_stride) * kD, row0 + nxt_row,
+      async_chunk<NW>(nxt, k + kvo, v + kvo, nxt_row,
                       (int)(nkeys - nxt_row < kKA ? nkeys - nxt_row : kKA));
     } else if (has_next) {
       const int64_t nk = kv_keys(infn);
-      async_chunk<NW>(nxt, k + ((int64_t)gn * kv_stride) * kD,
-                      v + ((int64_t)gn * kv_stride) * kD, kv_row(infn),
-                      (int)(nk < kKA ? nk : kKA));
+      const int64_t kvn = kv_off(infn, gn);
+      async_chunk<NW>(nxt, k + kvn, v + kvn, 0, (int)(nk < kKA ? nk : kKA));
     }
 #pragma unroll
     for (int sub = 0; sub < kKA / 32; ++sub) {
@@ -786,6 +786,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     infn = infnn;
     qrawn = qrawnn;
     nkeys = kv_keys(inf);
+    kvo = kv_off(inf, g);
     n_chunks = (nkeys + kKA - 1) / kKA;
     ci = 0;
     read_q(qraw, qf);
@@ -819,7 +820,7 @@ int num_cus() {
 
 template <int G, int NB, int NW>
 hipError_t launch_mfma_g(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         int64_t kv_stride, const SeqTab &tab, int hq, int hkv,
+                         const KvMap &kvm, const SeqTab &tab, int hq, int hkv,
                          const int32_t *sel, int topk, const int32_t *row_ptr,
                          const int32_t *q_list, const int32_t *slot, float scale, float *o,
                          float *lse, int32_t *tile_ptr, int4 *info, int32_t *tq,
@@ -835,7 +836,7 @@ hipError_t launch_mfma_g(const uint16_t *q, const uint16_t *k, const uint16_t *v
                        row_ptr, tile_ptr, q_list, tab, info, tq);
     const int grid = 8 * ((num_cus() + 7) / 8);
     hipLaunchKernelGGL((prefill_nonown_persistent<G, NW>), dim3(grid), dim3(64 * NW),
-                       0, st, q, k, v, kv_stride, tab, hq, hkv, tile_ptr, info, tq, sl2,
+                       0, st, q, k, v, kvm, tab, hq, hkv, tile_ptr, info, tq, sl2,
                        part_o, part_le, n_part);
   }
   // own-block pass: 4-wave workgroups (see prefill_mfma_kernel), one per
@@ -845,7 +846,7 @@ hipError_t launch_mfma_g(const uint16_t *q, const uint16_t *k, const uint16_t *v
   const int64_t tiles = (int64_t)tab.ob0[tab.n] * ((tab.B + TPTB - 1) / TPTB);
   if (tiles > 0)
     hipLaunchKernelGGL((prefill_mfma_kernel<G, NB, NWB>), dim3((unsigned)tiles, hkv),
-                       dim3(64 * NWB), 0, st, q, k, v, kv_stride, tab, hq, sel, topk, slot,
+                       dim3(64 * NWB), 0, st, q, k, v, kvm, tab, hq, sel, topk, slot,
                        sl2, part_o, part_le, n_part, o, lse);
   return hipGetLastError();
 }
@@ -892,7 +893,7 @@ size_t prefill_chain_ws_bytes(const SeqTab &tab, int32_t hq, int32_t d, int32_t 
 }
 
 hipError_t launch_prefill_chain(const void *q, const void *k, const void *v,
-                                int64_t kv_stride, const SeqTab &tab, int32_t hq,
+                                const KvMap &kvm, const SeqTab &tab, int32_t hq,
                                 int32_t hkv, int32_t d, const int32_t *sel, int32_t topk,
                                 const int32_t *row_ptr, const int32_t *q_list,
                                 const int32_t *slot, float scale, float *o, float *lse,
@@ -910,7 +911,7 @@ hipError_t launch_prefill_chain(const void *q, const void *k, const void *v,
   const uint16_t *vv = static_cast<const uint16_t *>(v);
 #define MSA_MF(GG)                                                                \
   case GG:                                                                        \
-    return launch_mfma_g<GG, 1, 8>(qq, kk, vv, kv_stride, tab, hq, hkv, sel, topk,  \
+    return launch_mfma_g<GG, 1, 8>(qq, kk, vv, kvm, tab, hq, hkv, sel, topk,        \
                                    row_ptr, q_list, slot, scale, o, lse, tile_ptr,  \
                                    info, tq, part_o, part_le, L.np, L.max_tiles, st);
   switch (G) {
@@ -933,8 +934,20 @@ hipError_t launch_prefill_mfma(const void *q, const void *k, const void *v,
                                const int32_t *row_ptr, const int32_t *q_list,
                                const int32_t *slot, float scale, float *o,
                                float *lse, void *ws, hipStream_t st) {
-  return launch_prefill_chain(q, k, v, kv_stride, seqtab_one(q_pos0, n_q, block), hq, hkv, d,
-                              sel, topk, row_ptr, q_list, slot, scale, o, lse, ws, st);
+  const KvMap kvm{nullptr, 0, kv_stride, 0, hkv};
+  return launch_prefill_chain(q, k, v, kvm, seqtab_one(q_pos0, n_q, block), hq, hkv, d, sel,
+                              topk, row_ptr, q_list, slot, scale, o, lse, ws, st);
+}
+
+hipError_t launch_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
+                                int64_t n_pages, const int32_t *block_table, int64_t q_pos0,
+                                int64_t n_q, int32_t hq, int32_t hkv, int32_t d, int32_t block,
+                                const int32_t *sel, int32_t topk, const int32_t *row_ptr,
+                                const int32_t *q_list, const int32_t *slot, float scale,
+                                float *o, float *lse, void *ws, hipStream_t st) {
+  const KvMap kvm{block_table, n_pages, 0, 0, hkv};
+  return launch_prefill_chain(q, k_pages, v_pages, kvm, seqtab_one(q_pos0, n_q, block), hq, hkv,
+                              d, sel, topk, row_ptr, q_list, slot, scale, o, lse, ws, st);
 }
 
 }  // namespace msa

@@ -63,6 +63,33 @@ __host__ __device__ __forceinline__ int64_t own_through_g(const SeqTab &t, int s
   return t.q_row0[s] + (x - p0);
 }
 
+// Where a chain's keys and values live.  Contiguous (pages == null): the
+// [Hkv][kv_stride][d] caches, sequence s from row kv_row0[s].  Paged: the
+// [n_pages][Hkv][B][d] pools, local block b of sequence s in page
+// pages[s * pt_stride + b]; an entry outside [0, n_pages) is clamped into
+// the pool (nothing outside it is read; the outputs of queries that use such
+// a block are then unspecified).
+struct KvMap {
+  const int32_t *pages;
+  int64_t n_pages;
+  int64_t kv_stride;
+  int32_t pt_stride;
+  int32_t hkv;
+};
+
+// Element offset (head size D) of key 0 of local block b of sequence s in
+// KV head g; the block's keys follow row by row.
+template <int D>
+__host__ __device__ __forceinline__ int64_t kv_block_off(const KvMap &m, const SeqTab &t, int s,
+                                                         int64_t b, int g) {
+  if (m.pages) {
+    int64_t pg = m.pages[(int64_t)s * m.pt_stride + b];
+    pg = pg < 0 ? 0 : (pg >= m.n_pages ? m.n_pages - 1 : pg);
+    return ((pg * m.hkv + g) * t.B) * D;
+  }
+  return ((int64_t)g * m.kv_stride + t.kv_row0[s] + b * t.B) * D;
+}
+
 // The table of one sequence: queries at positions q_pos0 .. q_pos0 + n_q - 1,
 // K/V rows from 0, blocks 0 .. ceil((q_pos0 + n_q) / B) - 1.
 inline SeqTab seqtab_one(int64_t q_pos0, int64_t n_q, int32_t block) {

@@ -33,6 +33,7 @@ ENTRY_POINTS = (
     "msa_index_pool_mean", "msa_index_topk_window", "msa_index_topk_decode_window",
     "msa_sparse_gqa_decode_paged", "msa_prefill_varlen_workspace_bytes",
     "msa_prefill_varlen", "msa_decode_step_noalloc_max_bytes", "msa_decode_step_noalloc",
+    "msa_sparse_gqa_prefill_paged",
 )
 
 
@@ -75,6 +76,8 @@ def load():
         "msa_sparse_gqa_prefill": ([P, P, P, i32, i64, i64, i64, i32, i32, i32, i32,
                                     P, i32, P, P, P, f32, P, P, P, sz, P],
                                    ctypes.c_int),
+        "msa_sparse_gqa_prefill_paged": ([P, P, P, i64, P, i32, i64, i64, i32, i32, i32, i32,
+                                          P, i32, P, P, P, f32, P, P, P, sz, P], ctypes.c_int),
         "msa_decode_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
         "msa_sparse_gqa_decode": ([P, P, P, i32, i32, i64, P, i32, i32, i32, i32, P,
                                    i32, f32, P, P, P, sz, P], ctypes.c_int),
@@ -335,6 +338,37 @@ def msa_sparse_gqa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         d, block, _ptr(sel), topk, _ptr(row_ptr), _ptr(q_list), _ptr(slot), scale,
         _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(q))
     _check("msa_sparse_gqa_prefill", st)
+    return o, lse
+
+
+def msa_sparse_gqa_prefill_paged(q, k_pages, v_pages, block_table, sel, row_ptr, q_list, slot,
+                                 block: int, scale: float | None = None, q_pos0: int = 0,
+                                 o=None, lse=None, ws=None, want_lse: bool = True):
+    """Sparse GQA prefill of a query chunk against a paged bf16 cache.
+    ``q`` [n_q, Hq, d] bf16; ``k_pages``/``v_pages`` [n_pages, Hkv, B, d]
+    bf16; ``block_table`` [max_blocks] int32.  Returns ``(o, lse)`` as
+    msa_sparse_gqa_prefill."""
+    for t, nm in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _dev(t, nm, torch.bfloat16)
+    for t, nm in ((block_table, "block_table"), (sel, "sel"), (row_ptr, "row_ptr"),
+                  (q_list, "q_list"), (slot, "slot")):
+        _dev(t, nm, torch.int32)
+    n_q, hq, d = q.shape
+    n_pages, hkv = k_pages.shape[0], k_pages.shape[1]
+    topk = sel.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load()
+    ws = _ws(lib.msa_prefill_workspace_bytes(MSA_BF16, q_pos0, n_q, hq, d, block, topk), q, ws)
+    if o is None:
+        o = torch.empty((n_q, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, hq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.float32)
+    st = lib.msa_sparse_gqa_prefill_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), n_pages, _ptr(block_table), block_table.numel(),
+        q_pos0, n_q, hq, hkv, d, block, _ptr(sel), topk, _ptr(row_ptr), _ptr(q_list),
+        _ptr(slot), scale, _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(q))
+    _check("msa_sparse_gqa_prefill_paged", st)
     return o, lse
 
 

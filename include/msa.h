@@ -234,6 +234,34 @@ int msa_sparse_gqa_prefill(const void *q, const void *k, const void *v,
                            void *stream);
 
 /* --------------------------------------------------------------------------
+ * msa_sparse_gqa_prefill_paged -- msa_sparse_gqa_prefill for a chunk of
+ * queries against a paged bf16 KV cache ([CXT] section 3.3: prefill of a
+ * request's next chunk against the cache already built, the cache kept in
+ * block-granular pages, section 3.2).  Same page layout as
+ * msa_sparse_gqa_decode_paged: a page holds one MSA block of every KV head,
+ *
+ *   k_pages, v_pages  [n_pages][Hkv][B][d] bf16
+ *   block_table       [max_blocks] int32: block b of the sequence (keys
+ *                     b*B .. b*B+B-1) lives in page block_table[b];
+ *                     ceil((q_pos0 + n_q) / B) <= max_blocks
+ *   q, sel, row_ptr, q_list, slot, o, lse, scale, ws as msa_sparse_gqa_prefill
+ *                     (ws: msa_prefill_workspace_bytes with dtype MSA_BF16)
+ * Only the table entries of blocks the selection uses are read.  An entry
+ * outside [0, n_pages) is clamped into the pool (nothing outside it is
+ * read); the outputs of the queries that use such a block are unspecified.
+ * Results are bit-identical to msa_sparse_gqa_prefill on the same keys and
+ * values laid out contiguously.
+ * Supported: bf16, d = 128, Hq/Hkv in {1, 2, 4, 8, 16}.
+ * ------------------------------------------------------------------------ */
+int msa_sparse_gqa_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
+                                 int64_t n_pages, const int32_t *block_table,
+                                 int32_t max_blocks, int64_t q_pos0, int64_t n_q, int32_t hq,
+                                 int32_t hkv, int32_t d, int32_t block, const int32_t *sel,
+                                 int32_t topk, const int32_t *row_ptr, const int32_t *q_list,
+                                 const int32_t *slot, float scale, float *o, float *lse,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
  * msa_prefill_varlen -- the whole prefill path (pool, top-K, CSR, sparse
  * GQA with merge) for several sequences in one call, each a chunk of queries
  * against its own cache ([CXT] section 3.3: prefill over a batch of

@@ -196,3 +196,25 @@ def test_varlen_chain_grouping(lib):
     # the per-sequence path (fp32, or another head size) sizes for one sequence
     assert ws(1, dtype=0) == ws(8, dtype=0)
     assert ws(1, d=64) == ws(8, d=64)
+
+
+def test_paged_prefill_validation(lib):
+    P = FAKE
+    f = lib.msa_sparse_gqa_prefill_paged
+    args = lambda **kw: dict(dict(q=P, kp=P, vp=P, npg=100, bt=P, mb=64, q0=0, nq=4096, hq=64,
+                                  hkv=8, d=128, B=64, sel=P, K=16, rp=P, ql=P, sl=P, sc=0.1,
+                                  o=P, lse=None, ws=P, wsb=1 << 40, st=None), **kw)
+    call = lambda a: f(a["q"], a["kp"], a["vp"], a["npg"], a["bt"], a["mb"], a["q0"], a["nq"],
+                       a["hq"], a["hkv"], a["d"], a["B"], a["sel"], a["K"], a["rp"], a["ql"],
+                       a["sl"], a["sc"], a["o"], a["lse"], a["ws"], a["wsb"], a["st"])
+    assert call(args(bt=None)) == EINVAL
+    assert call(args(npg=0)) == EINVAL
+    assert call(args(mb=63)) == EINVAL                    # table shorter than the blocks used
+    assert call(args(q0=10)) == EINVAL                    # 65 blocks > 64 table entries
+    assert call(args(hq=60)) == EINVAL
+    assert call(args(sc=float("nan"))) == EINVAL
+    assert call(args(d=64)) == EUNSUP                     # bf16 matrix-core path only
+    assert call(args(hq=24, hkv=8)) == EUNSUP
+    need = lib.msa_prefill_workspace_bytes(1, 0, 4096, 64, 128, 64, 16)
+    assert call(args(wsb=need - 1)) == EWS
+    assert call(args(nq=0)) == 0                          # nothing to do
