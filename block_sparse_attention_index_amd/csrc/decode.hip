@@ -266,8 +266,9 @@ __device__ __forceinline__ int dvswz(int r, int sg) { return sg ^ (2 * (r & 7));
 
 struct DecUnit {
   int s, g;
-  int64_t t0;   // first key of the unit
-  int nk;       // keys in the unit (0: empty)
+  int64_t t0;    // first key of the unit
+  int64_t kvo;   // element offset of that key's K (and V) row
+  int nk;        // keys in the unit (0: empty)
 };
 
 // FUSED: the step of msa_decode_step -- the query sits at position
@@ -373,8 +374,8 @@ __device__ __forceinline__ void combine_run(uint32_t sg, uint32_t ups_g, uint32_
 template <int G, bool FUSED>
 __global__ __launch_bounds__(256) void decode_stream(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vc, int64_t len_max,
-    const int64_t *__restrict__ seq_len, int hq, int hkv, int B,
+    const uint16_t *__restrict__ vc, int64_t len_max, const int32_t *__restrict__ ptab,
+    int pt_stride, int64_t n_pages, const int64_t *__restrict__ seq_len, int hq, int hkv, int B,
     int32_t *__restrict__ sel, int topk, int nseg, int seg_len,
     uint32_t u_q, uint32_t u_r, float scale_log2, float *__restrict__ part_o,
     float *__restrict__ part_lse, const float *__restrict__ cand_s,
@@ -400,6 +401,17 @@ __global__ __launch_bounds__(256) void decode_stream(
   auto query_len = [&](uint32_t s) __attribute__((always_inline)) {
     int64_t len = seq_len[s] + (FUSED ? 1 : 0);
     return len > len_max ? len_max : len;
+  };
+  // element offset of key b * B + off of sequence s, KV head g: contiguous
+  // [n_seq][Hkv][len_max][d] caches, or (ptab) the page of block b in
+  // [n_pages][Hkv][B][d] pools; -1 when the block has no page
+  auto kv_offset = [&](int s, int g, int64_t b, int64_t off) __attribute__((always_inline)) {
+    if (ptab) {
+      const int32_t pg = b < pt_stride ? ptab[(int64_t)s * pt_stride + b] : -1;
+      if (pg < 0 || pg >= n_pages) return (int64_t)-1;
+      return (((int64_t)pg * hkv + g) * B + off) * D;
+    }
+    return (((int64_t)s * hkv + g) * len_max + b * B + off) * D;
   };
 
   // Unit u of (sequence, KV head) sg = u / (topk * nseg): segment-major, and
@@ -430,7 +442,8 @@ __global__ __launch_bounds__(256) void decode_stream(
     int64_t n = (b < 0 || len < 1) ? 0 : len - d.t0;   // keys t0 .. len-1
     if (n > seg_len) n = seg_len;
     if (n > (int64_t)B - (int64_t)seg * seg_len) n = (int64_t)B - (int64_t)seg * seg_len;
-    d.nk = n > 0 ? (int)n : 0;
+    d.kvo = n > 0 ? kv_offset(d.s, d.g, b, (int64_t)seg * seg_len) : -1;
+    d.nk = n > 0 && d.kvo >= 0 ? (int)n : 0;
     return d;
   };
   // first non-empty unit at or after u (empty ones get their neutral
@@ -487,10 +500,11 @@ __global__ __launch_bounds__(256) void decode_stream(
     arrive(sg);
   };
   uint32_t sg_next = u_begin / ups_g;   // runs before this one are written
+  // rows row0 .. row0 + nrows - 1 of the unit (from its first key)
   auto dma_kv = [&](StreamBuf &buf, const DecUnit &d, int64_t row0, int nrows)
       __attribute__((always_inline)) {
-    const uint16_t *kb = kc + (((int64_t)d.s * hkv + d.g) * len_max + row0) * D;
-    const uint16_t *vb = vc + (((int64_t)d.s * hkv + d.g) * len_max + row0) * D;
+    const uint16_t *kb = kc + d.kvo + row0 * D;
+    const uint16_t *vb = vc + d.kvo + row0 * D;
     constexpr int IPW = (kSK * D / 8) / 256;   // instructions per wave per tensor
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
@@ -536,10 +550,11 @@ __global__ __launch_bounds__(256) void decode_stream(
         int64_t n0 = len0 - d0.t0;
         if (n0 > seg_len) n0 = seg_len;
         if (n0 > (int64_t)B - (int64_t)seg0 * seg_len) n0 = (int64_t)B - (int64_t)seg0 * seg_len;
-        if (n0 > 0) {
+        d0.kvo = n0 > 0 ? kv_offset(d0.s, d0.g, own0, (int64_t)seg0 * seg_len) : -1;
+        if (n0 > 0 && d0.kvo >= 0) {
           d0.nk = (int)n0;
           dma_q(d0);
-          dma_kv(sb0, d0, d0.t0, kv_rows(d0.nk));
+          dma_kv(sb0, d0, 0, kv_rows(d0.nk));
           pre = true;
         }
       }
@@ -582,7 +597,7 @@ __global__ __launch_bounds__(256) void decode_stream(
   uint32_t un = next_unit(u + 1, nu);
   if (!(pre && u == u_begin)) {   // else the same unit's chunk is already on its way
     dma_q(cu);
-    dma_kv(sb0, cu, cu.t0, kv_rows(cu.nk));
+    dma_kv(sb0, cu, 0, kv_rows(cu.nk));
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -616,13 +631,13 @@ __global__ __launch_bounds__(256) void decode_stream(
     const int nk_c = kv_rows(cu.nk - kc0);
     const bool last = kc0 + kSK >= cu.nk;
     if (!last) {
-      dma_kv(nxt, cu, cu.t0 + kc0 + kSK, kv_rows(cu.nk - kc0 - kSK));
+      dma_kv(nxt, cu, kc0 + kSK, kv_rows(cu.nk - kc0 - kSK));
     } else if (un < u_end) {
       // a one-chunk unit read its queries just now: every wave must be done
       // with the staging area before the next unit's copy lands there
       if (ci == 0) __syncthreads();
       dma_q(nu);
-      dma_kv(nxt, nu, nu.t0, kv_rows(nu.nk));
+      dma_kv(nxt, nu, 0, kv_rows(nu.nk));
     }
     const int k0 = wave * 32;
     if (k0 < nk_c) {
@@ -1561,11 +1576,17 @@ __global__ __launch_bounds__(256) void dstep_scan(
     T *__restrict__ v_cache, float *__restrict__ idx_k_cache,
     float *__restrict__ kmax, const float *__restrict__ idx_q,
     const int64_t *__restrict__ seq_len, int64_t len_max, int64_t nb_max,
+    const int32_t *__restrict__ ptab, int pt_stride, int64_t n_pages,
     int hkv, int d, int d_idx, int B, int topk, float *__restrict__ cand_s,
     int *__restrict__ cand_b, int n_chunks, int *__restrict__ run_cnt) {
   const int s = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
   const int64_t L = seq_len[s];
-  const bool room = L >= 0 && L < len_max && L / B < nb_max;   // else: nothing is written
+  // paged caches: the new token's row lives in the page of its block
+  int64_t pg = 0;
+  if (ptab && L >= 0 && L / B < pt_stride) pg = ptab[(int64_t)s * pt_stride + L / B];
+  const bool room = L >= 0 && L < len_max && L / B < nb_max &&
+                    (!ptab || (L / B < pt_stride && pg >= 0 && pg < n_pages));
+  // (else: nothing is written)
   const int64_t own = room ? L / B : nb_max - 1;
   if (ch == n_chunks) {
     // the attention kernel's arrival counters of this sequence start at zero
@@ -1577,7 +1598,8 @@ __global__ __launch_bounds__(256) void dstep_scan(
     for (int x = tid; x < hkv * vpr; x += 256) {
       const int g = x / vpr, c = (x % vpr) * kV;
       const int64_t src = ((int64_t)s * hkv + g) * d + c;
-      const int64_t dst = (((int64_t)s * hkv + g) * len_max + L) * d + c;
+      const int64_t dst = ptab ? ((pg * hkv + g) * B + L % B) * d + c
+                               : (((int64_t)s * hkv + g) * len_max + L) * d + c;
       const uint4 kx = *reinterpret_cast<const uint4 *>(k_new + src);
       const uint4 vx = *reinterpret_cast<const uint4 *>(v_new + src);
       *reinterpret_cast<uint4 *>(k_cache + dst) = kx;
@@ -1652,7 +1674,8 @@ hipError_t launch_dec(const T *q, const T *kc, const T *vc, int32_t n_seq,
   if constexpr (sizeof(T) == 2 && D == 128) {
     const StreamPlan pl = stream_plan(n_seq, hkv, B, topk);
     hipLaunchKernelGGL((decode_stream<G, false>), dim3(pl.grid), dim3(256), 0, st, q, kc, vc,
-                       len_max, seq_len, hq, hkv, B, const_cast<int32_t *>(sel), topk, pl.nseg,
+                       len_max, nullptr, 0, (int64_t)0, seq_len, hq, hkv, B,
+                       const_cast<int32_t *>(sel), topk, pl.nseg,
                        pl.seg_len, pl.u_q, pl.u_r, scale * kLog2e, part_o, part_lse, nullptr,
                        nullptr, 0, (int64_t)0, nullptr, nullptr, nullptr);
     hipLaunchKernelGGL((decode_merge_runs<D>), dim3(hq, n_seq), dim3(D), 0, st, G, hkv,
@@ -1851,7 +1874,8 @@ bool decode_step_supported(int32_t dtype, int32_t d, int32_t group) {
 
 hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_new,
                               const float *idx_q, const float *idx_k_new, void *k_cache,
-                              void *v_cache, float *idx_k_cache, float *kmax,
+                              void *v_cache, const int32_t *ptab, int32_t pt_stride,
+                              int64_t n_pages, float *idx_k_cache, float *kmax,
                               int32_t n_seq, int64_t len_max, int64_t nb_max,
                               const int64_t *seq_len, int32_t hq, int32_t hkv, int32_t d,
                               int32_t d_idx, int32_t block, int32_t topk, float scale,
@@ -1878,12 +1902,14 @@ hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_ne
   hipLaunchKernelGGL((dstep_scan<uint16_t>), dim3(n_chunks + 1, n_seq), dim3(256), 0, st,
                      static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
                      idx_k_new, kc, vc, idx_k_cache, kmax, idx_q, seq_len, len_max, nb_max,
-                     hkv, d, d_idx, block, topk, cand_s, cand_b, n_chunks, run_cnt);
+                     ptab, pt_stride, n_pages, hkv, d, d_idx, block, topk, cand_s, cand_b,
+                     n_chunks, run_cnt);
   const StreamPlan pl = stream_plan(n_seq, hkv, block, topk);
 #define MSA_STEP_CASE(GG)                                                               \
   case GG:                                                                              \
     hipLaunchKernelGGL((decode_stream<GG, true>), dim3(pl.grid), dim3(256), 0, st, qq, kc, \
-                       vc, len_max, seq_len, hq, hkv, block, sel, topk, pl.nseg,         \
+                       vc, len_max, ptab, pt_stride, n_pages, seq_len, hq, hkv, block, sel, \
+                       topk, pl.nseg,                                                    \
                        pl.seg_len, pl.u_q, pl.u_r, scale * kLog2e, part_o, part_lse, cand_s, \
                        cand_b, n_chunks, nb_max, run_cnt, o, lse);                       \
     break;

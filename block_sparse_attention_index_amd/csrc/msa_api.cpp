@@ -595,9 +595,37 @@ int msa_decode_step(const void *q, const void *k_new, const void *v_new,
   if (ws_bytes < msa::decode_step_ws_bytes(n_seq, nb_max, hq, d, block, topk))
     return MSA_ERR_WORKSPACE;
   return status_of(msa::launch_decode_step(q, k_new, v_new, idx_q, idx_k_new, k_cache,
-                                           v_cache, idx_k_cache, kmax, n_seq, len_max,
+                                           v_cache, nullptr, 0, 0, idx_k_cache, kmax, n_seq,
+                                           len_max,
                                            nb_max, seq_len, hq, hkv, d, d_idx, block, topk,
                                            scale, sel, o, lse, ws, as_stream(stream)));
+}
+
+int msa_decode_step_paged(const void *q, const void *k_new, const void *v_new,
+                          const float *idx_q, const float *idx_k_new, void *k_pages,
+                          void *v_pages, int64_t n_pages, const int32_t *block_table,
+                          int32_t max_blocks, float *idx_k_cache, float *kmax, int32_t n_seq,
+                          int64_t len_max, int64_t nb_max, const int64_t *seq_len, int32_t hq,
+                          int32_t hkv, int32_t d, int32_t d_idx, int32_t block, int32_t topk,
+                          float scale, int32_t *sel, float *o, float *lse, void *ws,
+                          size_t ws_bytes, void *stream) {
+  if (!q || !k_new || !v_new || !idx_q || !idx_k_new || !k_pages || !v_pages ||
+      !block_table || !kmax || !seq_len || !sel || !o || !ws || n_pages < 1 ||
+      max_blocks < 1 || n_seq < 1 || n_seq > kMaxGridY || len_max < 1 || nb_max < 1 ||
+      nb_max > INT32_MAX || hq < 1 || hkv < 1 || hq % hkv != 0 || d < 1 ||
+      !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk) || !std::isfinite(scale) ||
+      (int64_t)n_seq * hkv * topk > kMaxDecodeItems ||
+      (int64_t)n_pages * hkv * block > (int64_t(1) << 40) ||
+      !decode_shape_ok(n_seq, nb_max, hq, d, block, topk))
+    return MSA_ERR_INVALID_ARG;
+  if (!msa::decode_step_supported(MSA_BF16, d, hq / hkv)) return MSA_ERR_UNSUPPORTED;
+  if (ws_bytes < msa::decode_step_ws_bytes(n_seq, nb_max, hq, d, block, topk))
+    return MSA_ERR_WORKSPACE;
+  return status_of(msa::launch_decode_step(q, k_new, v_new, idx_q, idx_k_new, k_pages, v_pages,
+                                           block_table, max_blocks, n_pages, idx_k_cache,
+                                           kmax, n_seq, len_max, nb_max, seq_len, hq, hkv, d,
+                                           d_idx, block, topk, scale, sel, o, lse, ws,
+                                           as_stream(stream)));
 }
 
 size_t msa_decode_step_noalloc_max_bytes(void) { return msa::noalloc_scratch_bytes(); }
@@ -624,7 +652,8 @@ int msa_decode_step_noalloc(const void *q, const void *k_new, const void *v_new,
   void *ws = nullptr;
   if (msa::noalloc_scratch(&ws) != hipSuccess) return MSA_ERR_HIP;
   return status_of(msa::launch_decode_step(q, k_new, v_new, idx_q, idx_k_new, k_cache,
-                                           v_cache, idx_k_cache, kmax, n_seq, len_max,
+                                           v_cache, nullptr, 0, 0, idx_k_cache, kmax, n_seq,
+                                           len_max,
                                            nb_max, seq_len, hq, hkv, d, d_idx, block, topk,
                                            scale, sel, o, lse, ws, as_stream(stream)));
 }

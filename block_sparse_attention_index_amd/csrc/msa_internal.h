@@ -107,9 +107,12 @@ hipError_t launch_decode_paged(const void *q, const void *k_pages, const void *v
 size_t decode_step_ws_bytes(int32_t n_seq, int64_t nb_max, int32_t hq, int32_t d,
                             int32_t block, int32_t topk);
 bool decode_step_supported(int32_t dtype, int32_t d, int32_t group);
+// ptab: null for contiguous [n_seq][Hkv][len_max][d] caches, else the
+// [n_seq][pt_stride] block table of [n_pages][Hkv][B][d] page pools.
 hipError_t launch_decode_step(const void *q, const void *k_new, const void *v_new,
                               const float *idx_q, const float *idx_k_new, void *k_cache,
-                              void *v_cache, float *idx_k_cache, float *kmax,
+                              void *v_cache, const int32_t *ptab, int32_t pt_stride,
+                              int64_t n_pages, float *idx_k_cache, float *kmax,
                               int32_t n_seq, int64_t len_max, int64_t nb_max,
                               const int64_t *seq_len, int32_t hq, int32_t hkv, int32_t d,
                               int32_t d_idx, int32_t block, int32_t topk, float scale,

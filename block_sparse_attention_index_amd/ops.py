@@ -33,7 +33,7 @@ ENTRY_POINTS = (
     "msa_index_pool_mean", "msa_index_topk_window", "msa_index_topk_decode_window",
     "msa_sparse_gqa_decode_paged", "msa_prefill_varlen_workspace_bytes",
     "msa_prefill_varlen", "msa_decode_step_noalloc_max_bytes", "msa_decode_step_noalloc",
-    "msa_sparse_gqa_prefill_paged",
+    "msa_sparse_gqa_prefill_paged", "msa_decode_step_paged",
 )
 
 
@@ -89,6 +89,9 @@ def load():
         "msa_decode_step_workspace_bytes": ([i32, i64, i32, i32, i32, i32], sz),
         "msa_decode_step": ([P, P, P, P, P, P, P, P, P, i32, i32, i64, i64, P, i32, i32,
                              i32, i32, i32, i32, f32, P, P, P, P, sz, P], ctypes.c_int),
+        "msa_decode_step_paged": ([P, P, P, P, P, P, P, i64, P, i32, P, P, i32, i64, i64, P,
+                                   i32, i32, i32, i32, i32, i32, f32, P, P, P, P, sz, P],
+                                  ctypes.c_int),
         "msa_decode_step_noalloc_max_bytes": ([], sz),
         "msa_decode_step_noalloc": ([P, P, P, P, P, P, P, P, P, i32, i32, i64, i64, P, i32,
                                      i32, i32, i32, i32, i32, f32, P, P, P, P], ctypes.c_int),
@@ -527,6 +530,45 @@ def msa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         _ptr(seq_len), hq, hkv, d, d_idx, block, topk, scale, _ptr(sel), _ptr(o), _ptr(lse),
         _ptr(ws), ws.numel(), _stream(q))
     _check("msa_decode_step", st)
+    return o, lse, sel
+
+
+def msa_decode_step_paged(q, k_new, v_new, idx_q, idx_k_new, k_pages, v_pages, block_table,
+                          kmax, seq_len, block: int, topk: int, len_max: int,
+                          scale: float | None = None, idx_k_cache=None, sel=None, o=None,
+                          lse=None, ws=None, want_lse: bool = True):
+    """Fused decode step over a paged bf16 cache: ``k_pages``/``v_pages``
+    [n_pages, Hkv, B, d]; ``block_table`` [n_seq, max_blocks] int32; the new
+    token's rows go to row ``L % B`` of page ``block_table[s][L // B]``.
+    ``len_max`` bounds L (and is the row capacity of ``idx_k_cache`` [n_seq,
+    len_max, d_idx] when given).  Otherwise as :func:`msa_decode_step`."""
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pages, "k_pages"),
+                  (v_pages, "v_pages")):
+        _dev(t, nm, torch.bfloat16)
+    for t, nm in ((idx_q, "idx_q"), (idx_k_new, "idx_k_new"), (kmax, "kmax")):
+        _dev(t, nm, torch.float32)
+    if idx_k_cache is not None:
+        _dev(idx_k_cache, "idx_k_cache", torch.float32)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_len, "seq_len", torch.int64)
+    n_seq, hq, d = q.shape
+    n_pages, hkv = k_pages.shape[0], k_pages.shape[1]
+    nb_max, d_idx = kmax.shape[1], kmax.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load()
+    ws = _ws(lib.msa_decode_step_workspace_bytes(n_seq, nb_max, hq, d, block, topk), q, ws)
+    if sel is None:
+        sel = torch.empty((n_seq, topk), dtype=torch.int32, device=q.device)
+    if o is None:
+        o = torch.empty((n_seq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((n_seq, hq), dtype=torch.float32, device=q.device)
+    st = lib.msa_decode_step_paged(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(idx_q), _ptr(idx_k_new), _ptr(k_pages),
+        _ptr(v_pages), n_pages, _ptr(block_table), block_table.shape[1], _ptr(idx_k_cache),
+        _ptr(kmax), n_seq, len_max, nb_max, _ptr(seq_len), hq, hkv, d, d_idx, block, topk,
+        scale, _ptr(sel), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(q))
+    _check("msa_decode_step_paged", st)
     return o, lse, sel
 
 

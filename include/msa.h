@@ -393,6 +393,35 @@ int msa_decode_step(const void *q, const void *k_new, const void *v_new,
                     int32_t *sel, float *o, float *lse, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* --------------------------------------------------------------------------
+ * msa_decode_step_paged -- msa_decode_step with the keys and values in a
+ * paged bf16 cache ([CXT] section 3.3: block-granular KV cache management,
+ * the new token appended into its block's page).  Page layout and table as
+ * msa_sparse_gqa_decode_paged:
+ *
+ *   k_pages, v_pages  [n_pages][Hkv][B][d] bf16; the new token's K and V
+ *                     rows are written at row L % B of page block_table[s][L / B]
+ *   block_table       [n_seq][max_blocks] int32 (the caller places a page
+ *                     there before the step whose token opens the block)
+ *   idx_k_cache       [n_seq][len_max][d_idx] fp32 or NULL; len_max bounds L
+ *   everything else as msa_decode_step (ws: msa_decode_step_workspace_bytes)
+ * Requires L < len_max, L / B < nb_max and L / B < max_blocks with a table
+ * entry in [0, n_pages) for the new token's block; a sequence without them
+ * gets no append and unspecified outputs (nothing outside the given buffers
+ * is written).  A selected block whose entry is outside [0, n_pages) attends
+ * no keys.  Results are bit-identical to msa_decode_step on the same cache
+ * laid out contiguously.
+ * Supported: d = 128, Hq/Hkv in {1, 2, 4, 8, 16}; n_seq * Hkv * K <= 2^28.
+ * ------------------------------------------------------------------------ */
+int msa_decode_step_paged(const void *q, const void *k_new, const void *v_new,
+                          const float *idx_q, const float *idx_k_new, void *k_pages,
+                          void *v_pages, int64_t n_pages, const int32_t *block_table,
+                          int32_t max_blocks, float *idx_k_cache, float *kmax, int32_t n_seq,
+                          int64_t len_max, int64_t nb_max, const int64_t *seq_len, int32_t hq,
+                          int32_t hkv, int32_t d, int32_t d_idx, int32_t block, int32_t topk,
+                          float scale, int32_t *sel, float *o, float *lse, void *ws,
+                          size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * msa_decode_step_noalloc -- msa_decode_step for callers that cannot
  * allocate device memory or pass a workspace (code under HIP graph capture,

@@ -218,3 +218,23 @@ def test_paged_prefill_validation(lib):
     need = lib.msa_prefill_workspace_bytes(1, 0, 4096, 64, 128, 64, 16)
     assert call(args(wsb=need - 1)) == EWS
     assert call(args(nq=0)) == 0                          # nothing to do
+
+
+def test_paged_decode_step_validation(lib):
+    P = FAKE
+    f = lib.msa_decode_step_paged
+    args = lambda **kw: dict(dict(q=P, kn=P, vn=P, iq=P, ikn=P, kp=P, vp=P, npg=64, bt=P, mb=8,
+                                  ikc=None, km=P, n=4, lm=4096, nbm=8, sl=P, hq=64, hkv=8,
+                                  d=128, di=128, B=512, K=8, sc=0.1, sel=P, o=P, lse=None, ws=P,
+                                  wsb=1 << 40, st=None), **kw)
+    keys = ["q", "kn", "vn", "iq", "ikn", "kp", "vp", "npg", "bt", "mb", "ikc", "km", "n", "lm",
+            "nbm", "sl", "hq", "hkv", "d", "di", "B", "K", "sc", "sel", "o", "lse", "ws", "wsb",
+            "st"]
+    call = lambda a: f(*[a[k_] for k_ in keys])
+    assert call(args(bt=None)) == EINVAL
+    assert call(args(npg=0)) == EINVAL
+    assert call(args(mb=0)) == EINVAL
+    assert call(args(hq=60)) == EINVAL
+    assert call(args(d=64)) == EUNSUP
+    need = lib.msa_decode_step_workspace_bytes(4, 8, 64, 128, 512, 8)
+    assert call(args(wsb=need - 1)) == EWS
