@@ -524,10 +524,22 @@ __device__ __forceinline__ void async_wait_barrier() {
 // first CSR position, row end, sequence) and tq[t][i] = query row of the
 // tile's i-th row token (-1 past the row end).
 // ---------------------------------------------------------------------------
+// Per-tile metadata of the KV-outer pass, everything an item needs resolved
+// here once per tile, so the persistent kernel's prefetch of the next items
+// is a few independent loads: the element offset of the tile's block in KV
+// head 0 (head g adds g times the head stride), the partial-record index of
+// the tile's first row (record of row i = nb0 + i), and the block's key count.
+struct __attribute__((aligned(16))) TileMeta {
+  int64_t kvb;
+  int64_t nb0;
+  int32_t nkeys;
+  int32_t pad[3];
+};
+
 template <int TPT>
 __global__ __launch_bounds__(256) void prefill_tile_info(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ tile_ptr,
-    const int32_t *__restrict__ q_list, SeqTab tab, int4 *__restrict__ info,
+    const int32_t *__restrict__ q_list, SeqTab tab, KvMap kvm, TileMeta *__restrict__ info,
     int32_t *__restrict__ tq) {
   const int64_t gb = blockIdx.x;
   const int32_t t0 = tile_ptr[gb], t1 = tile_ptr[gb + 1];
@@ -536,11 +548,26 @@ __global__ __launch_bounds__(256) void prefill_tile_info(
   const int64_t b = gb - tab.blk0[sq];
   const int64_t own_b = own_through_g(tab, sq, b) - own_through_g(tab, sq, b - 1);
   const int32_t base = (int32_t)(row_ptr[gb] + own_b), end = row_ptr[gb + 1];
+  int64_t nkeys = tab.B;   // a non-own block is always full
+  if (!kvm.pages) {        // contiguous rows: never past the cache (invalid input only)
+    const int64_t r0 = tab.kv_row0[sq] + b * tab.B;
+    if (r0 + nkeys > kvm.kv_stride) nkeys = kvm.kv_stride - r0;
+    if (nkeys < 0) nkeys = 0;
+  }
+  const int64_t kvb = kv_block_off<kD>(kvm, tab, sq, b, 0);
+  const int64_t own_thr = own_through_g(tab, sq, b);
   for (int x = threadIdx.x; x < (t1 - t0) * TPT; x += 256) {
     const int tt = x / TPT, i = x % TPT;
     const int32_t e = base + tt * TPT + i;
     tq[(int64_t)(t0 + tt) * TPT + i] = e < end ? q_list[e] : -1;
-    if (i == 0) info[t0 + tt] = make_int4((int)gb, base + tt * TPT, end, sq);
+    if (i == 0) {
+      TileMeta m;
+      m.kvb = kvb;
+      m.nb0 = (int64_t)(base + tt * TPT) - own_thr;
+      m.nkeys = (int32_t)nkeys;
+      m.pad[0] = m.pad[1] = m.pad[2] = 0;
+      info[t0 + tt] = m;
+    }
   }
 }
 
@@ -548,7 +575,7 @@ template <int G, int NW>
 __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, KvMap kvm, SeqTab tab, int hq, int hkv,
-    const int32_t *__restrict__ tile_ptr, const int4 *__restrict__ info,
+    const int32_t *__restrict__ tile_ptr, const TileMeta *__restrict__ info,
     const int32_t *__restrict__ tq,
     float scale_log2, uint16_t *__restrict__ part_o, float2 *__restrict__ part_le,
     int64_t n_part) {
@@ -593,23 +620,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
       dst[cc] = as_bf16x8(x);
     }
   };
-  // element offset of an item's block (info: global block, ..., sequence) in
-  // KV head gg, and its key count (B: a non-own block is always full)
-  auto kv_off = [&](const int4 &f, int gg) {
-    return kv_block_off<kD>(kvm, tab, f.w, f.x - tab.blk0[f.w], gg);
-  };
-  auto kv_keys = [&](const int4 &f) {
-    int64_t n = B;
-    if (!kvm.pages) {   // contiguous rows: never past the cache (invalid input only)
-      const int64_t r0 = tab.kv_row0[f.w] + (int64_t)(f.x - tab.blk0[f.w]) * B;
-      if (r0 + n > kvm.kv_stride) n = kvm.kv_stride - r0;
-    }
-    return n;
-  };
+  // element offset of an item's block in KV head gg, and its key count
+  const int64_t hstride = kvm.pages ? (int64_t)B * kD : kvm.kv_stride * kD;
+  auto kv_off = [&](const TileMeta &f, int gg) { return f.kvb + (int64_t)gg * hstride; };
+  auto kv_keys = [&](const TileMeta &f) { return (int64_t)f.nkeys; };
 
   // current item: head, tile info, this lane's query, K/V span
   int g = (int)(w / T);
-  int4 inf = info[w % T];
+  TileMeta inf = info[w % T];
   int32_t qraw = tq[(w % T) * TPT + tl];
   int64_t nkeys = kv_keys(inf);
   int64_t n_chunks = (nkeys + kKA - 1) / kKA;
@@ -623,9 +641,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   int64_t wn = w + per;
   bool has_next = wn < w_end;
   int gn = 0;
-  int4 infn = make_int4(0, 0, 0, 0);
+  TileMeta infn = {};
   int32_t qrawn = -1;
-  auto fetch = [&](int64_t ww, int &gg, int4 &ii, int32_t &qq) {
+  auto fetch = [&](int64_t ww, int &gg, TileMeta &ii, int32_t &qq) {
     if (ww < w_end) {
       gg = (int)(ww / T);
       ii = info[ww % T];
@@ -673,7 +691,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
     const int64_t kc = ci * kKA;
     const bool last = ci + 1 >= n_chunks;
     int gnn = 0;
-    int4 infnn = make_int4(0, 0, 0, 0);
+    TileMeta infnn = {};
     int32_t qrawnn = -1;
     if (last && has_next) {
       stage_q(gn, qrawn);
@@ -764,8 +782,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
       const bool act = qraw >= 0 && qraw < n_q;
       const float ltot = sum_with_partner(lsum);
       if (act) {
-        const int64_t e = (int64_t)inf.y + tl;
-        const int64_t n_idx = e - own_through_g(tab, inf.w, inf.x - tab.blk0[inf.w]);
+        const int64_t n_idx = inf.nb0 + tl;
         if (n_idx >= 0 && n_idx < n_part)
           put_partial(part_o, part_le, n_idx, g, hq, G, hl, h, acc, mref, ltot);
       }
@@ -823,7 +840,7 @@ hipError_t launch_mfma_g(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          const KvMap &kvm, const SeqTab &tab, int hq, int hkv,
                          const int32_t *sel, int topk, const int32_t *row_ptr,
                          const int32_t *q_list, const int32_t *slot, float scale, float *o,
-                         float *lse, int32_t *tile_ptr, int4 *info, int32_t *tq,
+                         float *lse, int32_t *tile_ptr, TileMeta *info, int32_t *tq,
                          uint16_t *part_o, float2 *part_le, int64_t n_part,
                          int64_t max_tiles, hipStream_t st) {
   constexpr int TPT = NW * NB * (32 / G);
@@ -833,7 +850,7 @@ hipError_t launch_mfma_g(const uint16_t *q, const uint16_t *k, const uint16_t *v
     hipLaunchKernelGGL(prefill_tiles, dim3(1), dim3(1024), 0, st, row_ptr, tab, TPT,
                        max_tiles, tile_ptr);
     hipLaunchKernelGGL((prefill_tile_info<TPT>), dim3((unsigned)nb), dim3(256), 0, st,
-                       row_ptr, tile_ptr, q_list, tab, info, tq);
+                       row_ptr, tile_ptr, q_list, tab, kvm, info, tq);
     const int grid = 8 * ((num_cus() + 7) / 8);
     hipLaunchKernelGGL((prefill_nonown_persistent<G, NW>), dim3(grid), dim3(64 * NW),
                        0, st, q, k, v, kvm, tab, hq, hkv, tile_ptr, info, tq, sl2,
@@ -873,7 +890,7 @@ MfmaLayout mfma_layout(const SeqTab &tab, int32_t hq, int32_t d, int32_t topk, i
   L.tile_ptr = off; off += align256((size_t)(L.nb + 1) * 4);
   L.part_o = off;   off += align256((size_t)L.np * hq * d * 2);
   L.part_le = off;  off += align256((size_t)L.np * hq * 8);
-  L.info = off;     off += align256((size_t)(L.np / 16 + L.nb) * 16);
+  L.info = off;     off += align256((size_t)(L.np / 16 + L.nb) * sizeof(TileMeta));
   L.tq = off;       off += align256((size_t)(L.np + 256 * L.nb) * 4);
   L.total = off;
   const int64_t by_info = L.np / 16 + L.nb, by_tq = (L.np + 256 * L.nb) / tpt;
@@ -904,7 +921,7 @@ hipError_t launch_prefill_chain(const void *q, const void *k, const void *v,
   int32_t *tile_ptr = reinterpret_cast<int32_t *>(w + L.tile_ptr);
   uint16_t *part_o = reinterpret_cast<uint16_t *>(w + L.part_o);
   float2 *part_le = reinterpret_cast<float2 *>(w + L.part_le);
-  int4 *info = reinterpret_cast<int4 *>(w + L.info);
+  TileMeta *info = reinterpret_cast<TileMeta *>(w + L.info);
   int32_t *tq = reinterpret_cast<int32_t *>(w + L.tq);
   const uint16_t *qq = static_cast<const uint16_t *>(q);
   const uint16_t *kk = static_cast<const uint16_t *>(k);

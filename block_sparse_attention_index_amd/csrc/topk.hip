@@ -64,6 +64,7 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
   __shared__ int lst_b[kQT][KMAX];
   __shared__ int lst_n[kQT];
   __shared__ float lst_t[kQT];   // entry threshold: the (K-1)-th score, -inf until full
+  __shared__ int64_t lst_lim[kQT];   // first block past the query's candidates
   // scores alias the block rows (written after the MFMAs' last read of them,
   // read before the next chunk's staging; both sides fenced)
   float(*sc)[kPad] = ks;
@@ -114,6 +115,8 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
   if (tid < kQT) {
     lst_n[tid] = 0;
     lst_t[tid] = -INFINITY;
+    // one 64-bit division per query, not one per query and chunk
+    lst_lim[tid] = (q_pos0 + q0 + tid) / B - win + 1;
   }
   for (int e = tid; e < kQT * KMAX; e += 256) {
     lst_s[e / KMAX][e % KMAX] = -INFINITY;
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
 #pragma unroll
     for (int jq = 0; jq < 16; ++jq) {
       const int qi = wave * 16 + jq;
-      const int64_t lim = (q_pos0 + q0 + qi) / B - win + 1;
+      const int64_t lim = lst_lim[qi];
       const float s = sc[qi][lane];
       const float t = lst_t[qi];
       const bool valid = qi < nq && lane < nbk && b0 + lane < lim;
@@ -182,6 +185,191 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
       }
     }
     __syncthreads();   // sc (aliasing ks) is read above; the next staging overwrites it
+  }
+  for (int jq = 0; jq < 16; ++jq) {
+    const int qi = wave * 16 + jq;
+    if (qi >= nq) break;
+    const int own = (int)((q_pos0 + q0 + qi) / B);
+    const int cnt = km > 0 ? lst_n[qi] : 0;
+    const int lb = (lane < cnt) ? lst_b[qi][lane] : INT32_MAX;
+    write_row(sel + (q0 + qi) * topk, topk, cnt, lb, own, window_first(own, win));
+    if (sel_g)
+      write_row(sel_g + (tab.q_row0[sq] + q0 + qi) * topk, topk, cnt,
+                lane < cnt ? lb + tab.blk0[sq] : INT32_MAX, own + tab.blk0[sq],
+                window_first(own, win) + tab.blk0[sq]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill, d_idx <= DW (DW = 64 or 128): the same tiles, lists and merge as
+// topk_prefill_kernel, with the operands laid out for fewer memory steps.
+// The dot product runs over DW/2 matrix-core steps, step t taking index
+// columns t (lanes 0-31) and t + DW/2 (lanes 32-63) -- a sum over all
+// columns in another order, which the near-tie bound covers.  So each lane's
+// query operands are DW/2 consecutive columns of one query row, held in
+// registers for the whole tile, and its summary operands four steps at a
+// time are one 16-byte LDS read.  The next chunk of summaries is loaded
+// into registers while the current chunk's products run, then written to
+// LDS after the barrier that ends the current chunk's reads.  Columns past
+// d_idx and rows past the chunk are zero.
+// ---------------------------------------------------------------------------
+template <int KMAX, int DW>
+__global__ __launch_bounds__(256) void topk_prefill_reg(
+    const float *__restrict__ idx_q_all, SeqTab tab, const float *__restrict__ kmax_all,
+    int d_idx, int topk, int win, int32_t *__restrict__ sel_all,
+    int32_t *__restrict__ sel_g) {
+  constexpr int kHalf = DW / 2;        // matrix-core steps; also columns per half-wave
+  constexpr int kStr = DW + 4;         // LDS row stride (floats): 16-byte aligned rows
+  constexpr int kV = DW / 4;           // float4 per row
+  constexpr int kLd = kCB * kV / 256;  // float4 per thread per chunk
+  __shared__ __attribute__((aligned(16))) float ks[kCB * kStr];
+  __shared__ float sc[kQT][kCB + 1];
+  __shared__ float lst_s[kQT][KMAX];
+  __shared__ int lst_b[kQT][KMAX];
+  __shared__ int lst_n[kQT];
+  __shared__ float lst_t[kQT];   // entry threshold: the (K-1)-th score, -inf until full
+  __shared__ int64_t lst_lim[kQT];   // first block past the query's candidates
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Heavier (later) tiles first.
+  const int64_t tile_g = (int64_t)tab.qt0[tab.n] - 1 - blockIdx.x;
+  const int sq = prefix_find(tab.qt0, tab.n, tile_g);
+  const int64_t tile = tile_g - tab.qt0[sq];
+  const int64_t n_q = seq_nq(tab, sq), q_pos0 = tab.q_pos0[sq];
+  const int B = tab.B;
+  const float *idx_q = idx_q_all + tab.q_row0[sq] * d_idx;
+  const float *kmax = kmax_all + (int64_t)tab.blk0[sq] * d_idx;
+  int32_t *sel = sel_all + tab.q_row0[sq] * topk;
+  const int64_t q0 = tile * kQT;
+  const int nq = (int)(n_q - q0 < kQT ? n_q - q0 : kQT);
+  const int km = topk - win;   // picks by score; the window win is forced
+  const int64_t cand_last = (q_pos0 + q0 + nq - 1) / B - win + 1;
+  const bool vq = (d_idx & 3) == 0 && (reinterpret_cast<uintptr_t>(idx_q) & 15) == 0;
+  const bool vk = (d_idx & 3) == 0 && (reinterpret_cast<uintptr_t>(kmax) & 15) == 0;
+
+  // four consecutive columns c .. c+3 of row r of a [*, d_idx] matrix (zero
+  // past d_idx), with one 16-byte load when rows are aligned
+  auto load4 = [&](const float *m, bool vec, int64_t r, int c) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (vec) {
+      if (c < d_idx) x = *reinterpret_cast<const float4 *>(m + r * d_idx + c);
+    } else {
+      const float *p = m + r * d_idx;
+      if (c < d_idx) x.x = p[c];
+      if (c + 1 < d_idx) x.y = p[c + 1];
+      if (c + 2 < d_idx) x.z = p[c + 2];
+      if (c + 3 < d_idx) x.w = p[c + 3];
+    }
+    return x;
+  };
+
+  const int qw = wave >> 1, bw = wave & 1;
+  const int h = lane >> 5, j = lane & 31;
+  // this lane's query operands: row 32*qw + j, columns kHalf*h .. + kHalf-1
+  float qreg[kHalf];
+  {
+    const int qr = 32 * qw + j;
+#pragma unroll
+    for (int u = 0; u < kHalf / 4; ++u) {
+      const float4 x = qr < nq ? load4(idx_q, vq, q0 + qr, kHalf * h + 4 * u)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      qreg[4 * u] = x.x;
+      qreg[4 * u + 1] = x.y;
+      qreg[4 * u + 2] = x.z;
+      qreg[4 * u + 3] = x.w;
+    }
+  }
+  // the next chunk's summaries, in flight in registers
+  float4 kn[kLd];
+  auto fetch = [&](int64_t b0) {
+    const int nbk = (int)(cand_last - b0 < kCB ? cand_last - b0 : kCB);
+#pragma unroll
+    for (int i = 0; i < kLd; ++i) {
+      const int e = tid + 256 * i, r = e / kV, c = 4 * (e % kV);
+      kn[i] = r < nbk ? load4(kmax, vk, b0 + r, c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int i = 0; i < kLd; ++i) {
+      const int e = tid + 256 * i, r = e / kV, c = 4 * (e % kV);
+      *reinterpret_cast<float4 *>(&ks[r * kStr + c]) = kn[i];
+    }
+  };
+
+  if (tid < kQT) {
+    lst_n[tid] = 0;
+    lst_t[tid] = -INFINITY;
+    // one 64-bit division per query, not one per query and chunk
+    lst_lim[tid] = (q_pos0 + q0 + tid) / B - win + 1;
+  }
+  for (int e = tid; e < kQT * KMAX; e += 256) {
+    lst_s[e / KMAX][e % KMAX] = -INFINITY;
+    lst_b[e / KMAX][e % KMAX] = -1;
+  }
+  if (km > 0 && cand_last > 0) {
+    fetch(0);
+    put();
+  }
+  __syncthreads();
+
+  for (int64_t b0 = 0; km > 0 && b0 < cand_last; b0 += kCB) {
+    const int nbk = (int)(cand_last - b0 < kCB ? cand_last - b0 : kCB);
+    const bool more = b0 + kCB < cand_last;
+    if (more) fetch(b0 + kCB);   // lands under this chunk's products
+    f32x16s d;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) d[r] = 0.f;
+    const float *krow = &ks[(32 * bw + j) * kStr + kHalf * h];
+#pragma unroll
+    for (int u = 0; u < kHalf / 4; ++u) {
+      const float4 kv = *reinterpret_cast<const float4 *>(krow + 4 * u);
+      d = __builtin_amdgcn_mfma_f32_32x32x2f32(qreg[4 * u], kv.x, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_32x32x2f32(qreg[4 * u + 1], kv.y, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_32x32x2f32(qreg[4 * u + 2], kv.z, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_32x32x2f32(qreg[4 * u + 3], kv.w, d, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[32 * qw + 8 * (r >> 2) + 4 * h + (r & 3)][32 * bw + j] = d[r];
+    __syncthreads();   // scores visible; every wave done reading ks
+    if (more) put();   // the next chunk, for after the merge
+    // Merge: wave w owns queries 16w .. 16w+15.
+    uint32_t need = 0;
+    uint64_t masks[16];
+#pragma unroll
+    for (int jq = 0; jq < 16; ++jq) {
+      const int qi = wave * 16 + jq;
+      const int64_t lim = lst_lim[qi];
+      const float sv = sc[qi][lane];
+      const float t = lst_t[qi];
+      const bool valid = qi < nq && lane < nbk && b0 + lane < lim;
+      masks[jq] = __ballot(valid && sv > t);
+      if (masks[jq]) need |= 1u << jq;
+    }
+    while (need) {
+      const int jq = __ffs(need) - 1;
+      need &= need - 1;
+      const int qi = wave * 16 + jq;
+      const float sv = sc[qi][lane];
+      int cnt = lst_n[qi];
+      float ls = lane < km ? lst_s[qi][lane] : -INFINITY;
+      int lb = lane < km ? lst_b[qi][lane] : -1;
+      uint64_t mask = 0;
+#pragma unroll
+      for (int x = 0; x < 16; ++x)
+        if (x == jq) mask = masks[x];
+      list_insert(sv, (int)b0, mask, km, cnt, ls, lb);
+      if (lane < km) {
+        lst_s[qi][lane] = ls;
+        lst_b[qi][lane] = lb;
+      }
+      const float thr = lane_f(ls, km - 1);
+      if (lane == 0) {
+        lst_n[qi] = cnt;
+        lst_t[qi] = cnt < km ? -INFINITY : thr;
+      }
+    }
+    __syncthreads();   // sc read above and ks written: the next chunk may start
   }
   for (int jq = 0; jq < 16; ++jq) {
     const int qi = wave * 16 + jq;
@@ -245,6 +433,24 @@ hipError_t launch_topk_tab(const float *idx_q, const SeqTab &tab, const float *k
 #define MSA_TK(KM, FU)                                                                     \
   hipLaunchKernelGGL((topk_prefill_kernel<KM, FU>), grid, wg, 0, st, idx_q, tab, kmax, d_idx, \
                      topk, win, sel, sel_g)
+#define MSA_TR(KM, DW)                                                                     \
+  hipLaunchKernelGGL((topk_prefill_reg<KM, DW>), grid, wg, 0, st, idx_q, tab, kmax, d_idx,    \
+                     topk, win, sel, sel_g)
+  if (d_idx <= 128) {   // query operands in registers
+    if (topk - win <= 16) {
+      if (d_idx <= 64)
+        MSA_TR(16, 64);
+      else
+        MSA_TR(16, 128);
+    } else {
+      if (d_idx <= 64)
+        MSA_TR(64, 64);
+      else
+        MSA_TR(64, 128);
+    }
+#undef MSA_TR
+    return hipGetLastError();
+  }
   if (topk - win <= 16) {
     if (full)
       MSA_TK(16, true);
