@@ -346,27 +346,58 @@ __global__ __launch_bounds__(256) void topk_prefill_reg(
       masks[jq] = __ballot(valid && sv > t);
       if (masks[jq]) need |= 1u << jq;
     }
-    while (need) {
-      const int jq = __ffs(need) - 1;
-      need &= need - 1;
-      const int qi = wave * 16 + jq;
-      const float sv = sc[qi][lane];
-      int cnt = lst_n[qi];
-      float ls = lane < km ? lst_s[qi][lane] : -INFINITY;
-      int lb = lane < km ? lst_b[qi][lane] : -1;
-      uint64_t mask = 0;
+    // Insertions, several queries at once: the wave splits into groups of
+    // S lanes (S >= km), group gr holding the list of one query (entry gl in
+    // lane gl of the group) and inserting that query's candidates in block
+    // order, one per pass -- the same sequence of insertions as one query at
+    // a time, so the same lists.
+    {
+      const int S = km <= 8 ? 8 : (km <= 16 ? 16 : (km <= 32 ? 32 : 64));
+      const int NG = 64 / S;
+      const int gr = lane / S, gl = lane % S;
+      const uint64_t gmask = S == 64 ? ~0ull : ((1ull << S) - 1) << (gr * S);
+      for (int r0 = 0; r0 < 16; r0 += NG) {
+        if (!((need >> r0) & ((1u << NG) - 1))) continue;
+        const int jq = r0 + gr;
+        const int qi = wave * 16 + jq;
+        uint64_t mask = 0;
 #pragma unroll
-      for (int x = 0; x < 16; ++x)
-        if (x == jq) mask = masks[x];
-      list_insert(sv, (int)b0, mask, km, cnt, ls, lb);
-      if (lane < km) {
-        lst_s[qi][lane] = ls;
-        lst_b[qi][lane] = lb;
-      }
-      const float thr = lane_f(ls, km - 1);
-      if (lane == 0) {
-        lst_n[qi] = cnt;
-        lst_t[qi] = cnt < km ? -INFINITY : thr;
+        for (int x = 0; x < 16; ++x)
+          if (x == jq) mask = masks[x];
+        int cnt = lst_n[qi];
+        float ls = gl < km ? lst_s[qi][gl] : -INFINITY;
+        int lb = gl < km ? lst_b[qi][gl] : -1;
+        float thr = lst_t[qi];
+        while (__ballot(mask != 0)) {
+          const bool act = mask != 0;
+          const int src = act ? __ffsll((unsigned long long)mask) - 1 : 0;
+          const float sj = sc[qi][src];
+          if (act) mask &= mask - 1;
+          const bool ins = act && (cnt < km || sj > thr);
+          const int pos = __popcll(__ballot(gl < cnt && ls >= sj) & gmask);
+          const float up_s = __shfl_up(ls, 1, S);
+          const int up_b = __shfl_up(lb, 1, S);
+          const int last = cnt < km - 1 ? cnt : km - 1;
+          if (ins && gl > pos && gl <= last) {
+            ls = up_s;
+            lb = up_b;
+          }
+          if (ins && gl == pos) {
+            ls = sj;
+            lb = (int)b0 + src;
+          }
+          if (ins) cnt = cnt + 1 < km ? cnt + 1 : km;
+          const float kth = __shfl(ls, gr * S + km - 1);
+          thr = cnt < km ? -INFINITY : kth;
+        }
+        if (gl < km) {
+          lst_s[qi][gl] = ls;
+          lst_b[qi][gl] = lb;
+        }
+        if (gl == 0) {
+          lst_n[qi] = cnt;
+          lst_t[qi] = thr;
+        }
       }
     }
     __syncthreads();   // sc read above and ks written: the next chunk may start
