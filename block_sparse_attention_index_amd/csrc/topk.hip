@@ -368,15 +368,25 @@ __global__ __launch_bounds__(256) void topk_prefill_reg(
         float ls = gl < km ? lst_s[qi][gl] : -INFINITY;
         int lb = gl < km ? lst_b[qi][gl] : -1;
         float thr = lst_t[qi];
+        // each pass reads the score of the group's next candidate ahead, so
+        // the LDS round trip overlaps the current insertion
+        int nsrc = mask != 0 ? __ffsll((unsigned long long)mask) - 1 : 0;
+        float nsj = sc[qi][nsrc];
         while (__ballot(mask != 0)) {
           const bool act = mask != 0;
-          const int src = act ? __ffsll((unsigned long long)mask) - 1 : 0;
-          const float sj = sc[qi][src];
+          const int src = nsrc;
+          const float sj = nsj;
           if (act) mask &= mask - 1;
-          const bool ins = act && (cnt < km || sj > thr);
+          nsrc = mask != 0 ? __ffsll((unsigned long long)mask) - 1 : 0;
+          nsj = sc[qi][nsrc];
+          // rank among the group's entries; below km it enters (a full list:
+          // strictly above the km-th entry, which a tie does not pass)
           const int pos = __popcll(__ballot(gl < cnt && ls >= sj) & gmask);
-          const float up_s = __shfl_up(ls, 1, S);
-          const int up_b = __shfl_up(lb, 1, S);
+          const bool ins = act && pos < km;
+          // entries shift down one lane (DPP; a group's first lane never takes
+          // its neighbour's value: pos >= 0)
+          const float up_s = prev_lane_f(ls);
+          const int up_b = prev_lane_i(lb);
           const int last = cnt < km - 1 ? cnt : km - 1;
           if (ins && gl > pos && gl <= last) {
             ls = up_s;
@@ -387,9 +397,9 @@ __global__ __launch_bounds__(256) void topk_prefill_reg(
             lb = (int)b0 + src;
           }
           if (ins) cnt = cnt + 1 < km ? cnt + 1 : km;
-          const float kth = __shfl(ls, gr * S + km - 1);
-          thr = cnt < km ? -INFINITY : kth;
         }
+        const float kth = __shfl(ls, gr * S + km - 1);
+        thr = cnt < km ? -INFINITY : kth;
         if (gl < km) {
           lst_s[qi][gl] = ls;
           lst_b[qi][gl] = lb;
