@@ -1260,17 +1260,29 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
     d.vs = d.nk > 0 ? v_scale[(int64_t)page * hkv + d.g] : 1.f;
     return d;
   };
-  auto next_unit = [&](uint32_t u, PagedUnit &d, bool empties) __attribute__((always_inline)) {
+  auto next_unit = [&](uint32_t u, PagedUnit &d) __attribute__((always_inline)) {
     for (; u < u_end; ++u) {
       d = unit(u);
       if (d.nk > 0) break;
-      if (empties) {
-        for (int x = tid; x < G * D; x += 256) part_o[(size_t)u * G * D + x] = 0.f;
-        if (tid < G) part_lse[(size_t)u * G + tid] = -INFINITY;
-      }
     }
     return u;
   };
+  // Runs of one (sequence, KV head), as in decode_paged: the page's V scale
+  // is folded into the weights of its keys (the normaliser keeps the
+  // unscaled ones), so the online softmax runs on across pages and one
+  // partial per run is written, in the slot of the run's first unit in this
+  // workgroup's range; a run whose units are all empty gets the neutral one.
+  const uint32_t ups_g = (uint32_t)(topk * nseg);
+  auto run_slot = [&](uint32_t sg) __attribute__((always_inline)) {
+    const uint32_t u0 = sg * ups_g;
+    return u0 > u_begin ? u0 : u_begin;
+  };
+  auto put_neutral = [&](uint32_t sg) __attribute__((always_inline)) {
+    const size_t sl = run_slot(sg);
+    for (int x = tid; x < G * D; x += 256) part_o[sl * G * D + x] = 0.f;
+    if (tid < G) part_lse[sl * G + tid] = -INFINITY;
+  };
+  uint32_t sg_next = u_begin / ups_g;
   auto dma_kv = [&](PagedBuf<true> &buf, const PagedUnit &d, int64_t row, int nrows)
       __attribute__((always_inline)) {
     const uint8_t *kb = kpool + (d.row0 + row) * RB;
@@ -1299,10 +1311,13 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
 
   // compute cursor (unit u, chunk ci) and the next non-empty unit
   PagedUnit cu;
-  uint32_t u = next_unit(u_begin, cu, true);
-  if (u >= u_end) return;
+  uint32_t u = next_unit(u_begin, cu);
+  if (u >= u_end) {
+    for (uint32_t sg = sg_next; sg <= (u_end - 1) / ups_g; ++sg) put_neutral(sg);
+    return;
+  }
   PagedUnit nu = cu;
-  uint32_t un = next_unit(u + 1, nu, true);
+  uint32_t un = next_unit(u + 1, nu);
   // copy cursor, two chunks ahead
   PagedUnit du = cu;
   uint32_t ud = u;
@@ -1311,7 +1326,7 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
     if (ud >= u_end) return false;
     dma_kv(buf, du, (int64_t)cd * kSK, kv_rows(du.nk - cd * kSK));
     if (++cd * kSK >= du.nk) {
-      ud = next_unit(ud + 1, du, false);
+      ud = next_unit(ud + 1, du);
       cd = 0;
     }
     return true;
@@ -1357,12 +1372,17 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
         if (j >= G) xq = u32x4{0u, 0u, 0u, 0u};
         qf[cc] = as_bf16x8(xq);
       }
+      const uint32_t sg = (uint32_t)cu.s * (uint32_t)hkv + (uint32_t)cu.g;
+      if (sg >= sg_next) {   // a new run (runs whose units were all empty: neutral)
+        for (; sg_next < sg; ++sg_next) put_neutral(sg_next);
+        sg_next = sg + 1;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
-      m = -INFINITY;
-      l = 0.f;
+          for (int rr = 0; rr < 16; ++rr) acc[cb][rr] = 0.f;
+        m = -INFINITY;
+        l = 0.f;
+      }
       if (un < u_end) {
         lds_barrier();   // every wave holds its queries: the staging area is free
         dma_q(nu);
@@ -1415,6 +1435,12 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
         ps += p0[rr] + p1[rr];
       }
       l += sum_with_partner(ps);
+      // the P.V weights carry the page's V scale
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        p0[rr] *= cu.vs;
+        p1[rr] *= cu.vs;
+      }
       const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
       const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
 #pragma unroll
@@ -1431,7 +1457,8 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
       wait_vm<kChunkOps>();
     else
       wait_vm<0>();
-    if (last) {
+    const uint32_t sg_cur = (uint32_t)cu.s * (uint32_t)hkv + (uint32_t)cu.g;
+    if (last && (un >= u_end || (uint32_t)nu.s * (uint32_t)hkv + (uint32_t)nu.g != sg_cur)) {
       lds_barrier();
       float *mo = reinterpret_cast<float *>(&cur);      // [4][G][D]
       float *mm = mml;                                  // [4][G]
@@ -1462,8 +1489,9 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
           z = fmaf(sc, ml[w * G + hd], z);
           ov = fmaf(sc, mo[(w * G + hd) * D + c], ov);
         }
-        part_o[((size_t)u * G + hd) * D + c] = cu.vs * (ov / z);
-        if (c == 0) part_lse[(size_t)u * G + hd] = mx + __log2f(z);
+        const size_t sl = run_slot(sg_cur);
+        part_o[(sl * G + hd) * D + c] = ov / z;
+        if (c == 0) part_lse[sl * G + hd] = mx + __log2f(z);
       }
     }
     lds_barrier();   // chunk i+1 visible to every wave; buffer P reusable
@@ -1474,7 +1502,7 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
     if (un >= u_end) return false;
     u = un;
     cu = nu;
-    un = next_unit(u + 1, nu, true);
+    un = next_unit(u + 1, nu);
     ci = 0;
     return true;
   };
@@ -1484,6 +1512,7 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
     if (!step(std::integral_constant<int, 1>{})) break;
     if (!step(std::integral_constant<int, 2>{})) break;
   }
+  for (; sg_next <= (u_end - 1) / ups_g; ++sg_next) put_neutral(sg_next);
 }
 
 // ---------------------------------------------------------------------------
@@ -1842,12 +1871,9 @@ hipError_t launch_decode_paged(const void *q, const void *k_pages, const void *v
     default:
       return hipErrorInvalidValue;
   }
-  if (kv_dtype == 2)   // FP8: one partial per unit (each unit carries its page's V scale)
-    hipLaunchKernelGGL((decode_merge<128>), dim3(hq, n_seq), dim3(128), 0, st,
-                       topk * pl.nseg, G, hkv, part_o, part_lse, o, lse);
-  else                 // bf16: one partial per run
-    hipLaunchKernelGGL((decode_merge_runs<128>), dim3(hq, n_seq), dim3(128), 0, st, G, hkv,
-                       (uint32_t)(topk * pl.nseg), pl.u_q, pl.u_r, part_o, part_lse, o, lse);
+  // one partial per run (bf16 and FP8 pages alike)
+  hipLaunchKernelGGL((decode_merge_runs<128>), dim3(hq, n_seq), dim3(128), 0, st, G, hkv,
+                     (uint32_t)(topk * pl.nseg), pl.u_q, pl.u_r, part_o, part_lse, o, lse);
   return hipGetLastError();
 }
 
