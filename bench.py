@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 from block_sparse_attention_index_amd import ops, pipeline, synth  # noqa: E402
 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "sparse_gqa_prefill_p1m_traffic.md")
-KERNEL_SOURCES = ("prefill_mfma.hip", "prefill_common.h", "mfma_common.h")
+KERNEL_SOURCES = ("prefill_mfma.hip", "prefill_common.h", "mfma_common.h", "seqtab.h")
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector / MFMA)
