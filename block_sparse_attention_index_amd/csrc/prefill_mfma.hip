@@ -152,18 +152,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int TPT = NW * TPW;  // tokens per tile (workgroup)
   __shared__ MfmaSmem smb[2];
 
-  const int g = blockIdx.y;
+  // XCD-aware order: workgroups are dealt to the eight XCDs round-robin by
+  // linear id, so linear id L runs work item L' = the (L / 8)-th of the L % 8-th
+  // eighth of all (tile, KV head) items.  Each XCD then walks a contiguous
+  // range -- every tile of a block and head on one XCD, whose L2 holds that
+  // block's keys and values for all of them.
+  const uint64_t n_items = (uint64_t)gridDim.x * gridDim.y;
+  const uint64_t lin = blockIdx.x + (uint64_t)blockIdx.y * gridDim.x;
+  const uint64_t xq = n_items / 8, xr = n_items % 8, xc = lin % 8, xk = lin / 8;
+  const uint64_t item = (xc < xr ? xc * (xq + 1) : xr * (xq + 1) + (xc - xr) * xq) + xk;
+  const int64_t tile_x = (int64_t)(item % gridDim.x);
+  const int g = (int)(item / gridDim.x);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = lane >> 5, j = lane & 31;
 
   // ---- the tile: sequence s, its block b, the key count, each row's query ----
   const int B = tab.B;
   const int tpb = (B + TPT - 1) / TPT;
-  const int64_t bt = blockIdx.x / tpb;   // query-holding block of the chain
+  const int64_t bt = tile_x / tpb;   // query-holding block of the chain
   const int sq = prefix_find(tab.ob0, tab.n, bt);
   const int64_t q_pos0 = tab.q_pos0[sq], n_q = seq_nq(tab, sq), row0 = tab.q_row0[sq];
   const int64_t b = q_pos0 / B + (bt - tab.ob0[sq]);
-  const int64_t tok0 = b * B + (int64_t)(blockIdx.x % tpb) * TPT;
+  const int64_t tok0 = b * B + (int64_t)(tile_x % tpb) * TPT;
   int64_t hi = tok0 + TPT - 1;
   if (hi > b * B + B - 1) hi = b * B + B - 1;
   if (hi > q_pos0 + n_q - 1) hi = q_pos0 + n_q - 1;
