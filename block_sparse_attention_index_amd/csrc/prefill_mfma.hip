@@ -493,8 +493,10 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lptr_t dst, 
 
 // One chunk (nrows <= kKA keys of K and of V) into LDS: every lane copies
 // 16-byte pieces, (kKA * kD / 8) / (64 * NW) of K and as many of V.  Piece
-// (row r, segment sp) lands at the row's swizzled slot; rows past nrows
-// re-read the last row (never used: those keys are masked).  The offsets are
+// (row r, segment sp) lands at the row's swizzled slot.  Rows past nrows
+// (a short block) lie beyond the buffer resource's range of nrows rows, so
+// their copies fetch nothing from memory (an out-of-range buffer read yields
+// zero); those keys are masked.  The offsets are
 // recomputed per copy (a few integer operations) rather than kept in
 // registers across the chunk loop.
 template <int NW>
@@ -509,9 +511,8 @@ __device__ __forceinline__ void async_chunk(AsyncSmem &sm, const uint16_t *k,
   for (int i = 0; i < IPW; ++i) {
     const int inst = wave * IPW + i;
     const int r = (inst * 64 + lane) >> 4, sp = lane & 15;
-    const int rr = r < nrows ? r : nrows - 1;
-    lds_dma16(rk, (lptr_t)(&sm.Ks[inst * 64 * 8]), (uint32_t)(rr * kD + kswz(r, sp) * 8) * 2);
-    lds_dma16(rv, (lptr_t)(&sm.Vs[inst * 64 * 8]), (uint32_t)(rr * kD + vswz(r, sp) * 8) * 2);
+    lds_dma16(rk, (lptr_t)(&sm.Ks[inst * 64 * 8]), (uint32_t)(r * kD + kswz(r, sp) * 8) * 2);
+    lds_dma16(rv, (lptr_t)(&sm.Vs[inst * 64 * 8]), (uint32_t)(r * kD + vswz(r, sp) * 8) * 2);
   }
 }
 
@@ -600,6 +601,17 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
   const int h = lane >> 5, j = lane & 31;
   const int tl = wave * TPN + j / G;  // token slot of this lane's row
   const int hl = j % G;                // head of this lane's row in the group
+
+  // A short block's rows past its keys read as out of range: their LDS rows
+  // then hold zeros or what an earlier chunk left there -- finite either
+  // way, so the masked keys' zero weights times those values add nothing.
+  for (int x = threadIdx.x; x < kKA * kD / 8; x += 64 * NW) {
+    reinterpret_cast<u32x4 *>(sm0.Ks)[x] = u32x4{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4 *>(sm0.Vs)[x] = u32x4{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4 *>(sm1.Ks)[x] = u32x4{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4 *>(sm1.Vs)[x] = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
 
   const int B = tab.B;
   const int64_t n_q = tab.q_row0[tab.n];   // query rows of the chain
