@@ -850,6 +850,7 @@ struct PagedUnit {
   int nk;          // keys in the unit (0: empty)
   float ks, vs;    // the page's K and V scales (1 for bf16)
 };
+constexpr int kUnitTab = 64;   // units per workgroup resolved up front
 
 // 8 e4m3 bytes -> 8 bf16 (exact: every e4m3 value is a bf16 value)
 __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
@@ -912,9 +913,22 @@ __global__ __launch_bounds__(256) void decode_paged(
     d.vs = 1.f;
     return d;
   };
+  // The range's first kUnitTab units, resolved once at the start by one
+  // thread each, so their dependent loads (selection -> block table ->
+  // scales) are in flight together instead of stalling the copy cursor at
+  // every unit boundary; later units are resolved when reached.
+  __shared__ PagedUnit utab[kUnitTab];
+  {
+    const uint32_t n_tab = u_end - u_begin < (uint32_t)kUnitTab ? u_end - u_begin : kUnitTab;
+    for (uint32_t t = tid; t < n_tab; t += 256) utab[t] = unit(u_begin + t);
+    __syncthreads();
+  }
+  auto unit_c = [&](uint32_t u) __attribute__((always_inline)) {
+    return u - u_begin < (uint32_t)kUnitTab ? utab[u - u_begin] : unit(u);
+  };
   auto next_unit = [&](uint32_t u, PagedUnit &d) __attribute__((always_inline)) {
     for (; u < u_end; ++u) {
-      d = unit(u);
+      d = unit_c(u);
       if (d.nk > 0) break;
     }
     return u;
@@ -1260,9 +1274,22 @@ __global__ __launch_bounds__(256) void decode_paged_fp8(
     d.vs = d.nk > 0 ? v_scale[(int64_t)page * hkv + d.g] : 1.f;
     return d;
   };
+  // The range's first kUnitTab units, resolved once at the start by one
+  // thread each, so their dependent loads (selection -> block table ->
+  // scales) are in flight together instead of stalling the copy cursor at
+  // every unit boundary; later units are resolved when reached.
+  __shared__ PagedUnit utab[kUnitTab];
+  {
+    const uint32_t n_tab = u_end - u_begin < (uint32_t)kUnitTab ? u_end - u_begin : kUnitTab;
+    for (uint32_t t = tid; t < n_tab; t += 256) utab[t] = unit(u_begin + t);
+    __syncthreads();
+  }
+  auto unit_c = [&](uint32_t u) __attribute__((always_inline)) {
+    return u - u_begin < (uint32_t)kUnitTab ? utab[u - u_begin] : unit(u);
+  };
   auto next_unit = [&](uint32_t u, PagedUnit &d) __attribute__((always_inline)) {
     for (; u < u_end; ++u) {
-      d = unit(u);
+      d = unit_c(u);
       if (d.nk > 0) break;
     }
     return u;

@@ -109,6 +109,9 @@ def _paged_case(orc, hq, hkv, B, K, lens, fp8, seed):
     (64, 8, 64, 8, [1, 64, 65, 700, 3000]),
     (16, 1, 512, 4, [511, 512, 2049]),      # G = 16
     (8, 8, 128, 6, [128, 1000]),            # G = 1
+    # 40 sequences: ~10 one-chunk units per workgroup, so the copies run
+    # several units ahead of the computation
+    (64, 8, 64, 8, [50 + 37 * i for i in range(40)]),
 ])
 @pytest.mark.parametrize("fp8", [False, True])
 def test_paged_decode(orc, hq, hkv, B, K, lens, fp8):
