@@ -211,9 +211,11 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(
 // time are one 16-byte LDS read.  The next chunk of summaries is loaded
 // into registers while the current chunk's products run, then written to
 // LDS after the barrier that ends the current chunk's reads.  Columns past
-// d_idx and rows past the chunk are zero.
+// d_idx and rows past the chunk are zero.  VEC: d_idx is a multiple of 4 and
+// both matrices 16-byte aligned (every row then is), so each summary piece
+// is one unconditional 16-byte load from a valid address, zeroed after.
 // ---------------------------------------------------------------------------
-template <int KMAX, int DW>
+template <int KMAX, int DW, bool VEC>
 __global__ __launch_bounds__(256) void topk_prefill_reg(
     const float *__restrict__ idx_q_all, SeqTab tab, const float *__restrict__ kmax_all,
     int d_idx, int topk, int win, int32_t *__restrict__ sel_all,
@@ -279,14 +281,22 @@ __global__ __launch_bounds__(256) void topk_prefill_reg(
       qreg[4 * u + 3] = x.w;
     }
   }
-  // the next chunk's summaries, in flight in registers
+  // the next chunk's summaries, in flight in registers (b0 < cand_last:
+  // row b0 exists)
   float4 kn[kLd];
   auto fetch = [&](int64_t b0) {
     const int nbk = (int)(cand_last - b0 < kCB ? cand_last - b0 : kCB);
 #pragma unroll
     for (int i = 0; i < kLd; ++i) {
       const int e = tid + 256 * i, r = e / kV, c = 4 * (e % kV);
-      kn[i] = r < nbk ? load4(kmax, vk, b0 + r, c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (VEC) {
+        const bool ok = r < nbk && c < d_idx;
+        const float4 x = *reinterpret_cast<const float4 *>(
+            kmax + (b0 + (ok ? r : 0)) * d_idx + (ok ? c : 0));
+        kn[i] = ok ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        kn[i] = r < nbk ? load4(kmax, vk, b0 + r, c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
   };
   auto put = [&]() {
@@ -474,9 +484,17 @@ hipError_t launch_topk_tab(const float *idx_q, const SeqTab &tab, const float *k
 #define MSA_TK(KM, FU)                                                                     \
   hipLaunchKernelGGL((topk_prefill_kernel<KM, FU>), grid, wg, 0, st, idx_q, tab, kmax, d_idx, \
                      topk, win, sel, sel_g)
-#define MSA_TR(KM, DW)                                                                     \
-  hipLaunchKernelGGL((topk_prefill_reg<KM, DW>), grid, wg, 0, st, idx_q, tab, kmax, d_idx,    \
-                     topk, win, sel, sel_g)
+  const bool vec = (d_idx & 3) == 0 && (reinterpret_cast<uintptr_t>(idx_q) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(kmax) & 15) == 0;
+#define MSA_TR(KM, DW)                                                                       \
+  do {                                                                                       \
+    if (vec)                                                                                 \
+      hipLaunchKernelGGL((topk_prefill_reg<KM, DW, true>), grid, wg, 0, st, idx_q, tab, kmax, \
+                         d_idx, topk, win, sel, sel_g);                                      \
+    else                                                                                     \
+      hipLaunchKernelGGL((topk_prefill_reg<KM, DW, false>), grid, wg, 0, st, idx_q, tab,     \
+                         kmax, d_idx, topk, win, sel, sel_g);                                \
+  } while (0)
   if (d_idx <= 128) {   // query operands in registers
     if (topk - win <= 16) {
       if (d_idx <= 64)
