@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void topk_prefill_reg(
   __shared__ int lst_b[kQT][KMAX];
   __shared__ int lst_n[kQT];
   __shared__ float lst_t[kQT];   // entry threshold: the (K-1)-th score, -inf until full
-  __shared__ int64_t lst_lim[kQT];   // first block past the query's candidates
+  __shared__ int lst_lim[kQT];   // first block past the query's candidates (< 2^31)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Heavier (later) tiles first.
@@ -311,7 +311,8 @@ __global__ __launch_bounds__(256) void topk_prefill_reg(
     lst_n[tid] = 0;
     lst_t[tid] = -INFINITY;
     // one 64-bit division per query, not one per query and chunk
-    lst_lim[tid] = (q_pos0 + q0 + tid) / B - win + 1;
+    const int64_t lim = (q_pos0 + q0 + tid) / B - win + 1;
+    lst_lim[tid] = (int)(lim < INT32_MAX ? lim : INT32_MAX);
   }
   for (int e = tid; e < kQT * KMAX; e += 256) {
     lst_s[e / KMAX][e % KMAX] = -INFINITY;
@@ -343,18 +344,22 @@ __global__ __launch_bounds__(256) void topk_prefill_reg(
     for (int r = 0; r < 16; ++r) sc[32 * qw + 8 * (r >> 2) + 4 * h + (r & 3)][32 * bw + j] = d[r];
     __syncthreads();   // scores visible; every wave done reading ks
     if (more) put();   // the next chunk, for after the merge
-    // Merge: wave w owns queries 16w .. 16w+15.
+    // Merge: wave w owns queries 16w .. 16w+15.  Query jq's candidate mask
+    // (a wave ballot) is kept in lane jq of (mlo, mhi), where each insertion
+    // group fetches its own with a cross-lane read.
     uint32_t need = 0;
-    uint64_t masks[16];
+    int mlo = 0, mhi = 0;
 #pragma unroll
     for (int jq = 0; jq < 16; ++jq) {
       const int qi = wave * 16 + jq;
-      const int64_t lim = lst_lim[qi];
+      const int lrel = lst_lim[qi] - (int)b0;   // b0 < cand_last < 2^31
       const float sv = sc[qi][lane];
       const float t = lst_t[qi];
-      const bool valid = qi < nq && lane < nbk && b0 + lane < lim;
-      masks[jq] = __ballot(valid && sv > t);
-      if (masks[jq]) need |= 1u << jq;
+      const bool valid = qi < nq && lane < nbk && lane < lrel;
+      const uint64_t m = __ballot(valid && sv > t);
+      mlo = lane == jq ? (int)(uint32_t)m : mlo;
+      mhi = lane == jq ? (int)(uint32_t)(m >> 32) : mhi;
+      if (m) need |= 1u << jq;
     }
     // Insertions, several queries at once: the wave splits into groups of
     // S lanes (S >= km), group gr holding the list of one query (entry gl in
@@ -370,10 +375,8 @@ __global__ __launch_bounds__(256) void topk_prefill_reg(
         if (!((need >> r0) & ((1u << NG) - 1))) continue;
         const int jq = r0 + gr;
         const int qi = wave * 16 + jq;
-        uint64_t mask = 0;
-#pragma unroll
-        for (int x = 0; x < 16; ++x)
-          if (x == jq) mask = masks[x];
+        uint64_t mask = ((uint64_t)(uint32_t)__shfl(mhi, jq, 64) << 32) |
+                        (uint64_t)(uint32_t)__shfl(mlo, jq, 64);
         int cnt = lst_n[qi];
         float ls = gl < km ? lst_s[qi][gl] : -INFINITY;
         int lb = gl < km ? lst_b[qi][gl] : -1;
