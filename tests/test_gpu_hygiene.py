@@ -11,6 +11,8 @@
 * Canary bands: every output is a view into a larger buffer whose margins
   hold a fixed NaN pattern; the margins must be unchanged after each call, so
   no kernel writes outside its outputs.
+* A selection whose CSR holds more pairs than the prefill workspace was sized
+  for stays inside the workspace.
 """
 import numpy as np
 import pytest
@@ -108,6 +110,35 @@ def test_prefill_poisoned_workspace_and_canaries():
         for a, b in zip(results[0], r):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
     _say("  outputs independent of workspace contents; all canaries intact")
+
+
+def test_prefill_csr_beyond_workspace_bound():
+    """A CSR with more non-own pairs than the workspace was sized for (every
+    query lists blocks 0..K-1, so rows hold queries of later blocks too, and
+    each query K - 1 non-own pairs even where the causal bound allows fewer):
+    the tile table is clamped to the workspace's bound, the call returns OK,
+    and nothing past the workspace or outside the outputs is written.  (The
+    outputs of such a call are unspecified.)"""
+    n_q, hq, hkv, d, B, K = 4096, 64, 8, 128, 512, 8
+    nb = n_q // B
+    _say(f"over-full CSR: n_q={n_q} B={B} K={K}")
+    g = torch.Generator().manual_seed(7)
+    q = torch.randn(n_q, hq, d, generator=g).to(torch.bfloat16).to(DEV)
+    k = torch.randn(hkv, n_q, d, generator=g).to(torch.bfloat16).to(DEV)
+    v = torch.randn(hkv, n_q, d, generator=g).to(torch.bfloat16).to(DEV)
+    sel = torch.arange(K, dtype=torch.int32, device=DEV).repeat(n_q, 1).contiguous()
+    rp, ql, sl = ops.msa_invert_selection(sel, nb)
+    lib = ops.load()
+    nbytes = lib.msa_prefill_workspace_bytes(ops.MSA_BF16, 0, n_q, hq, d, B, K)
+    tail = 1 << 20
+    big = torch.full((nbytes + tail,), 0xA5, dtype=torch.uint8, device=DEV)
+    o, lse = Guarded((n_q, hq, d), torch.float32), Guarded((n_q, hq), torch.float32)
+    ops.msa_sparse_gqa_prefill(q, k, v, sel, rp, ql, sl, B, d ** -0.5, o=o.t, lse=lse.t,
+                               ws=big[:nbytes])
+    torch.cuda.synchronize()
+    assert bool((big[nbytes:] == 0xA5).all()), "write past the workspace"
+    assert o.intact() and lse.intact(), "write outside the outputs"
+    _say("  clamped: workspace tail and output canaries intact")
 
 
 def test_prefill_f32_poisoned_workspace_and_canaries():
