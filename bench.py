@@ -257,12 +257,63 @@ def _event_ms(fn, reps: int = 5) -> float:
     return a.elapsed_time(b) / reps
 
 
+def decode_cache_residency(dev, seed: int, reps: int = 10) -> dict:
+    """The fused decode step at 1M cached tokens (one sequence, the 1M-token
+    workload's shape), timed two ways: back to back, as the bench's decode
+    loop runs it (a step may find the previous step's blocks in the L2 or in
+    the last-level cache in front of HBM), and after streaming 1 GiB through
+    a scratch copy before each step (both caches evicted). The gap between
+    the two is what cache residency is worth to the step; the L2-side
+    counters cannot tell a last-level-cache hit from an HBM read."""
+    cfg = synth.CONFIGS["dec16"].replace(name="dec1m", n_seq=1, T=1 << 20, n_hot=128)
+    x = synth.decode_inputs(cfg, dev, seed)
+    kmax = ops.msa_index_pool(x["idx_k"], cfg.block, seq_len=x["seq_len"], nb_max=cfg.nb)
+    bufs = pipeline.alloc_decode_step(x["q"], kmax, cfg.block, cfg.topk)
+    L = cfg.T - 1
+    before = x["seq_len"] - 1
+    k_new = x["k_cache"][:, :, L].contiguous()
+    v_new = x["v_cache"][:, :, L].contiguous()
+    ik_new = x["idx_k"][:, L].contiguous()
+
+    def one():
+        pipeline.decode_append_step(x["q"], k_new, v_new, x["idx_q"], ik_new, x["k_cache"],
+                                    x["v_cache"], kmax, before, cfg.block, cfg.topk, cfg.scale,
+                                    idx_k_cache=x["idx_k"], bufs=bufs)
+
+    warm = _graph_us(one)
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        one()
+    src = torch.ones(1 << 29, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream(dev)
+    times = []
+    for _ in range(reps):
+        dst.copy_(src)                      # 512 MiB read + 512 MiB written
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        g1.replay()
+        b.record(st)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    nbytes = decode_bytes(cfg.T, cfg)
+    res = {"workload": f"1 sequence x {cfg.T}-token bf16 cache, Hq {cfg.Hq} / Hkv {cfg.Hkv}, "
+                       f"d {cfg.d}, block {cfg.block}, top-K {cfg.topk}; fused decode step",
+           "bytes_per_step": int(nbytes), "us_back_to_back": round(warm, 2),
+           "us_caches_evicted": round(float(np.median(times)), 2)}
+    del x, kmax, bufs, g1, src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_next(dev, seed: int) -> dict:
     """The rows past the default path, each against its own roofline:
     several sequences per prefill call (chunks of queries against their
     caches, and many short requests), the paged bf16 / FP8 decode attention
-    at the batched decode shape, and the index variants (mean-pool, forced
-    local window) beside the default max-pool and top-K."""
+    at the batched decode shape, the 1M-token decode step with and without
+    warm caches, and the index variants (mean-pool, forced local window)
+    beside the default max-pool and top-K."""
     out = {"metric": "next-row measurements (one GPU)", "data": "synthetic, seeded"}
     # -- several sequences per call: the 32K-token workload's sequence packed
     cfg = synth.CONFIGS["p32k"]
@@ -327,6 +378,7 @@ def measure_next(dev, seed: int) -> dict:
                         "hbm_frac": round(kv_elems * 2 / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     del kp, vp, ks, vs, q, o, lse, ws
     torch.cuda.empty_cache()
+    out["decode_1m_caches"] = decode_cache_residency(dev, seed)
     # -- index variants next to the default rule
     T1, B1, di = 1 << 20, 512, 128
     ik = torch.randn((T1, di), device=dev, generator=g)
