@@ -4,10 +4,13 @@
 // 模型算力成本大幅降低原因深度解析").
 //
 // Split-KV: the selected blocks of every (sequence, KV head) are cut into
-// units whose normalised partial outputs and base-2 log-sum-exps a second
-// kernel merges per (sequence, query head).  (A same-kernel merge by the
-// last-arriving unit was measured slower: the cross-XCD release fence it
-// needs costs more than a launch.)  bf16 with d = 128 runs a persistent
+// units whose normalised partial outputs and base-2 log-sum-exps are merged
+// per (sequence, query head).  The attention calls merge in a second kernel;
+// the fused decode step merges inside the streaming kernel, the last
+// workgroup of each run combining the run's records, which are written and
+// read with device-coherent (SC1) accesses and ordered by an arrival counter
+// -- no cache write-back or invalidate (a release fence per workgroup cost
+// more than the second launch).  bf16 with d = 128 runs a persistent
 // streaming kernel on the matrix cores (one workgroup per CU, K/V chunks
 // arriving by LDS DMA while the previous chunk computes); other shapes use a
 // VALU kernel with one work item per (sequence, KV head, selected block,

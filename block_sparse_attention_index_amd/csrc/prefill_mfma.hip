@@ -435,8 +435,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ---------------------------------------------------------------------------
-// Asynchronous chunk staging for the persistent pass: global_load_lds_dwordx4
-// copies 16 bytes per lane straight into LDS at base + 16 * lane, so one wave
+// Asynchronous chunk staging for the persistent pass: a buffer load with the
+// LDS bit copies 16 bytes per lane straight into LDS at base + 16 * lane, so one wave
 // instruction fills four 256-byte rows; each lane picks which global segment
 // lands in its slot.  Rows are unpadded and XOR-swizzled by segment instead:
 //   K: segment s of row r at slot s ^ (r & 15)  -- the 16 rows read by a
@@ -447,9 +447,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 //      slots, so the 32 lanes cover all 64 banks once; rows 4 apart share the
 //      pattern, so all of a lane's V reads sit at constant offsets from one
 //      address per column block.
-// Rows past the chunk repeat its last valid row (masked keys then meet finite
-// values: their weight is exactly 0).  Chunks are kKA = 128 keys (64 KiB of
-// K and V), two in LDS: one computed while the next streams in.
+// Rows past a short chunk are out of the buffer's range and fetch nothing;
+// their LDS rows hold zeros (the buffers start zeroed) or an earlier chunk's
+// rows -- finite either way, so the masked keys' zero weights add nothing.
+// Chunks are kKA = 128 keys (64 KiB of K and V), two in LDS: one computed
+// while the next streams in.
 // ---------------------------------------------------------------------------
 constexpr int kKA = 128;   // keys per staged chunk, persistent pass
 constexpr float kCap = 256.f;   // bound on a lane's weight sum per sub-tile
@@ -481,9 +483,8 @@ __device__ __forceinline__ int kswz(int r, int sgm) { return sgm ^ (r & 15); }
 __device__ __forceinline__ int vswz(int r, int sgm) { return sgm ^ (4 * (r & 3)); }
 
 // Each 16-byte piece of a chunk goes by a buffer load straight into LDS: the
-// chunk's first row is the buffer base (scalar registers), so a lane's
-// source offset is a constant of its slot for every full chunk (no address
-// arithmetic per chunk); only a short chunk recomputes them, clamping rows.
+// chunk's first row is the buffer base (scalar registers) and its nrows rows
+// the buffer's range, so a lane's source offset depends on its slot only.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const uint16_t *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p), 0, bytes, 0x00020000);
 }
