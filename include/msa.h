@@ -31,8 +31,9 @@
  *     says otherwise.  Workspaces are scratch: their contents on entry do not
  *     matter and are undefined on exit.
  *   - Inputs must be finite.  Calls on one stream are ordered; calls that
- *     share a workspace must not overlap.  No global mutable state:
- *     calls from several host threads are safe.
+ *     share a workspace must not overlap.  No global mutable state except
+ *     msa_decode_step_noalloc's per-device scratch (see there): every other
+ *     call is safe from several host threads.
  *   - Block size B: a multiple of 16, at most 4096.  Top-K: 1 <= K <= 64.
  *     Index dimension d_idx: 1..1024 (multiples of 4 up to 1024, any value up
  *     to 256).  Token positions and counts are at most 2^40, Hq at most
