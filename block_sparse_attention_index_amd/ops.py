@@ -122,6 +122,16 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> None:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _shape(t, want, name: str) -> None:
+    """Raise ValueError unless ``t`` has ``len(want)`` dimensions matching
+    ``want`` (None: any extent).  The C calls receive sizes, not shapes, so a
+    tensor of another layout would be read as if it had the stated one."""
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        exp = tuple("*" if w is None else w for w in want)
+        raise ValueError(f"{name} has shape {got}, expected {exp}")
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -317,6 +327,10 @@ def msa_sparse_gqa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """Sparse GQA prefill, KV outer.  ``q`` [n_q, Hq, d]; ``k``/``v``
     [Hkv, kv_stride, d] (fp32 or bf16); returns ``(o [n_q, Hq, d] fp32,
     lse [n_q, Hq] fp32 or None)``."""
+    _shape(q, (None, None, None), "q")
+    _shape(k, (None, None, q.shape[2]), "k")
+    _shape(v, tuple(k.shape), "v")
+    _shape(sel, (q.shape[0], None), "sel")
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, nm)
     if not (q.dtype == k.dtype == v.dtype):
@@ -351,6 +365,11 @@ def msa_sparse_gqa_prefill_paged(q, k_pages, v_pages, block_table, sel, row_ptr,
     ``q`` [n_q, Hq, d] bf16; ``k_pages``/``v_pages`` [n_pages, Hkv, B, d]
     bf16; ``block_table`` [max_blocks] int32.  Returns ``(o, lse)`` as
     msa_sparse_gqa_prefill."""
+    _shape(q, (None, None, None), "q")
+    _shape(k_pages, (None, None, block, q.shape[2]), "k_pages")
+    _shape(v_pages, tuple(k_pages.shape), "v_pages")
+    _shape(block_table, (None,), "block_table")
+    _shape(sel, (q.shape[0], None), "sel")
     for t, nm in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
         _dev(t, nm, torch.bfloat16)
     for t, nm in ((block_table, "block_table"), (sel, "sel"), (row_ptr, "row_ptr"),
@@ -385,6 +404,10 @@ def msa_sparse_gqa_decode(q: torch.Tensor, k_cache: torch.Tensor,
                           o=None, lse=None, ws=None, want_lse: bool = True):
     """Sparse GQA decode.  ``q`` [n_seq, Hq, d]; caches [n_seq, Hkv, len_max, d];
     returns ``(o [n_seq, Hq, d] fp32, lse [n_seq, Hq] fp32 or None)``."""
+    _shape(q, (None, None, None), "q")
+    _shape(k_cache, (q.shape[0], None, None, q.shape[2]), "k_cache")
+    _shape(v_cache, tuple(k_cache.shape), "v_cache")
+    _shape(sel, (q.shape[0], None), "sel")
     for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, nm)
     if not (q.dtype == k_cache.dtype == v_cache.dtype):
@@ -456,6 +479,11 @@ def msa_sparse_gqa_decode_paged(q, k_pages, v_pages, block_table, seq_len, sel, 
     ``k_pages``/``v_pages`` [n_pages, Hkv, B, d] bf16 or float8_e4m3fn (then
     ``k_scale``/``v_scale`` [n_pages, Hkv] fp32); ``block_table``
     [n_seq, max_blocks] int32.  Returns ``(o, lse)`` as msa_sparse_gqa_decode."""
+    _shape(q, (None, None, None), "q")
+    _shape(k_pages, (None, None, block, q.shape[2]), "k_pages")
+    _shape(v_pages, tuple(k_pages.shape), "v_pages")
+    _shape(block_table, (q.shape[0], None), "block_table")
+    _shape(sel, (q.shape[0], None), "sel")
     for t, nm in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
         _dev(t, nm)
     _dev(block_table, "block_table", torch.int32)
@@ -491,6 +519,19 @@ def msa_sparse_gqa_decode_paged(q, k_pages, v_pages, block_table, seq_len, sel, 
     _check("msa_sparse_gqa_decode_paged", st)
     return o, lse
 
+def _step_shapes(q, k_new, v_new, idx_q, idx_k_new, kmax) -> None:
+    """The shapes every fused-step binding shares: q [n_seq, Hq, d], the new
+    rows [n_seq, Hkv, d], idx_q / idx_k_new [n_seq, d_idx], kmax [n_seq,
+    nb_max, d_idx]."""
+    _shape(q, (None, None, None), "q")
+    n_seq, d = q.shape[0], q.shape[2]
+    _shape(k_new, (n_seq, None, d), "k_new")
+    _shape(v_new, tuple(k_new.shape), "v_new")
+    _shape(idx_q, (n_seq, None), "idx_q")
+    _shape(idx_k_new, tuple(idx_q.shape), "idx_k_new")
+    _shape(kmax, (n_seq, None, idx_q.shape[1]), "kmax")
+
+
 def msa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                     idx_q: torch.Tensor, idx_k_new: torch.Tensor, k_cache: torch.Tensor,
                     v_cache: torch.Tensor, kmax: torch.Tensor, seq_len: torch.Tensor,
@@ -502,6 +543,9 @@ def msa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     Hq, d]; ``k_new``/``v_new`` [n_seq, Hkv, d]; ``idx_q``/``idx_k_new``
     [n_seq, d_idx]; caches [n_seq, Hkv, len_max, d]; ``kmax`` [n_seq, nb_max,
     d_idx].  ``seq_len`` is not advanced.  Returns ``(o, lse, sel)``."""
+    _step_shapes(q, k_new, v_new, idx_q, idx_k_new, kmax)
+    _shape(k_cache, (q.shape[0], k_new.shape[1], None, q.shape[2]), "k_cache")
+    _shape(v_cache, tuple(k_cache.shape), "v_cache")
     for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
                   (v_cache, "v_cache")):
         _dev(t, nm)
@@ -542,6 +586,10 @@ def msa_decode_step_paged(q, k_new, v_new, idx_q, idx_k_new, k_pages, v_pages, b
     token's rows go to row ``L % B`` of page ``block_table[s][L // B]``.
     ``len_max`` bounds L (and is the row capacity of ``idx_k_cache`` [n_seq,
     len_max, d_idx] when given).  Otherwise as :func:`msa_decode_step`."""
+    _step_shapes(q, k_new, v_new, idx_q, idx_k_new, kmax)
+    _shape(k_pages, (None, k_new.shape[1], block, q.shape[2]), "k_pages")
+    _shape(v_pages, tuple(k_pages.shape), "v_pages")
+    _shape(block_table, (q.shape[0], None), "block_table")
     for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pages, "k_pages"),
                   (v_pages, "v_pages")):
         _dev(t, nm, torch.bfloat16)
@@ -579,6 +627,9 @@ def msa_decode_step_noalloc(q, k_new, v_new, idx_q, idx_k_new, k_cache, v_cache,
     """:func:`msa_decode_step` on the library's static scratch (no workspace
     argument; the C call allocates nothing).  Outputs not passed in are
     allocated here by torch; pass them to keep the whole call allocation-free."""
+    _step_shapes(q, k_new, v_new, idx_q, idx_k_new, kmax)
+    _shape(k_cache, (q.shape[0], k_new.shape[1], None, q.shape[2]), "k_cache")
+    _shape(v_cache, tuple(k_cache.shape), "v_cache")
     for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
                   (v_cache, "v_cache")):
         _dev(t, nm)
