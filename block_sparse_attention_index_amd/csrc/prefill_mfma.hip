@@ -736,13 +736,19 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
       f32x16 sacc;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) sacc[rr] = 0.f;
+      // all eight K operands of the sub-tile are read before its first
+      // product, so the LDS round trips overlap instead of stalling each
+      // product of the dependent Q.K^T chain
+      u32x4 kpre[8];
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
         const int kr = sub * 32 + j;
-        const u32x4 kraw = *reinterpret_cast<const u32x4 *>(
+        kpre[cc] = *reinterpret_cast<const u32x4 *>(
             &cur.Ks[kr * kD + kswz(kr, cc * 2 + h) * 8]);
-        sacc = mfma32(as_bf16x8(kraw), qf[cc], sacc);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) sacc = mfma32(as_bf16x8(kpre[cc]), qf[cc], sacc);
       if (koff0 + 31 >= nkeys) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
@@ -768,6 +774,19 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
         pb1 = __builtin_convertvector(p1, bf16x8);
         ps = row_sum16(pb0, pb1);
       };
+      // V^T operands of the first k-step, read ahead of the softmax: their
+      // LDS round trip runs under its exponentials
+      const char *vbase = reinterpret_cast<const char *>(cur.Vs);
+      u32x4 vpre[4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        constexpr int kRow = kD * 2;
+        const int o0 = voff[cb] + (sub * 32) * kRow;
+        const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0));
+        const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0 + 8 * kRow));
+        vpre[cb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+      __builtin_amdgcn_sched_barrier(0);
       weights();
       if (__ballot(!(ps <= kCap))) {
         float mloc = sacc[0];
@@ -785,18 +804,16 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
         weights();
       }
       lsum += ps;
-      const char *vbase = reinterpret_cast<const char *>(cur.Vs);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int cb = 0; cb < 4; ++cb) acc[cb] = mfma32(as_bf16x8(vpre[cb]), pb0, acc[cb]);
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          constexpr int kRow = kD * 2;   // bytes per V row
-          const int o0 = voff[cb] + (sub * 32 + 16 * ks) * kRow;
-          const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0));
-          const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0 + 8 * kRow));
-          const u32x4 vraw = {lo[0], lo[1], hi[0], hi[1]};
-          acc[cb] = mfma32(as_bf16x8(vraw), ks == 0 ? pb0 : pb1, acc[cb]);
-        }
+      for (int cb = 0; cb < 4; ++cb) {
+        constexpr int kRow = kD * 2;   // bytes per V row
+        const int o0 = voff[cb] + (sub * 32 + 16) * kRow;
+        const u32x2 lo = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0));
+        const u32x2 hi = lds_read_tr(reinterpret_cast<const uint16_t *>(vbase + o0 + 8 * kRow));
+        const u32x4 vraw = {lo[0], lo[1], hi[0], hi[1]};
+        acc[cb] = mfma32(as_bf16x8(vraw), pb1, acc[cb]);
       }
     }
     if (last) {
