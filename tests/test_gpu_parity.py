@@ -263,6 +263,7 @@ def test_prefill_small_heads_d64(orc):
 @pytest.mark.parametrize("dtype,hq,hkv,d,B,K,lens", [
     ("bf16", 16, 2, 128, 64, 8, [3000, 2049, 100]),     # matrix-core path
     ("bf16", 64, 8, 128, 512, 8, [3000, 1537, 600]),    # the 1M decode shape
+    ("bf16", 64, 8, 128, 512, 8, [4700]),               # one sequence: two segments per block
     ("bf16", 32, 2, 128, 128, 5, [2000, 129, 1]),       # G = 16, one-token cache
     ("f32", 8, 2, 64, 64, 4, [1200, 700, 65]),          # VALU path
 ])
@@ -468,6 +469,9 @@ def test_fused_steps_in_a_captured_graph():
     # the 1M-token decode shape (Hq 64 / Hkv 8, B 512, K 8): caches of 4..9
     # blocks, one sequence opening a block, one just short of full rows
     (64, 8, 512, 8, [4096, 4607, 3583, 1535]),
+    # one sequence at that shape: blocks split into two 128-key segments, the
+    # last workgroup of each KV head combining 16 partials (as at 1M tokens)
+    (64, 8, 512, 8, [4700]),
     # 128 sequences with full rows (own block >= K - 1): the workgroups whose
     # range starts on an own-block unit fetch its first chunk before the
     # selection merge (own blocks from 7 to 512 keys)
