@@ -787,6 +787,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
         vpre[cb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (sub == 0 && ci == 0) {
+        // an item's first sub-tile: the reference max is its own row max, so
+        // its weights are taken once (the test below then passes)
+        float m0 = sacc[0];
+#pragma unroll
+        for (int rr = 1; rr < 16; ++rr) m0 = fmaxf(m0, sacc[rr]);
+        mref = max_with_partner(m0) * scale_log2;
+      }
       weights();
       if (__ballot(!(ps <= kCap))) {
         float mloc = sacc[0];
