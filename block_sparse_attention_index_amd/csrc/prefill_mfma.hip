@@ -756,10 +756,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
           if (koff >= nkeys) sacc[rr] = -INFINITY;
         }
       }
-      // Weights against the current reference max; the row max itself is
-      // only computed when some lane's 16 weights sum past 2^8 (or are not
-      // finite: the item's first sub-tile), which bounds every weight by 2^8
-      // as a per-sub-tile max test would.
+      // Weights against the current reference max; after an item's first
+      // sub-tile (which takes its row max as the reference) the row max is
+      // only computed when some lane's 16 weights sum past 2^8, which bounds
+      // every weight by 2^8 as a per-sub-tile max test would.
       bf16x8 pb0, pb1;
       float ps;
       auto weights = [&]() {
