@@ -634,14 +634,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_nonown_persistent(
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) qn[cc] = *reinterpret_cast<const u32x4 *>(qp + cc * 16 + 8 * h);
   };
+  // A row past the tile's queries keeps the fragments of query row 0 (a
+  // valid row, so its scores are finite); its results are never stored.
   auto read_q = [&](int32_t qr, bf16x8 (&dst)[8]) {
-    const bool a = qr >= 0 && qr < n_q;
+    (void)qr;
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      u32x4 x = qn[cc];
-      if (!a) x = u32x4{0u, 0u, 0u, 0u};
-      dst[cc] = as_bf16x8(x);
-    }
+    for (int cc = 0; cc < 8; ++cc) dst[cc] = as_bf16x8(qn[cc]);
   };
   // element offset of an item's block in KV head gg, and its key count
   const int64_t hstride = kvm.pages ? (int64_t)B * kD : kvm.kv_stride * kD;
