@@ -204,6 +204,31 @@ int msa_index_topk_decode_window(const float *idx_q, int32_t n_seq,
                                            as_stream(stream)));
 }
 
+// One workgroup per (query, 64-block chunk): the chunks run along grid y.
+static bool batch_dims_ok(int64_t n_q, int64_t nb_max) {
+  return n_q >= 0 && n_q <= INT32_MAX && nb_max >= 1 &&
+         (nb_max + 63) / 64 <= kMaxGridY;
+}
+
+size_t msa_topk_batch_workspace_bytes(int64_t n_q, int64_t nb_max, int32_t topk) {
+  if (!batch_dims_ok(n_q, nb_max) || !topk_ok(topk)) return 0;
+  return msa::topk_batch_ws_bytes(n_q, nb_max, topk);
+}
+
+int msa_index_topk_batch(const float *idx_q, int64_t n_q, const int32_t *q_seq,
+                         const int64_t *q_pos, const float *kmax, int32_t n_seq,
+                         int64_t nb_max, int32_t d_idx, int32_t block, int32_t topk,
+                         int32_t *sel, void *ws, size_t ws_bytes, void *stream) {
+  if (!batch_dims_ok(n_q, nb_max) || n_seq < 1 || n_seq > kMaxGridY ||
+      !didx_ok(d_idx) || !block_ok(block) || !topk_ok(topk))
+    return MSA_ERR_INVALID_ARG;
+  if (n_q == 0) return MSA_OK;
+  if (!idx_q || !q_seq || !q_pos || !kmax || !sel || !ws) return MSA_ERR_INVALID_ARG;
+  if (ws_bytes < msa::topk_batch_ws_bytes(n_q, nb_max, topk)) return MSA_ERR_WORKSPACE;
+  return status_of(msa::launch_topk_batch(idx_q, n_q, q_seq, q_pos, kmax, n_seq, nb_max,
+                                          d_idx, block, topk, sel, ws, as_stream(stream)));
+}
+
 int msa_index_topk_decode(const float *idx_q, int32_t n_seq,
                           const int64_t *seq_len, const float *kmax,
                           int64_t nb_max, int32_t d_idx, int32_t block,

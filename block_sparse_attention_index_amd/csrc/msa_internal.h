@@ -37,6 +37,11 @@ hipError_t launch_topk_tab(const float *idx_q, const SeqTab &tab, const float *k
                            int32_t *sel_g, hipStream_t st);
 
 size_t topk_decode_ws_bytes(int32_t n_seq, int64_t nb_max, int32_t topk);
+size_t topk_batch_ws_bytes(int64_t n_q, int64_t nb_max, int32_t topk);
+hipError_t launch_topk_batch(const float *idx_q, int64_t n_q, const int32_t *q_seq,
+                             const int64_t *q_pos, const float *kmax, int32_t n_seq,
+                             int64_t nb_max, int32_t d_idx, int32_t block, int32_t topk,
+                             int32_t *sel, void *ws, hipStream_t st);
 hipError_t launch_topk_decode(const float *idx_q, int32_t n_seq,
                               const int64_t *seq_len, const float *kmax,
                               int64_t nb_max, int32_t d_idx, int32_t block,

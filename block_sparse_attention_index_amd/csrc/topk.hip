@@ -475,6 +475,49 @@ __global__ __launch_bounds__(64) void topk_decode_merge(
                      sel + (int64_t)s * topk, st_s, st_b, 2048);
 }
 
+// A batch of queries of several sequences, each at its own position: query
+// i of sequence q_seq[i] at q_pos[i] is scanned like a decode query (chunks
+// of 64 blocks of its sequence's summaries, then the chunk lists merged).  A
+// query whose sequence or position is out of range gets no candidates and a
+// row of -1.
+__device__ __forceinline__ bool batch_query_ok(int32_t s, int64_t p, int32_t n_seq,
+                                               int64_t nb_max, int B) {
+  return s >= 0 && s < n_seq && p >= 0 && p < nb_max * B;
+}
+
+__global__ __launch_bounds__(256) void topk_batch_kernel(
+    const float *__restrict__ idx_q, const int32_t *__restrict__ q_seq,
+    const int64_t *__restrict__ q_pos, const float *__restrict__ kmax, int32_t n_seq,
+    int64_t nb_max, int d_idx, int B, int km, float *__restrict__ ws_s,
+    int *__restrict__ ws_b, int n_chunks) {
+  const int64_t i = blockIdx.x;
+  const int32_t s = q_seq[i];
+  const int64_t p = q_pos[i];
+  const bool ok = batch_query_ok(s, p, n_seq, nb_max, B);
+  decode_scan_chunk(idx_q + i * d_idx, kmax + (int64_t)(ok ? s : 0) * nb_max * d_idx,
+                    ok ? p / B : 0, nb_max, d_idx, km, blockIdx.y,
+                    ws_s + (i * n_chunks + blockIdx.y) * km,
+                    ws_b + (i * n_chunks + blockIdx.y) * km);
+}
+
+__global__ __launch_bounds__(64) void topk_batch_merge(
+    const int32_t *__restrict__ q_seq, const int64_t *__restrict__ q_pos, int32_t n_seq,
+    int64_t nb_max, int B, int topk, const float *__restrict__ ws_s,
+    const int *__restrict__ ws_b, int n_chunks, int32_t *__restrict__ sel) {
+  __shared__ float st_s[2048];
+  __shared__ int st_b[2048];
+  const int64_t i = blockIdx.x;
+  const int32_t s = q_seq[i];
+  const int64_t p = q_pos[i];
+  if (!batch_query_ok(s, p, n_seq, nb_max, B)) {   // uniform: one query per workgroup
+    for (int k = threadIdx.x; k < topk; k += 64) sel[i * topk + k] = -1;
+    return;
+  }
+  const int km = topk - 1;
+  decode_merge_lists(ws_s + i * n_chunks * km, ws_b + i * n_chunks * km, n_chunks, topk, 1,
+                     [&] { return (int)(p / B); }, sel + i * topk, st_s, st_b, 2048);
+}
+
 }  // namespace
 
 hipError_t launch_topk_tab(const float *idx_q, const SeqTab &tab, const float *kmax,
@@ -562,6 +605,33 @@ hipError_t launch_topk_decode(const float *idx_q, int32_t n_seq,
   }
   hipLaunchKernelGGL(topk_decode_merge, dim3(n_seq), dim3(64), 0, st, seq_len,
                      block, topk, win, ws_s, ws_b, n_chunks, sel);
+  return hipGetLastError();
+}
+
+// Layout as the decode selection's: [chunk scores][chunk block ids] per query.
+size_t topk_batch_ws_bytes(int64_t n_q, int64_t nb_max, int32_t topk) {
+  const int64_t n_chunks = (nb_max + kDecChunk - 1) / kDecChunk;
+  const size_t n = (size_t)n_q * n_chunks * (topk > 1 ? topk - 1 : 1);
+  return align256(n * sizeof(float)) + align256(n * sizeof(int));
+}
+
+hipError_t launch_topk_batch(const float *idx_q, int64_t n_q, const int32_t *q_seq,
+                             const int64_t *q_pos, const float *kmax, int32_t n_seq,
+                             int64_t nb_max, int32_t d_idx, int32_t block, int32_t topk,
+                             int32_t *sel, void *ws, hipStream_t st) {
+  if (n_q <= 0) return hipSuccess;
+  const int n_chunks = (int)((nb_max + kDecChunk - 1) / kDecChunk);
+  const size_t n = (size_t)n_q * n_chunks * (topk > 1 ? topk - 1 : 1);
+  char *w = static_cast<char *>(ws);
+  float *ws_s = reinterpret_cast<float *>(w);
+  w += align256(n * sizeof(float));
+  int *ws_b = reinterpret_cast<int *>(w);
+  if (topk > 1)
+    hipLaunchKernelGGL(topk_batch_kernel, dim3((unsigned)n_q, n_chunks), dim3(256), 0, st,
+                       idx_q, q_seq, q_pos, kmax, n_seq, nb_max, d_idx, block, topk - 1, ws_s,
+                       ws_b, n_chunks);
+  hipLaunchKernelGGL(topk_batch_merge, dim3((unsigned)n_q), dim3(64), 0, st, q_seq, q_pos,
+                     n_seq, nb_max, block, topk, ws_s, ws_b, n_chunks, sel);
   return hipGetLastError();
 }
 

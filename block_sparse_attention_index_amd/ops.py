@@ -34,6 +34,7 @@ ENTRY_POINTS = (
     "msa_sparse_gqa_decode_paged", "msa_prefill_varlen_workspace_bytes",
     "msa_prefill_varlen", "msa_decode_step_noalloc_max_bytes", "msa_decode_step_noalloc",
     "msa_sparse_gqa_prefill_paged", "msa_decode_step_paged",
+    "msa_topk_batch_workspace_bytes", "msa_index_topk_batch",
 )
 
 
@@ -68,6 +69,9 @@ def load():
         "msa_index_topk_decode_window": ([P, i32, P, P, i64, i32, i32, i32, i32, P, P, sz,
                                           P], ctypes.c_int),
         "msa_topk_decode_workspace_bytes": ([i32, i64, i32], sz),
+        "msa_topk_batch_workspace_bytes": ([i64, i64, i32], sz),
+        "msa_index_topk_batch": ([P, i64, P, P, P, i32, i64, i32, i32, i32, P, P, sz, P],
+                                 i32),
         "msa_index_topk_decode": ([P, i32, P, P, i64, i32, i32, i32, P, P, sz, P],
                                   ctypes.c_int),
         "msa_invert_workspace_bytes": ([i64, i32, i64], sz),
@@ -284,6 +288,34 @@ def msa_index_topk_decode_window(idx_q: torch.Tensor, seq_len: torch.Tensor,
                                           nb_max, d, block, topk, window, _ptr(sel),
                                           _ptr(ws), ws.numel(), _stream(idx_q))
     _check("msa_index_topk_decode_window", st)
+    return sel
+
+
+def msa_index_topk_batch(idx_q: torch.Tensor, q_seq: torch.Tensor, q_pos: torch.Tensor,
+                         kmax: torch.Tensor, block: int, topk: int,
+                         sel: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Top-K for a batch of queries of several sequences, each at its own
+    position: ``idx_q`` [n_q, d_idx] fp32, ``q_seq`` [n_q] int32, ``q_pos``
+    [n_q] int64, ``kmax`` [n_seq, nb_max, d_idx] -> ``sel`` [n_q, topk]."""
+    _dev(idx_q, "idx_q", torch.float32)
+    _dev(q_seq, "q_seq", torch.int32)
+    _dev(q_pos, "q_pos", torch.int64)
+    _dev(kmax, "kmax", torch.float32)
+    n_q, d = idx_q.shape
+    n_seq, nb_max = kmax.shape[0], kmax.shape[1]
+    _shape(q_seq, (n_q,), "q_seq")
+    _shape(q_pos, (n_q,), "q_pos")
+    _shape(kmax, (n_seq, nb_max, d), "kmax")
+    lib = load()
+    ws = _ws(lib.msa_topk_batch_workspace_bytes(n_q, nb_max, topk), idx_q, ws)
+    if sel is None:
+        sel = torch.empty((n_q, topk), dtype=torch.int32, device=idx_q.device)
+    _dev(sel, "sel", torch.int32)
+    _shape(sel, (n_q, topk), "sel")
+    st = lib.msa_index_topk_batch(_ptr(idx_q), n_q, _ptr(q_seq), _ptr(q_pos), _ptr(kmax),
+                                  n_seq, nb_max, d, block, topk, _ptr(sel), _ptr(ws),
+                                  ws.numel(), _stream(idx_q))
+    _check("msa_index_topk_batch", st)
     return sel
 
 

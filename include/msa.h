@@ -175,6 +175,32 @@ int msa_index_topk_decode_window(const float *idx_q, int32_t n_seq,
                                  size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
+ * msa_index_topk_batch -- the same selection for a batch of queries drawn
+ * from several sequences, each at its own position ([CXT] section 3.3: the
+ * index branch scores a query against the block summaries of its own
+ * sequence; [YLY] "索引分支（Index Branch）").  Query i belongs to sequence
+ * q_seq[i] and sits at position p = q_pos[i], own = p / B; its row is that of
+ * msa_index_topk for that query against sequence q_seq[i]'s summaries.  A
+ * query with q_seq[i] outside [0, n_seq) or p outside [0, nb_max * B) gets a
+ * row of -1 (no error: the arrays are on the device).
+ *
+ *   idx_q  [n_q][d_idx] fp32
+ *   q_seq  device int32 [n_q];  q_pos device int64 [n_q]
+ *   kmax   [n_seq][nb_max][d_idx] fp32 (rows past a sequence's own block of
+ *          the query are read but never selected)
+ *   sel    [n_q][K] int32 (output)
+ *   ws     device scratch of msa_topk_batch_workspace_bytes() bytes
+ *
+ * n_q = 0 returns MSA_OK and launches nothing; 1 <= n_seq <= 65535 and
+ * nb_max <= 65535 * 64 (else MSA_ERR_INVALID_ARG).
+ * ------------------------------------------------------------------------ */
+size_t msa_topk_batch_workspace_bytes(int64_t n_q, int64_t nb_max, int32_t topk);
+int msa_index_topk_batch(const float *idx_q, int64_t n_q, const int32_t *q_seq,
+                         const int64_t *q_pos, const float *kmax, int32_t n_seq,
+                         int64_t nb_max, int32_t d_idx, int32_t block, int32_t topk,
+                         int32_t *sel, void *ws, size_t ws_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
  * msa_invert_selection -- the queries that hit each KV block, as CSR.
  * [CXT] section 2.2: the KV-outer loop needs, per block, the queries that
  * chose it.  Histogram, prefix sum and a deterministic scatter:

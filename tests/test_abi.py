@@ -68,6 +68,16 @@ def test_topk_validation(lib):
     assert need > 0
     assert lib.msa_index_topk_decode(P, 2, P, P, 100, 64, 64, 8, P, P, need - 1, None) == EWS
     assert lib.msa_index_topk_decode(P, 2, None, P, 100, 64, 64, 8, P, P, need, None) == EINVAL
+    f = lib.msa_index_topk_batch
+    need = lib.msa_topk_batch_workspace_bytes(300, 100, 8)
+    assert need > 0
+    assert lib.msa_topk_batch_workspace_bytes(300, 65535 * 64 + 1, 8) == 0   # grid y
+    assert f(P, 300, P, P, P, 2, 100, 64, 64, 8, P, P, need - 1, None) == EWS
+    assert f(P, 300, None, P, P, 2, 100, 64, 64, 8, P, P, need, None) == EINVAL  # q_seq
+    assert f(P, 300, P, P, P, 0, 100, 64, 64, 8, P, P, need, None) == EINVAL     # n_seq
+    assert f(P, 300, P, P, P, 2, 100, 64, 64, 65, P, P, need, None) == EINVAL    # topk
+    assert f(P, 300, P, P, P, 2, 65535 * 64 + 1, 64, 64, 8, P, P, need, None) == EINVAL
+    assert f(None, 0, None, None, None, 2, 100, 64, 64, 8, None, None, 0, None) == OK
 
 
 def test_invert_validation(lib):

@@ -163,6 +163,51 @@ def test_topk_ties_go_low(orc):
         assert sel[p].tolist() == list(range(m)) + [own] + [-1] * (K - m - 1)
 
 
+@pytest.mark.parametrize("lens,B,K,d", [
+    ([9000, 4100, 700], 64, 16, 128),   # three chunk lists, the last sequences shorter
+    ([5000, 2600], 32, 64, 77),         # K = 64 (max), odd d_idx (scalar scan)
+    ([3000], 16, 1, 32),                # K = 1: own block only
+])
+def test_topk_batch(orc, lens, B, K, d):
+    """Queries of several sequences at scattered positions, each row against
+    its own sequence's summaries; out-of-range sequence ids and positions get
+    rows of -1."""
+    _say(f"topk batch lens={lens} B={B} K={K} d={d}")
+    n_seq = len(lens)
+    nb_max = -(-max(lens) // B) + 3          # summaries past every sequence's end
+    kmax = np.zeros((n_seq, nb_max, d), np.float32)
+    qrows, qs, qp = [], [], []
+    rng = np.random.default_rng(7)
+    for s_, L in enumerate(lens):
+        cfg = synth.Config("t", L, "f32", 1, 1, 64, d, B, K, 4)
+        x = synth.sequence_inputs(cfg, "cpu", 10 + s_)
+        kmax[s_, :-(-L // B)] = orc.pool(x["idx_k"].numpy(), B)
+        pos = np.unique(np.concatenate([[0, B - 1, B, L - 1], rng.integers(0, L, 120)]))
+        qrows.append(x["idx_q"].numpy()[pos])
+        qs += [s_] * len(pos)
+        qp += pos.tolist()
+    n_ok = len(qs)
+    bad = [(-1, 0), (n_seq, 5), (0, -1), (0, nb_max * B), (n_seq - 1, 1 << 40)]
+    qs += [b[0] for b in bad]
+    qp += [b[1] for b in bad]
+    idx_q = np.concatenate(qrows + [np.ones((len(bad), d), np.float32)])
+    perm = rng.permutation(len(qs))           # sequences interleaved in the batch
+    idx_q, qs, qp = idx_q[perm], np.array(qs, np.int32)[perm], np.array(qp, np.int64)[perm]
+    ws = torch.empty(ops.load().msa_topk_batch_workspace_bytes(len(qs), nb_max, K),
+                     dtype=torch.uint8, device=DEV)
+    for rep in range(2):                      # the second call reuses the workspace
+        sel_d = _np(ops.msa_index_topk_batch(torch.from_numpy(idx_q).to(DEV),
+                                             torch.from_numpy(qs).to(DEV),
+                                             torch.from_numpy(qp).to(DEV),
+                                             torch.from_numpy(kmax).to(DEV), B, K, ws=ws))
+    valid = perm < n_ok
+    assert np.all(sel_d[~valid] == -1)
+    for s_ in range(n_seq):
+        rows = np.nonzero(valid & (qs == s_))[0]
+        so, gr, ga, eb = orc.select(idx_q[rows], qp[rows], kmax[s_], B, K)
+        check_selection(sel_d[rows], so, gr, ga, eb, idx_q[rows], kmax[s_], qp[rows], B)
+
+
 # --------------------------------------------------------------------------
 # CSR
 # --------------------------------------------------------------------------
