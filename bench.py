@@ -404,6 +404,20 @@ def measure_next(dev, seed: int) -> dict:
         out[name] = {"workload": f"{T2} queries x {T2 // B2} blocks, d_idx {di}, top-K {K2}",
                      "ms": round(ms, 3), "tflops": round(flop / ms / 1e9, 2),
                      "frac_fp32_peak": round(flop / ms / 1e9 / PEAK_F32_TFLOPS, 4)}
+    # -- a batch of queries of 16 sequences at scattered positions
+    n_s, per = 16, 256
+    nbs = T2 // B2
+    kms = torch.randn((n_s, nbs, di), device=dev, generator=g)
+    qs = torch.arange(n_s, dtype=torch.int32, device=dev).repeat_interleave(per)
+    qp = torch.randint(0, T2, (n_s * per,), device=dev, generator=g)
+    iqb = torch.randn((n_s * per, di), device=dev, generator=g)
+    flop = 2 * di * int((qp // B2).sum().item())
+    ms = _event_ms(lambda: ops.msa_index_topk_batch(iqb, qs, qp, kms, B2, K2))
+    out["topk_batch"] = {"workload": f"{n_s} sequences x {nbs} blocks, {per} queries each at "
+                                     f"uniform positions, d_idx {di}, top-K {K2}",
+                         "ms": round(ms, 3), "tflops": round(flop / ms / 1e9, 2),
+                         "frac_fp32_peak": round(flop / ms / 1e9 / PEAK_F32_TFLOPS, 4)}
+    del iq, kmax, kms, qs, qp, iqb
     return out
 
 

@@ -494,10 +494,18 @@ __global__ __launch_bounds__(256) void topk_batch_kernel(
   const int32_t s = q_seq[i];
   const int64_t p = q_pos[i];
   const bool ok = batch_query_ok(s, p, n_seq, nb_max, B);
-  decode_scan_chunk(idx_q + i * d_idx, kmax + (int64_t)(ok ? s : 0) * nb_max * d_idx,
-                    ok ? p / B : 0, nb_max, d_idx, km, blockIdx.y,
-                    ws_s + (i * n_chunks + blockIdx.y) * km,
-                    ws_b + (i * n_chunks + blockIdx.y) * km);
+  const int64_t own = ok ? p / B : 0;
+  float *out_s = ws_s + (i * n_chunks + blockIdx.y) * km;
+  int *out_b = ws_b + (i * n_chunks + blockIdx.y) * km;
+  if ((int64_t)blockIdx.y * kDecChunk >= own) {   // no candidate here (uniform): empty list
+    for (int r = threadIdx.x; r < km; r += 256) {
+      out_s[r] = -INFINITY;
+      out_b[r] = -1;
+    }
+    return;
+  }
+  decode_scan_chunk(idx_q + i * d_idx, kmax + (int64_t)(ok ? s : 0) * nb_max * d_idx, own,
+                    nb_max, d_idx, km, blockIdx.y, out_s, out_b);
 }
 
 __global__ __launch_bounds__(64) void topk_batch_merge(
