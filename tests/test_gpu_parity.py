@@ -167,12 +167,14 @@ def test_topk_ties_go_low(orc):
     ([9000, 4100, 700], 64, 16, 128),   # three chunk lists, the last sequences shorter
     ([5000, 2600], 32, 64, 77),         # K = 64 (max), odd d_idx (scalar scan)
     ([3000], 16, 1, 32),                # K = 1: own block only
+    ([3000, 2000], 32, 8, 300),         # d_idx over two staged column slabs
 ])
-def test_topk_batch(orc, lens, B, K, d):
+@pytest.mark.parametrize("shuffle", [True, False])
+def test_topk_batch(orc, lens, B, K, d, shuffle):
     """Queries of several sequences at scattered positions, each row against
     its own sequence's summaries; out-of-range sequence ids and positions get
-    rows of -1."""
-    _say(f"topk batch lens={lens} B={B} K={K} d={d}")
+    rows of -1, in a shuffled batch and in one ordered by sequence."""
+    _say(f"topk batch lens={lens} B={B} K={K} d={d} shuffle={shuffle}")
     n_seq = len(lens)
     nb_max = -(-max(lens) // B) + 3          # summaries past every sequence's end
     kmax = np.zeros((n_seq, nb_max, d), np.float32)
@@ -191,7 +193,7 @@ def test_topk_batch(orc, lens, B, K, d):
     qs += [b[0] for b in bad]
     qp += [b[1] for b in bad]
     idx_q = np.concatenate(qrows + [np.ones((len(bad), d), np.float32)])
-    perm = rng.permutation(len(qs))           # sequences interleaved in the batch
+    perm = rng.permutation(len(qs)) if shuffle else np.arange(len(qs))
     idx_q, qs, qp = idx_q[perm], np.array(qs, np.int32)[perm], np.array(qp, np.int64)[perm]
     ws = torch.empty(ops.load().msa_topk_batch_workspace_bytes(len(qs), nb_max, K),
                      dtype=torch.uint8, device=DEV)
